@@ -1,0 +1,162 @@
+/* dsa.h -- C ABI of the MI355X (gfx950) DSA hot path: Lightning Indexer with fused Top-K, and
+ * Sparse Flash Attention over the selected MLA latent rows.
+ *
+ * Pages cited:
+ *   [P1] "Inference Optimization for Kimi K3.1 Pro: Decoding Architecture Evolution and Systems
+ *        Engineering Practices"
+ *   [P2] "Optimizing Kimi K3.1 Pro Sparse Attention Inference: Day0 Adaptation and Performance
+ *        Tuning on Ascend"
+ *   [P3] "Day0 Inference Adaptation for Next-Gen LLMs: Deep Optimization Practices with CANN
+ *        Heterogeneous Computing Architecture"
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers into caller-owned memory, contiguous, row-major, with
+ *     the alignment stated per argument.  The library never allocates, frees or retains device
+ *     memory; scratch comes from the caller's `workspace` (size from the *_workspace_size call).
+ *   - Calls are asynchronous on `stream` (NULL = the null stream); nothing is synchronised and
+ *     nothing is allocated, so a call may be captured into a hipGraph.  Buffers must stay alive
+ *     until the stream has passed the call.  Calls are deterministic: identical inputs give
+ *     bitwise-identical outputs.  Two calls that share a workspace must be ordered on one stream.
+ *   - Argument errors (NULL pointer, misalignment, unsupported or inconsistent shape, workspace
+ *     too small) are detected on the host before anything is launched; the call then returns a
+ *     non-OK status, launches nothing and leaves outputs untouched.  A launch failure returns
+ *     DSA_ERR_HIP.  dsa_last_error() gives a thread-local description of the last failure.
+ *   - Device-side preconditions (not checked on the host because the data lives on the device):
+ *     T <= seq_lens[b] <= max_seq_len <= max_pages * page_size, block_table entries used by a
+ *     sequence lie in [0, num_pages), fp8 scales are finite and > 0.  The kernels clamp page ids
+ *     and lengths so that a violated precondition gives wrong numbers, never an out-of-bounds
+ *     access.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_VERSION 1
+#define DSA_PAGE_SIZE 64          /* tokens per cache page */
+#define DSA_DIM_QK 576            /* MLA latent row: 512 "nope" + 64 rope columns */
+#define DSA_DIM_V 512             /* V = the first 512 columns of the latent row */
+#define DSA_MAX_TOP_K 2048        /* largest supported K */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,          /* a required pointer is NULL */
+  DSA_ERR_SHAPE = 2,         /* inconsistent or out-of-range size */
+  DSA_ERR_ALIGN = 3,         /* pointer not aligned as documented */
+  DSA_ERR_UNSUPPORTED = 4,   /* valid request this build has no kernel for */
+  DSA_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than *_workspace_size */
+  DSA_ERR_HIP = 6            /* the HIP runtime reported an error at launch */
+} dsa_status;
+
+typedef enum {
+  DSA_BF16 = 0,              /* bfloat16 */
+  DSA_FP8_E4M3 = 1           /* OCP E4M3FN (max 448, no infinities) */
+} dsa_dtype;
+
+/* Geometry of the paged caches ([P1] §2 "on-demand in-page addressing"; [P3] §3.1, the paged K
+ * cache is read in place).  Logical token s of sequence b lives in physical page
+ * block_table[b * max_pages + s / page_size], slot s % page_size.  The indexer-K cache and the
+ * latent-KV cache share this geometry. */
+typedef struct {
+  const int32_t *block_table;   /* device, [batch, max_pages] physical page ids, 4-byte aligned */
+  const int32_t *seq_lens;      /* device, [batch] tokens in the cache INCLUDING the T query
+                                   tokens of this call; 4-byte aligned */
+  int32_t batch;                /* >= 1 */
+  int32_t max_pages;            /* row length of block_table, >= ceil(max_seq_len / page_size) */
+  int32_t page_size;            /* must be DSA_PAGE_SIZE */
+  int32_t num_pages;            /* pages in each cache pool */
+  int32_t max_seq_len;          /* host-side upper bound of seq_lens[] (sizes the launch grid) */
+} dsa_paged_layout;
+
+/* Query t (0 <= t < T) of sequence b sits at position pos = seq_lens[b] - T + t and sees keys
+ * 0..pos (its own key included): T = 1 is decode, T = 4 speculative verify of 4 causal drafts,
+ * T = seq_len a causal prefill chunk over its own context. */
+typedef struct {
+  int32_t T;                    /* query tokens per sequence, >= 1 */
+  int32_t heads;                /* indexer heads H_I: 8, 16, 32 or 64 */
+  int32_t dim;                  /* indexer head dim d_I: 64 or 128 */
+  int32_t top_k;                /* K, 1..DSA_MAX_TOP_K */
+  dsa_dtype dtype;              /* storage of q and the indexer-K cache */
+} dsa_indexer_shape;
+
+typedef struct {
+  int32_t T;                    /* query tokens per sequence, >= 1 */
+  int32_t heads;                /* attention heads H: a multiple of 16, 16..128 */
+  int32_t dim_qk;               /* must be DSA_DIM_QK */
+  int32_t dim_v;                /* must be DSA_DIM_V */
+  int32_t top_k;                /* row length of the index tensor, 1..DSA_MAX_TOP_K */
+  float sm_scale;               /* softmax scale applied to q.k (e.g. 1/sqrt(576)) */
+} dsa_attn_shape;
+
+/* Bytes of workspace dsa_indexer_topk needs for this layout and shape (0 on invalid input). */
+size_t dsa_indexer_workspace_size(const dsa_paged_layout *layout, const dsa_indexer_shape *shape);
+
+/* Lightning Indexer with fused Top-K ([P1] §1 DSA steps 1-2; [P1] §2 "Single Fused Kernel":
+ * score, head weighting and Top-K keep their intermediates on chip and only the selected indices
+ * are output; [P3] §3.1, bf16 and quantised indexer paths in prefill and decode).
+ *
+ * For every query row (b, t) it computes, for each visible key s (0 <= s <= pos),
+ *     I[s] = sum_h w[b,t,h] * max(0, q[b,t,h,:] . k[s,:])
+ * (fp8: q = q_scale[b,t,h] * e4m3(q code), k = k_scale[page of s] * e4m3(k code)), keeps the
+ * K' = min(top_k, pos + 1) largest scores with ties going to the lower position, and writes
+ * those positions in ascending order followed by -1 up to top_k.  Scores are accumulated in fp32.
+ *
+ *   q        [batch, T, heads, dim]  bf16 or e4m3, 16-byte aligned
+ *   q_scale  [batch, T, heads] fp32 > 0 for DSA_FP8_E4M3, else must be NULL; 4-byte aligned
+ *   w        [batch, T, heads] fp32 head weights, 4-byte aligned
+ *   k_cache  [num_pages, page_size, dim] bf16 or e4m3 (same dtype as q), 16-byte aligned
+ *   k_scale  [num_pages] fp32 > 0, one per page, for DSA_FP8_E4M3, else must be NULL
+ *   idx_out  [batch, T, top_k] int32 logical positions, ascending, -1 padded; 4-byte aligned
+ *   workspace / workspace_bytes: device scratch, 256-byte aligned, at least
+ *            dsa_indexer_workspace_size() bytes; contents on entry are ignored.
+ */
+dsa_status dsa_indexer_topk(const void *q, const float *q_scale, const float *w,
+                            const void *k_cache, const float *k_scale,
+                            const dsa_paged_layout *layout, const dsa_indexer_shape *shape,
+                            int32_t *idx_out, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Bytes of workspace dsa_sparse_attn needs for this layout and shape (0 on invalid input). */
+size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_attn_shape *shape);
+
+/* Sparse Flash Attention ([P1] §1 DSA step 3: read the KV cache at the selected indices and
+ * attend over them; [P1] §2: indices resolve to pages in place; [P2] "Inheritance and Extension
+ * of Core Operators": blockwise attention with a cross-block reduction that reproduces the
+ * global softmax).
+ *
+ * For each query row (b, t) with selected set S = { idx[b,t,j] : idx[b,t,j] >= 0 } and each head h:
+ *     z_j = sm_scale * q[b,t,h,:] . X[s_j,:]     (X = 576-wide latent row of token s_j)
+ *     out[b,t,h,:] = sum_j softmax(z)_j * X[s_j, 0:512],   lse[b,t,h] = ln sum_j exp(z_j)
+ * with fp32 accumulation; out is rounded to bf16 (round to nearest even).  An empty set gives
+ * out = 0 and lse = -inf.  Entries outside [0, seq_lens[b]) are treated as -1.
+ *
+ *   q         [batch, T, heads, 576] bf16 (MLA-absorbed query), 16-byte aligned
+ *   kv_cache  [num_pages, page_size, 576] bf16 latent rows, 16-byte aligned
+ *   idx       [batch, T, top_k] int32, -1 = skip; entries of a row must be unique
+ *   out       [batch, T, heads, 512] bf16, 16-byte aligned
+ *   lse       [batch, T, heads] fp32 natural-log LSE, or NULL
+ *   workspace / workspace_bytes: device scratch, 256-byte aligned, at least
+ *             dsa_sparse_attn_workspace_size() bytes (may be 0 / NULL when that size is 0).
+ */
+dsa_status dsa_sparse_attn(const void *q, const void *kv_cache, const int32_t *idx,
+                           const dsa_paged_layout *layout, const dsa_attn_shape *shape,
+                           void *out, float *lse, void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Thread-local text describing the last non-OK status returned on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* DSA_VERSION of the library. */
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,13 @@
+"""MI355X (gfx950) DSA hot path: Lightning Indexer with fused Top-K and Sparse Flash Attention.
+
+The computation lives in hand-written HIP kernels behind the C ABI of include/dsa.h (libdsa.so,
+built in-tree by sparse_attention_15_amd.build).  This package only marshals torch tensors into
+that ABI; it has no fallback path.
+"""
+from ._lib import (DSA_BF16, DSA_FP8_E4M3, AttnShape, DsaError, IndexerShape, Layout,  # noqa: F401
+                   dsa_indexer_topk, dsa_indexer_workspace_size, dsa_sparse_attn,
+                   dsa_sparse_attn_workspace_size, lib, make_layout)
+
+__all__ = ["dsa_indexer_topk", "dsa_sparse_attn", "dsa_indexer_workspace_size",
+           "dsa_sparse_attn_workspace_size", "DsaError", "Layout", "IndexerShape", "AttnShape",
+           "make_layout", "lib"]

@@ -1,0 +1,163 @@
+"""ctypes binding of libdsa.so (C ABI in include/dsa.h).
+
+Argument marshalling only: torch tensors become device pointers plus sizes, and the current HIP
+stream is passed through.  Every step of the computation runs in the HIP kernels behind the C ABI;
+nothing here computes.  Loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+DSA_OK = 0
+DSA_BF16 = 0
+DSA_FP8_E4M3 = 1
+PAGE_SIZE = 64
+DIM_QK = 576
+DIM_V = 512
+_STATUS = {0: "DSA_OK", 1: "DSA_ERR_NULL", 2: "DSA_ERR_SHAPE", 3: "DSA_ERR_ALIGN",
+           4: "DSA_ERR_UNSUPPORTED", 5: "DSA_ERR_WORKSPACE", 6: "DSA_ERR_HIP"}
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32)]
+
+
+class IndexerShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int)]
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim_qk", ctypes.c_int32),
+                ("dim_v", ctypes.c_int32), ("top_k", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
+           "dsa_sparse_attn", "dsa_last_error", "dsa_version"]
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} not found: build it first "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    L.dsa_indexer_workspace_size.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(IndexerShape)]
+    L.dsa_indexer_workspace_size.restype = sz
+    L.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(Layout),
+                                   ctypes.POINTER(IndexerShape), vp, vp, sz, vp]
+    L.dsa_indexer_topk.restype = ctypes.c_int
+    L.dsa_sparse_attn_workspace_size.argtypes = [ctypes.POINTER(Layout), ctypes.POINTER(AttnShape)]
+    L.dsa_sparse_attn_workspace_size.restype = sz
+    L.dsa_sparse_attn.argtypes = [vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
+                                  vp, vp, vp, sz, vp]
+    L.dsa_sparse_attn.restype = ctypes.c_int
+    L.dsa_last_error.argtypes = []
+    L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_version.argtypes = []
+    L.dsa_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        raise DsaError(status, lib().dsa_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def make_layout(block_table: torch.Tensor, seq_lens: torch.Tensor, num_pages: int,
+                max_seq_len: int) -> Layout:
+    B, max_pages = block_table.shape
+    return Layout(block_table.data_ptr(), seq_lens.data_ptr(), B, max_pages, PAGE_SIZE,
+                  int(num_pages), int(max_seq_len))
+
+
+def dsa_indexer_workspace_size(layout: Layout, shape: IndexerShape) -> int:
+    return int(lib().dsa_indexer_workspace_size(ctypes.byref(layout), ctypes.byref(shape)))
+
+
+def dsa_sparse_attn_workspace_size(layout: Layout, shape: AttnShape) -> int:
+    return int(lib().dsa_sparse_attn_workspace_size(ctypes.byref(layout), ctypes.byref(shape)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch allocations are at least 256-byte aligned
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def dsa_indexer_topk(q, q_scale, w, k_cache, k_scale, block_table, seq_lens, *, T: int, top_k: int,
+                     num_pages: int | None = None, max_seq_len: int, fp8: bool = False,
+                     idx_out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Lightning Indexer + Top-K.  q [B,T,HI,DI] (bf16 or uint8 e4m3 codes), w [B,T,HI] fp32,
+    k_cache [P,64,DI], block_table [B,max_pages] int32, seq_lens [B] int32 (device tensors).
+    Returns idx_out [B,T,top_k] int32."""
+    B, Tq, HI, DI = q.shape
+    assert Tq == T
+    P = k_cache.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    shape = IndexerShape(T, HI, DI, top_k, DSA_FP8_E4M3 if fp8 else DSA_BF16)
+    if idx_out is None:
+        idx_out = torch.empty((B, T, top_k), dtype=torch.int32, device=q.device)
+    need = dsa_indexer_workspace_size(layout, shape)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _check(lib().dsa_indexer_topk(_ptr(q), _ptr(q_scale), _ptr(w), _ptr(k_cache), _ptr(k_scale),
+                                  ctypes.byref(layout), ctypes.byref(shape), _ptr(idx_out),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)))
+    return idx_out
+
+
+def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float, max_seq_len: int,
+                    num_pages: int | None = None, out=None, lse=None, want_lse: bool = True,
+                    workspace=None, stream=None):
+    """Sparse attention.  q [B,T,H,576] bf16, kv_cache [P,64,576] bf16, idx [B,T,K] int32.
+    Returns (out [B,T,H,512] bf16, lse [B,T,H] fp32 or None)."""
+    B, T, H, D = q.shape
+    K = idx.shape[-1]
+    P = kv_cache.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    shape = AttnShape(T, H, D, DIM_V, K, float(sm_scale))
+    if out is None:
+        out = torch.empty((B, T, H, DIM_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    need = dsa_sparse_attn_workspace_size(layout, shape)
+    if workspace is None and need > 0:
+        workspace = _workspace(need, q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_sparse_attn(_ptr(q), _ptr(kv_cache), _ptr(idx), ctypes.byref(layout),
+                                 ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
+                                 _stream(stream)))
+    return out, lse

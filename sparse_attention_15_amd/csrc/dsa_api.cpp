@@ -1,0 +1,152 @@
+// dsa_api.cpp -- the C ABI declared in include/dsa.h: host-side validation, workspace sizing and
+// dispatch to the gfx950 kernels.  Nothing here allocates device memory or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dsa_status check_layout(const dsa_paged_layout* L, int T) {
+  if (L == nullptr) return fail(DSA_ERR_NULL, "layout is NULL");
+  if (L->block_table == nullptr || L->seq_lens == nullptr)
+    return fail(DSA_ERR_NULL, "layout.block_table / layout.seq_lens is NULL");
+  if (!aligned(L->block_table, 4) || !aligned(L->seq_lens, 4))
+    return fail(DSA_ERR_ALIGN, "block_table / seq_lens must be 4-byte aligned");
+  if (L->page_size != DSA_PAGE_SIZE)
+    return fail(DSA_ERR_UNSUPPORTED, "page_size %d unsupported (only %d)", L->page_size, DSA_PAGE_SIZE);
+  if (L->batch < 1) return fail(DSA_ERR_SHAPE, "batch %d < 1", L->batch);
+  if (L->num_pages < 1) return fail(DSA_ERR_SHAPE, "num_pages %d < 1", L->num_pages);
+  if (L->max_seq_len < T) return fail(DSA_ERR_SHAPE, "max_seq_len %d < T %d", L->max_seq_len, T);
+  if (L->max_seq_len > (1 << 20)) return fail(DSA_ERR_UNSUPPORTED, "max_seq_len %d > 1048576", L->max_seq_len);
+  if ((long long)L->max_pages * L->page_size < L->max_seq_len)
+    return fail(DSA_ERR_SHAPE, "max_pages %d * page_size too small for max_seq_len %d", L->max_pages, L->max_seq_len);
+  return DSA_OK;
+}
+
+dsa_status check_indexer_shape(const dsa_indexer_shape* S) {
+  if (S == nullptr) return fail(DSA_ERR_NULL, "shape is NULL");
+  if (S->T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", S->T);
+  if (S->top_k < 1 || S->top_k > DSA_MAX_TOP_K)
+    return fail(DSA_ERR_UNSUPPORTED, "top_k %d outside 1..%d", S->top_k, DSA_MAX_TOP_K);
+  if (S->dtype != DSA_BF16 && S->dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)S->dtype);
+  if (!dsa::indexer_supported(S->heads, S->dim))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer heads %d x dim %d unsupported (heads 8/16/32/64, dim 64/128)", S->heads, S->dim);
+  return DSA_OK;
+}
+
+dsa_status check_attn_shape(const dsa_attn_shape* S) {
+  if (S == nullptr) return fail(DSA_ERR_NULL, "shape is NULL");
+  if (S->T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", S->T);
+  if (S->dim_qk != DSA_DIM_QK || S->dim_v != DSA_DIM_V)
+    return fail(DSA_ERR_UNSUPPORTED, "dims %d/%d unsupported (only %d/%d)", S->dim_qk, S->dim_v, DSA_DIM_QK, DSA_DIM_V);
+  if (S->heads < 16 || S->heads > 128 || S->heads % 16 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "attention heads %d unsupported (multiple of 16, 16..128)", S->heads);
+  if (S->top_k < 1 || S->top_k > DSA_MAX_TOP_K)
+    return fail(DSA_ERR_UNSUPPORTED, "top_k %d outside 1..%d", S->top_k, DSA_MAX_TOP_K);
+  if (!(S->sm_scale == S->sm_scale) || S->sm_scale <= 0.f || S->sm_scale > 1e4f)
+    return fail(DSA_ERR_SHAPE, "sm_scale must be finite and > 0");
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_version(void) { return DSA_VERSION; }
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+size_t dsa_indexer_workspace_size(const dsa_paged_layout* layout, const dsa_indexer_shape* shape) {
+  if (check_indexer_shape(shape) != DSA_OK || check_layout(layout, shape->T) != DSA_OK) return 0;
+  return dsa::plan_indexer(*layout, *shape).total;
+}
+
+dsa_status dsa_indexer_topk(const void* q, const float* q_scale, const float* w, const void* k_cache,
+                            const float* k_scale, const dsa_paged_layout* layout,
+                            const dsa_indexer_shape* shape, int32_t* idx_out, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_indexer_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_layout(layout, shape->T)) != DSA_OK) return st;
+  const bool fp8 = shape->dtype == DSA_FP8_E4M3;
+  if (q == nullptr || w == nullptr || k_cache == nullptr || idx_out == nullptr)
+    return fail(DSA_ERR_NULL, "q / w / k_cache / idx_out is NULL");
+  if (fp8 && (q_scale == nullptr || k_scale == nullptr))
+    return fail(DSA_ERR_NULL, "fp8 indexer needs q_scale and k_scale");
+  if (!fp8 && (q_scale != nullptr || k_scale != nullptr))
+    return fail(DSA_ERR_SHAPE, "q_scale / k_scale must be NULL for the bf16 indexer");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(w, 4) || !aligned(idx_out, 4) ||
+      (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4))))
+    return fail(DSA_ERR_ALIGN, "q / k_cache need 16-byte alignment, w / scales / idx_out 4-byte");
+  const dsa::IndexerPlan plan = dsa::plan_indexer(*layout, *shape);
+  if (workspace == nullptr || workspace_bytes < plan.total)
+    return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total);
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+
+  dsa::IndexerArgs a;
+  a.q = q; a.q_scale = q_scale; a.w = w; a.k_cache = k_cache; a.k_scale = k_scale;
+  a.block_table = layout->block_table; a.seq_lens = layout->seq_lens;
+  a.B = layout->batch; a.T = shape->T; a.max_pages = layout->max_pages; a.num_pages = layout->num_pages;
+  a.max_seq_len = layout->max_seq_len;
+  a.heads = shape->heads; a.dim = shape->dim; a.top_k = shape->top_k; a.fp8 = fp8;
+  a.idx_out = idx_out; a.workspace = workspace;
+  const hipError_t e = dsa::launch_indexer(a, plan, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "indexer launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout* layout, const dsa_attn_shape* shape) {
+  if (check_attn_shape(shape) != DSA_OK || check_layout(layout, shape->T) != DSA_OK) return 0;
+  return dsa::plan_attn(*layout, *shape).total;
+}
+
+dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* idx,
+                           const dsa_paged_layout* layout, const dsa_attn_shape* shape, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dsa_status st = check_attn_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_layout(layout, shape->T)) != DSA_OK) return st;
+  if (q == nullptr || kv_cache == nullptr || idx == nullptr || out == nullptr)
+    return fail(DSA_ERR_NULL, "q / kv_cache / idx / out is NULL");
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return fail(DSA_ERR_ALIGN, "q / kv_cache / out need 16-byte alignment, idx / lse 4-byte");
+  const dsa::AttnPlan plan = dsa::plan_attn(*layout, *shape);
+  if (plan.total > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.total)
+      return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total);
+    if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  dsa::AttnArgs a;
+  a.q = q; a.kv_cache = kv_cache; a.idx = idx;
+  a.block_table = layout->block_table; a.seq_lens = layout->seq_lens;
+  a.B = layout->batch; a.T = shape->T; a.max_pages = layout->max_pages; a.num_pages = layout->num_pages;
+  a.max_seq_len = layout->max_seq_len;
+  a.heads = shape->heads; a.top_k = shape->top_k; a.sm_scale = shape->sm_scale;
+  a.out = out; a.lse = lse; a.workspace = workspace;
+  const hipError_t e = dsa::launch_attn(a, plan, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// dsa_device.h -- device-side building blocks shared by the gfx950 kernels of this library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kPage = 64;          // tokens per cache page
+constexpr int kDimQK = 576;        // latent row width
+constexpr int kDimV = 512;         // V columns of the latent row
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+// 32x32 output tile, K = 16 bf16 per instruction.  Lane l supplies A[m = l%32][k = 8(l/32)..+7]
+// and B[k = 8(l/32)..+7][n = l%32]; accumulator register r of lane l holds
+// C[m = 8(r/4) + 4(l/32) + r%4][n = l%32].
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// Same tile shape with K = 16 e4m3 values (8 bytes) per lane and operand.
+__device__ __forceinline__ f32x16 mfma_fp8(long a, long b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 is folded onto +0 so the
+// two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64).  `sh` holds NT/64
+// words of LDS.  Returns this thread's exclusive prefix and the workgroup total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    uint32_t s = sh[i];
+    pre += (i < wid) ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + x - v;
+}
+
+// Length of query row (b, t): keys 0..pos are visible, pos = seq_len - T + t.  seq_len is clamped
+// to the block-table capacity so a bad length can never address past the table.
+__device__ __forceinline__ int row_visible(const int32_t* seq_lens, int b, int T, int t, int cap) {
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  int n = L - T + t + 1;
+  return n < 0 ? 0 : n;
+}
+
+__device__ __forceinline__ int clamp_page(int p, int num_pages) {
+  return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+}
+
+}  // namespace dsa

@@ -1,0 +1,64 @@
+// dsa_internal.h -- host-side interface between the C ABI (dsa_api.cpp) and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// Workspace carving and grid sizes of one dsa_indexer_topk call.
+struct IndexerPlan {
+  int rows = 0;          // batch * T query rows
+  int row_stride = 0;    // u32 keys per row in the score scratch
+  int n_slices = 0;      // select-phase-1 slices per row
+  int gt_cap = 0;        // per-slice capacity of the "above the threshold bin" list
+  int n_chunks = 0;      // key chunks per sequence in the score grid
+  int tq = 1;            // query rows sharing one pass over the keys (1, 2 or 4)
+  int n_qtiles = 0;      // ceil(T / tq)
+  size_t off_hist = 0, off_keys = 0, off_gt = 0, off_cand = 0, off_cnt = 0, total = 0;
+};
+
+struct IndexerArgs {
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  const void* k_cache;
+  const float* k_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int B, T, max_pages, num_pages, max_seq_len, heads, dim, top_k;
+  bool fp8;
+  int32_t* idx_out;
+  void* workspace;
+};
+
+IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S);
+bool indexer_supported(int heads, int dim);
+hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t stream);
+
+struct AttnPlan {
+  int waves = 1;         // waves per workgroup (32 heads each)
+  int n_splits = 1;      // workgroups per query row along the selected set
+  int keys_per_split = 0;
+  size_t off_ml = 0, off_part = 0, total = 0;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* kv_cache;
+  const int32_t* idx;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int B, T, max_pages, num_pages, max_seq_len, heads, top_k;
+  float sm_scale;
+  void* out;
+  float* lse;
+  void* workspace;
+};
+
+AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S);
+hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,112 @@
+"""Helpers shared by the GPU parity tests: upload a synthetic case, run the HIP path through the
+C ABI, and the comparison gates.
+
+Gates (written here, used by every parity test):
+  * indices, exact-arithmetic cases (integer grids): the whole [B,T,K] int32 array must match the
+    oracle, order and -1 padding included;
+  * indices, Gaussian cases: with theta the oracle's K'-th score and
+    tau = max(1e-3 |theta|, 1e-6 max|I|), the GPU row must hold K' distinct positions in [0, pos],
+    contain every s with I[s] > theta + tau and none with I[s] < theta - tau (rows with
+    n <= K must equal 0..n-1 exactly);
+  * attention (always on one shared index tensor): G1 |o - o_ref| <= 2e-2 + 2e-2 |o_ref|
+    elementwise; G2 max_d |o - o_ref| <= 2e-2 max_d |o_ref| per (b, t, h); G3
+    |lse - lse_ref| <= 1e-3 max(1, |lse_ref|).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import sparse_attention_15_amd as dsa
+
+DEV = torch.device("cuda:0")
+
+
+def up(a: np.ndarray, dtype=None) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+class Dev:
+    """A case's tensors in device memory."""
+
+    def __init__(self, c):
+        self.c = c
+        s = c.spec
+        self.bt = up(c.block_table)
+        self.sl = up(c.seq_lens)
+        self.q_idx = up(c.q_idx)
+        self.w = up(c.w)
+        self.k = up(c.k_cache)
+        self.q_scale = None if c.q_scale is None else up(c.q_scale)
+        self.k_scale = None if c.k_scale is None else up(c.k_scale)
+        self.q_attn = up(c.q_attn)
+        self.kv = up(c.kv_cache)
+        self.fp8 = s.idx_dtype == "fp8"
+
+    def indexer(self, **kw) -> torch.Tensor:
+        s = self.c.spec
+        return dsa.dsa_indexer_topk(self.q_idx, self.q_scale, self.w, self.k, self.k_scale, self.bt,
+                                    self.sl, T=s.T, top_k=s.K, max_seq_len=s.max_len, fp8=self.fp8,
+                                    num_pages=self.c.num_pages, **kw)
+
+    def attn(self, idx, **kw):
+        s = self.c.spec
+        if isinstance(idx, np.ndarray):
+            idx = up(idx.astype(np.int32))
+        return dsa.dsa_sparse_attn(self.q_attn, self.kv, idx, self.bt, self.sl, sm_scale=s.sm_scale,
+                                   max_seq_len=s.max_len, num_pages=self.c.num_pages, **kw)
+
+
+def oracle_args(c):
+    return dict(q_idx=c.q_idx, q_scale=c.q_scale, w=c.w, k_cache=c.k_cache, k_scale=c.k_scale,
+                block_table=c.block_table, seq_lens=c.seq_lens)
+
+
+def check_indices_band(got: np.ndarray, ref: np.ndarray, extra: dict, K: int, seq_lens, T: int,
+                       rows=None) -> int:
+    """Near-tie gate for Gaussian cases; returns the number of band swaps."""
+    swaps = 0
+    B = got.shape[0]
+    rows = rows if rows is not None else [(b, t) for b in range(B) for t in range(T)]
+    for b, t in rows:
+        n = int(seq_lens[b]) - T + t + 1
+        g = got[b, t]
+        if n <= K:
+            assert np.array_equal(g, np.r_[np.arange(n), -np.ones(K - n)].astype(np.int32)), (b, t)
+            continue
+        sc, theta = extra[(b, t)]
+        assert np.all(g >= 0) and np.all(g < n), f"row ({b},{t}): positions outside [0, {n})"
+        assert np.all(np.diff(g) > 0), f"row ({b},{t}): not strictly ascending"
+        tau = max(1e-3 * abs(theta), 1e-6 * float(np.abs(sc).max()))
+        must = np.nonzero(sc > theta + tau)[0]
+        never = sc < theta - tau
+        gs = set(g.tolist())
+        assert set(must.tolist()) <= gs, f"row ({b},{t}): missing clear winners"
+        assert not never[g].any(), f"row ({b},{t}): selected a clear loser"
+        swaps += len(gs.symmetric_difference(set(ref[b, t].tolist()))) // 2
+    return swaps
+
+
+def check_attn(o: np.ndarray, lse: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray, rows=None):
+    if rows is not None:
+        bi = np.array([r[0] for r in rows]); ti = np.array([r[1] for r in rows])
+        o, lse, o_ref, lse_ref = o[bi, ti], lse[bi, ti], o_ref[bi, ti], lse_ref[bi, ti]
+    assert np.isfinite(o).all(), "non-finite attention output"
+    err = np.abs(o - o_ref)
+    assert np.all(err <= 2e-2 + 2e-2 * np.abs(o_ref)), f"G1 max err {err.max()}"
+    scale = np.abs(o_ref).max(axis=-1, keepdims=True)
+    assert np.all(err.max(axis=-1, keepdims=True) <= 2e-2 * scale + 1e-30), \
+        f"G2 worst ratio {(err.max(-1) / np.maximum(scale[..., 0], 1e-30)).max()}"
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= 1e-3 * np.maximum(1.0, np.abs(lse_ref[fin]))), \
+        f"G3 max err {np.abs(lse[fin] - lse_ref[fin]).max()}"
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()

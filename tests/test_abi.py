@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function that
+include/dsa.h declares, sizes workspaces, and rejects bad arguments before launching anything.
+Rejected calls never touch device memory, so fake (never dereferenced) pointers are safe here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_15_amd as dsa
+from sparse_attention_15_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libdsa.so not built")
+
+FAKE = 0x7000_0000_0000   # 256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dsa_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"dsa_indexer_topk", "dsa_sparse_attn", "dsa_indexer_workspace_size",
+            "dsa_sparse_attn_workspace_size", "dsa_last_error", "dsa_version"} <= set(names)
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+    assert dsa.lib().dsa_version() == 1
+
+
+def _layout(B=2, max_pages=4, max_len=256, num_pages=9, page=64):
+    return L.Layout(FAKE, FAKE + 256, B, max_pages, page, num_pages, max_len)
+
+
+def _ishape(T=1, H=64, D=128, K=64, dt=0):
+    return L.IndexerShape(T, H, D, K, dt)
+
+
+def _ashape(T=1, H=128, K=64, scale=0.05):
+    return L.AttnShape(T, H, 576, 512, K, scale)
+
+
+def test_workspace_sizes():
+    lib = dsa.lib()
+    ws = dsa.dsa_indexer_workspace_size(_layout(), _ishape())
+    assert ws > 0 and ws % 256 == 0
+    # bigger context -> bigger workspace; invalid shape -> 0
+    assert dsa.dsa_indexer_workspace_size(_layout(max_pages=128, max_len=8192), _ishape()) > ws
+    assert dsa.dsa_indexer_workspace_size(_layout(), _ishape(H=12)) == 0
+    assert dsa.dsa_indexer_workspace_size(_layout(page=32), _ishape()) == 0
+    assert lib.dsa_sparse_attn_workspace_size(ctypes.byref(_layout()), ctypes.byref(_ashape(K=2048))) > 0
+    assert dsa.dsa_sparse_attn_workspace_size(_layout(), _ashape(H=100)) == 0
+
+
+def _idx_call(q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, layout=None, shape=None, out=FAKE,
+              ws=FAKE, wsb=1 << 40):
+    lib = dsa.lib()
+    layout = layout or _layout()
+    shape = shape or _ishape()
+    return lib.dsa_indexer_topk(q, qs, w, k, ks, ctypes.byref(layout), ctypes.byref(shape), out,
+                                ws, wsb, None)
+
+
+def _attn_call(q=FAKE, kv=FAKE, idx=FAKE, layout=None, shape=None, out=FAKE, lse=None, ws=FAKE,
+               wsb=1 << 40):
+    lib = dsa.lib()
+    layout = layout or _layout()
+    shape = shape or _ashape()
+    return lib.dsa_sparse_attn(q, kv, idx, ctypes.byref(layout), ctypes.byref(shape), out, lse, ws,
+                               wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(w=None), 1), (dict(k=None), 1), (dict(out=None), 1),
+    (dict(q=FAKE + 8), 3), (dict(k=FAKE + 4), 3), (dict(w=FAKE + 2), 3),
+    (dict(shape=_ishape(H=12)), 4), (dict(shape=_ishape(D=96)), 4), (dict(shape=_ishape(K=0)), 4),
+    (dict(shape=_ishape(K=4096)), 4), (dict(shape=_ishape(T=0)), 2),
+    (dict(shape=_ishape(dt=1)), 1),                       # fp8 without scales
+    (dict(qs=FAKE, ks=FAKE), 2),                          # scales given for bf16
+    (dict(layout=_layout(page=128)), 4), (dict(layout=_layout(B=0)), 2),
+    (dict(layout=_layout(max_pages=2, max_len=256)), 2),  # table too short for max_len
+    (dict(layout=_layout(max_len=0)), 2),                 # max_len < T
+    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(ws=FAKE + 64), 3),
+])
+def test_indexer_rejects(kw, status):
+    assert _idx_call(**kw) == status
+    assert dsa.lib().dsa_last_error().decode() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(q=FAKE + 2), 3), (dict(out=FAKE + 8), 3), (dict(lse=FAKE + 2), 3),
+    (dict(shape=_ashape(H=100)), 4), (dict(shape=_ashape(H=256)), 4),
+    (dict(shape=L.AttnShape(1, 128, 512, 512, 64, 0.1)), 4),
+    (dict(shape=_ashape(K=0)), 4), (dict(shape=_ashape(scale=0.0)), 2),
+    (dict(shape=_ashape(scale=float("nan"))), 2),
+    (dict(layout=_layout(num_pages=0)), 2),
+    (dict(shape=_ashape(K=2048), ws=None), 5),
+])
+def test_attn_rejects(kw, status):
+    assert _attn_call(**kw) == status
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        L.lib()

@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Sizes span several score chunks (1024 keys), select slices (4096 keys), attention tiles (32 rows)
+and splits, with ragged tails (lengths not multiples of 64).  Exact-arithmetic cases (integer grids,
+exact fp8 grid) must match the oracle's indices bit for bit; Gaussian cases use the near-tie band.
+Attention is always compared on one shared index tensor (the GPU's own indices).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests._gpu import Dev, check_attn, check_indices_band, oracle_args, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(spec, exact, sfa_rows=None, check_sfa=True):
+    print(f"[case] {spec.name} B={spec.B} T={spec.T} lens={spec.lens[:4]} K={spec.K} "
+          f"{spec.idx_dtype}/{spec.values}", flush=True)
+    c = W.make_case(spec)
+    d = Dev(c)
+    idx_t = d.indexer()
+    torch.cuda.synchronize()
+    idx = to_np(idx_t)
+    dt = "fp8" if spec.idx_dtype == "fp8" else "bf16"
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype=dt,
+                                         return_scores=True)
+    if exact:
+        bad = np.nonzero((idx != ref).any(axis=-1))
+        assert np.array_equal(idx, ref), f"index mismatch in rows {list(zip(*bad))[:5]}"
+    else:
+        check_indices_band(idx, ref, extra, spec.K, c.seq_lens, spec.T)
+    if check_sfa:
+        out, lse = d.attn(idx_t)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
+                                              spec.sm_scale, rows=sfa_rows)
+        check_attn(to_np(out), to_np(lse), o_ref, l_ref, rows=sfa_rows)
+    return c, d, idx
+
+
+# ---------------------------------------------------------------- the five workloads (small size)
+def test_cfg1_decode_grid_exact():
+    _run(W.config(1), exact=True)
+
+
+def test_cfg2_small_ragged_decode():
+    _run(W.config(2, "small"), exact=False)
+
+
+def test_cfg3_small_causal_prefill():
+    spec = W.config(3, "small")
+    rows = [(0, t) for t in (0, 1, 63, 64, 100, 1000, 2046, 2047, 2048, 2049, 2200, 2303)]
+    _run(spec, exact=False, sfa_rows=rows)
+
+
+def test_cfg4_small_fp8_decode():
+    _run(W.config(4, "small"), exact=False)
+
+
+def test_cfg5_small_verify():
+    _run(W.config(5, "small"), exact=False)
+
+
+# ---------------------------------------------------------------- exact-arithmetic variants
+@pytest.mark.parametrize("T,lens", [(1, (3000, 5000)), (4, (2600, 4500))])
+def test_wide_grid_exact(T, lens):
+    spec = W.custom("grid8_wide", len(lens), T, lens, 64, 128, 2048, 128, values="grid8")
+    _run(spec, exact=True)
+
+
+def test_tie_heavy_exact():
+    spec = W.custom("ties_wide", 2, 1, (3500, 6000), 64, 128, 2048, 128, values="ties")
+    _run(spec, exact=True, check_sfa=False)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_fp8_grid_exact(T):
+    spec = W.custom("fp8grid", 2, T, (2500, 4100), 64, 128, 2048, 128, idx_dtype="fp8",
+                    values="fp8grid")
+    _run(spec, exact=True)
+
+
+@pytest.mark.parametrize("HI,DI,K", [(8, 64, 256), (16, 128, 100), (32, 64, 512), (64, 64, 1)])
+def test_other_indexer_shapes_exact(HI, DI, K):
+    spec = W.custom(f"grid_{HI}x{DI}", 2, 2, (1500, 777), HI, DI, K, 16, values="grid8")
+    _run(spec, exact=True)
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("T,lens,K", [
+    (1, (100, 2048, 2049, 1), 2048),     # n < K, n == K, n == K + 1, a single token
+    (4, (5, 70, 4), 8),                  # T = 4 with tiny contexts (n = 1 .. 70)
+    (2, (65, 129, 4095, 4097), 64),      # page and slice boundaries
+])
+def test_edge_lengths_exact(T, lens, K):
+    spec = W.custom("edges", len(lens), T, lens, 64, 128, K, 32, values="grid8")
+    _run(spec, exact=True)
+
+
+def test_page_permutation_and_determinism():
+    spec = W.config(2, "small")
+    c = W.make_case(spec)
+    d1 = Dev(c)
+    i1 = d1.indexer(); o1, l1 = d1.attn(i1)
+    i1b = d1.indexer(); o1b, l1b = d1.attn(i1b)
+    d2 = Dev(W.permute_pages(c))
+    i2 = d2.indexer(); o2, l2 = d2.attn(i2)
+    torch.cuda.synchronize()
+    for x, y in [(i1, i1b), (o1, o1b), (l1, l1b), (i1, i2), (o1, o2), (l1, l2)]:
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
+
+
+# ---------------------------------------------------------------- attention closed forms
+def _attn_case(H=128, lens=(700, 300), T=1, values="sharp"):
+    return W.make_case(W.custom("attn", len(lens), T, lens, 8, 64, 64, H, values=values,
+                                sharp_c=3.0))
+
+
+def test_attn_single_row_is_v_row_bitexact():
+    c = _attn_case()
+    d = Dev(c)
+    idx = np.full((2, 1, 64), -1, np.int32)
+    idx[0, 0, 0] = 650
+    idx[1, 0, 0] = 3
+    out, lse = d.attn(idx)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, s in [(0, 650), (1, 3)]:
+        row = c.kv_cache[c.block_table[b, s // 64], s % 64, :512]
+        assert np.array_equal(o[b, 0], np.broadcast_to(row, o[b, 0].shape))
+
+
+def test_attn_empty_rows_and_equal_logits():
+    c = _attn_case(H=48, values="gauss")
+    c.q_attn[1] = 0                       # sequence 1: all logits 0 -> mean of V
+    d = Dev(c)
+    idx = np.full((2, 1, 96), -1, np.int32)
+    sel = np.array([0, 5, 64, 65, 128, 200, 299])
+    idx[1, 0, :7] = sel
+    out, lse = d.attn(idx)
+    torch.cuda.synchronize()
+    o, l = to_np(out), to_np(lse)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx, 1 / 24)
+    check_attn(o[1:], l[1:], ref[0][1:], ref[1][1:])
+    np.testing.assert_allclose(l[1], np.log(7.0), rtol=1e-5)
+
+
+@pytest.mark.parametrize("B,K", [(1, 2048), (3, 1000), (300, 64)])
+def test_attn_random_index_sets_sharp(B, K):
+    """Random unique index sets (several splits when B is small, none when B is large)."""
+    rng = np.random.default_rng(B)
+    lens = tuple(int(x) for x in rng.integers(K, K + 3000, B))
+    c = W.make_case(W.custom("attn_rand", B, 1, lens, 8, 64, K, 128, values="sharp", sharp_c=1.0))
+    idx = np.full((B, 1, K), -1, np.int32)
+    for b in range(B):
+        m = int(rng.integers(1, K + 1))
+        idx[b, 0, :m] = np.sort(rng.choice(lens[b], m, replace=False))
+    d = Dev(c)
+    out, lse = d.attn(idx)
+    torch.cuda.synchronize()
+    rows = [(b, 0) for b in range(min(B, 40))]
+    o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
+                                          1 / 24, rows=rows)
+    check_attn(to_np(out), to_np(lse), o_ref, l_ref, rows=rows)

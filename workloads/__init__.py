@@ -49,7 +49,7 @@ class CaseSpec:
     K: int                 # top-k
     H: int                 # attention heads
     idx_dtype: str = "bf16"   # "bf16" | "fp8"
-    values: str = "gauss"     # "gauss" | "grid" | "ties" | "fp8grid" | "sharp"
+    values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "fp8grid" | "sharp"
     sharp_c: float = 1.0
     variant: int = 0
     spare_pages: int = 1
@@ -213,14 +213,17 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
 
     # ---- indexer q / k / w
     if spec.idx_dtype == "bf16":
-        if v in ("grid", "ties"):
-            q_idx = _grid_bf16(rngq, (B, T, HI, DI))
+        if v in ("grid", "grid8", "ties"):
+            # grid: multiples of 1/16 in [-1, 1]; grid8: in [-1/2, 1/2], which keeps the wide
+            # (64 heads x 128 dims) scores below 2^11 so fp32 sums are exact in any order
+            lim = 8 if v in ("grid8", "ties") else 16
+            q_idx = _grid_bf16(rngq, (B, T, HI, DI), -lim, lim)
             if v == "ties":
                 # few distinct key rows copied to many positions: many exact score ties
-                base = _grid_bf16(rngk, (7, DI))
+                base = _grid_bf16(rngk, (7, DI), -lim, lim)
                 k_cache = base[rngk.integers(0, 7, size=(P, PAGE))]
             else:
-                k_cache = _grid_bf16(rngk, (P, PAGE, DI))
+                k_cache = _grid_bf16(rngk, (P, PAGE, DI), -lim, lim)
             w = (rngw.integers(0, 16, size=(B, T, HI), endpoint=True) / 16.0).astype(np.float32)
         else:
             q_idx = _gauss_bf16(key0 + [2], (B, T, HI, DI), 1.0 / np.sqrt(DI))
@@ -231,10 +234,11 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
             k_cache[~valid] = BF16_NAN
     elif spec.idx_dtype == "fp8":
         if v == "fp8grid":
-            # integer codes in [-8, 8] (exact in e4m3) with power-of-two scales: exact scores
-            q_idx = f32_to_e4m3_codes(rngq.integers(-8, 8, size=(B, T, HI, DI), endpoint=True))
-            k_cache = f32_to_e4m3_codes(rngk.integers(-8, 8, size=(P, PAGE, DI), endpoint=True))
-            q_scale = (2.0 ** rngq.integers(-3, 3, size=(B, T, HI), endpoint=True)).astype(np.float32)
+            # integer codes in [-4, 4] (exact in e4m3) with power-of-two scales, q scales <= 1:
+            # every fp32 partial sum of the score is exact in any order
+            q_idx = f32_to_e4m3_codes(rngq.integers(-4, 4, size=(B, T, HI, DI), endpoint=True))
+            k_cache = f32_to_e4m3_codes(rngk.integers(-4, 4, size=(P, PAGE, DI), endpoint=True))
+            q_scale = (2.0 ** rngq.integers(-3, 0, size=(B, T, HI), endpoint=True)).astype(np.float32)
             k_scale = (2.0 ** rngk.integers(-3, 3, size=P, endpoint=True)).astype(np.float32)
             w = (rngw.integers(0, 16, size=(B, T, HI), endpoint=True) / 16.0).astype(np.float32)
         else:
@@ -256,7 +260,7 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
         raise ValueError(spec.idx_dtype)
 
     # ---- attention q / kv
-    if v in ("grid", "ties", "fp8grid"):
+    if v in ("grid", "grid8", "ties", "fp8grid"):
         q_attn = _grid_bf16(rngs, (B, T, H, DQK))
         kv_cache = _grid_bf16(rngv, (P, PAGE, DQK))
     elif v == "sharp":
