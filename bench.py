@@ -1,0 +1,253 @@
+"""Benchmark of the DSA decode hot path on one MI355X: dsa_indexer_topk followed by dsa_sparse_attn.
+
+One step = one batch of the workload through both calls (all query rows of the batch).  Inputs are
+synthetic (workloads/), resident in HBM before timing, and rotated across copies totalling >= 2 GiB
+of touched bytes so the 256 MiB Infinity Cache cannot serve a step from the previous one.
+
+Prints ONE JSON line on stdout.  Progress goes to stderr.
+
+  value       queries/s over exactly --steps steps (barrier + synchronize on both sides)
+  roofline    the dominant kernel (li_score): algorithmic bytes per launch / its mean duration,
+              from HIP events the library records around each launch during a second, profiled pass
+              over the same steps; peak = 8 TB/s HBM
+  path        whole-step algorithmic bytes / step time, against the same peak
+  cpu_baseline  the float64 CPU oracle timed on this host on the first rows of the same batch
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "indexer+SFA decode queries/sec at 32k ctx, K=2048; achieved HBM GB/s % of peak"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def visible(spec, seq_lens):
+    """Per row (b, t): number of visible keys n."""
+    return [(b, t, int(seq_lens[b]) - spec.T + t + 1) for b in range(spec.B) for t in range(spec.T)]
+
+
+def algorithmic_bytes(spec, seq_lens):
+    """Bytes the method must move per step (no over-fetch, no scratch): see the design doc."""
+    elt = 1 if spec.idx_dtype == "fp8" else 2
+    rows = visible(spec, seq_lens)
+    k_bytes = 0
+    for b in range(spec.B):
+        n = int(seq_lens[b])              # keys read once per sequence, shared by its T queries
+        pages = (n + 63) // 64
+        k_bytes += n * spec.DI * elt + pages * 4 + (pages * 4 if elt == 1 else 0)
+    q_idx = spec.B * spec.T * spec.HI * (spec.DI * elt + 4 + (4 if elt == 1 else 0))
+    li_score = k_bytes + q_idx
+    idx_rw = 2 * spec.B * spec.T * spec.K * 4
+    kp = sum(min(spec.K, n) for _, _, n in rows)
+    sfa = spec.B * spec.T * spec.H * (576 * 2 + 512 * 2 + 4) + kp * 1152
+    return dict(li_score=li_score, step=li_score + idx_rw + sfa, sfa=sfa, kp=kp)
+
+
+def describe(spec):
+    lens = np.asarray(spec.lens)
+    kind = {1: "decode", 2: "decode", 3: "causal prefill", 4: "decode, fp8 indexer",
+            5: "speculative verify"}.get(spec.cfg_id, "custom")
+    return (f"{kind}: B={spec.B} T={spec.T} ctx " +
+            (f"{lens.min()}..{lens.max()} (mean {lens.mean():.0f})" if lens.min() != lens.max() else f"{lens[0]}")
+            + f", K={spec.K}, indexer {spec.HI}x{spec.DI} {spec.idx_dtype}, attention {spec.H} heads 576/512 bf16, page 64")
+
+
+def cpu_baseline(case, max_rows: int, budget_s: float):
+    """Times the float64 oracle on the first rows of the batch (a bounded sample)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    spec = case.spec
+    rows = [(b, t) for b in range(spec.B) for t in range(spec.T)]
+    dt = "fp8" if spec.idx_dtype == "fp8" else "bf16"
+    done, t0 = 0, time.perf_counter()
+    for i in range(0, min(len(rows), max_rows), 1):
+        sel = [rows[i]]
+        idx = oracle.indexer_topk_ref(case.q_idx, case.q_scale, case.w, case.k_cache, case.k_scale,
+                                      case.block_table, case.seq_lens, spec.T, spec.K, dt, rows=sel)
+        oracle.sparse_attn_ref(case.q_attn, case.kv_cache, case.block_table, case.seq_lens, idx,
+                               spec.sm_scale, rows=sel)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "queries/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(rows)} query rows of one step (indexer + attention, float64 "
+                      f"NumPy), {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
+    ap.add_argument("--rotate-gib", type=float, default=2.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a device copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_15_amd as dsa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calib_mib} MiB x5")
+        return
+
+    spec = W.config(args.workload)
+    log("workload", describe(spec))
+    t0 = time.perf_counter()
+    case = W.make_case(spec)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f}s")
+    ab = algorithmic_bytes(spec, case.seq_lens)
+    R = max(1, math.ceil(args.rotate_gib * 2 ** 30 / ab["step"]))
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    fp8 = spec.idx_dtype == "fp8"
+    base = dict(q=up(case.q_idx), w=up(case.w), k=up(case.k_cache),
+                qs=None if case.q_scale is None else up(case.q_scale),
+                ks=None if case.k_scale is None else up(case.k_scale),
+                qa=up(case.q_attn), kv=up(case.kv_cache))
+    copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(R - 1)]
+    bt, sl = up(case.block_table), up(case.seq_lens)
+    log(f"uploaded {R} rotation copies ({ab['step'] * R / 2 ** 30:.2f} GiB of touched bytes)")
+
+    layout = dsa.make_layout(bt, sl, case.num_pages, spec.max_len)
+    ishape = dsa.IndexerShape(spec.T, spec.HI, spec.DI, spec.K, dsa.DSA_FP8_E4M3 if fp8 else dsa.DSA_BF16)
+    ashape = dsa.AttnShape(spec.T, spec.H, 576, 512, spec.K, spec.sm_scale)
+    iws = torch.empty(max(256, dsa.dsa_indexer_workspace_size(layout, ishape)), dtype=torch.uint8, device=dev)
+    aws_n = dsa.dsa_sparse_attn_workspace_size(layout, ashape)
+    aws = torch.empty(max(256, aws_n), dtype=torch.uint8, device=dev)
+    idx = torch.empty((spec.B, spec.T, spec.K), dtype=torch.int32, device=dev)
+    out = torch.empty((spec.B, spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((spec.B, spec.T, spec.H), dtype=torch.float32, device=dev)
+
+    import ctypes
+    L = dsa.lib()
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lref, iref, aref = ctypes.byref(layout), ctypes.byref(ishape), ctypes.byref(ashape)
+    calls = []
+    for c in copies:   # pre-marshalled arguments: the timed loop only issues the two C calls
+        calls.append(((P(c["q"]), P(c["qs"]), P(c["w"]), P(c["k"]), P(c["ks"]), lref, iref, P(idx),
+                       P(iws), iws.numel(), stream),
+                      (P(c["qa"]), P(c["kv"]), P(idx), lref, aref, P(out), P(lse), P(aws), aws.numel(),
+                       stream)))
+
+    def step(i):
+        a, b = calls[i % R]
+        s1 = L.dsa_indexer_topk(*a)
+        s2 = L.dsa_sparse_attn(*b)
+        if s1 or s2:
+            raise RuntimeError(L.dsa_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    qps = spec.B * spec.T / (ms * 1e-3)
+    log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/step, {qps:,.0f} queries/s")
+
+    kernels = {}
+    roof = None
+    if not args.no_profile:
+        dsa.dsa_profile_start()
+        for i in range(args.steps):
+            step(i)
+        prof = dsa.dsa_profile_stop()
+        kernels = {k: {"launches": n, "mean_us": round(1e3 * t / max(n, 1), 2)} for k, (n, t) in prof.items()}
+        log("per-kernel:", json.dumps(kernels))
+        if "li_score" in prof:
+            n, t = prof["li_score"]
+            mean_s = t / n * 1e-3
+            ach = ab["li_score"] / mean_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "li_score",
+                    "kernel_mean_us": round(mean_s * 1e6, 2),
+                    "algorithmic_bytes_per_launch": int(ab["li_score"])}
+
+    path_gbs = ab["step"] / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        cpu = cpu_baseline(case, args.cpu_rows, args.cpu_budget)
+        log("cpu baseline:", cpu)
+
+    lens = np.asarray(spec.lens)
+    res = {
+        "metric": METRIC,
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16" if fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(spec), "batch": spec.B, "query_tokens": spec.T,
+                   "ctx_min": int(lens.min()), "ctx_max": int(lens.max()), "ctx_mean": float(lens.mean()),
+                   "top_k": spec.K, "indexer_heads": spec.HI, "indexer_dim": spec.DI,
+                   "attn_heads": spec.H, "page": 64, "rotation_copies": R},
+        "roofline": roof,
+        "path": {"algorithmic_bytes_per_step": int(ab["step"]), "achieved": round(path_gbs, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -149,6 +149,23 @@ dsa_status dsa_sparse_attn(const void *q, const void *kv_cache, const int32_t *i
                            void *out, float *lse, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Opt-in per-kernel timing (off by default).  dsa_profile_start() turns recording on for the
+ * calling thread: each kernel the library then launches from this thread is bracketed by two
+ * hipEvents on its stream (events come from a reusable host-side pool; no device memory).
+ * dsa_profile_stop() turns recording off, waits for the recorded events, and writes up to
+ * max_entries per-kernel totals (kernel name, launch count, summed GPU milliseconds) to `out`;
+ * it returns the number of distinct kernels seen, or -1 if the HIP runtime reported an error.
+ * The extra event records perturb back-to-back launches slightly, so time whole calls without
+ * recording and use recording for the per-kernel split. */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} dsa_kernel_time;
+
+dsa_status dsa_profile_start(void);
+int dsa_profile_stop(dsa_kernel_time *out, int max_entries);
+
 /* Thread-local text describing the last non-OK status returned on this thread ("" if none). */
 const char *dsa_last_error(void);
 

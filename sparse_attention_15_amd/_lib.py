@@ -41,6 +41,11 @@ class AttnShape(ctypes.Structure):
                 ("dim_v", ctypes.c_int32), ("top_k", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
 
 
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
 class DsaError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{_STATUS.get(status, status)}: {msg}")
@@ -50,7 +55,8 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_last_error", "dsa_version"]
+           "dsa_sparse_attn", "dsa_profile_start", "dsa_profile_stop", "dsa_last_error",
+           "dsa_version"]
 
 
 def lib() -> ctypes.CDLL:
@@ -77,6 +83,10 @@ def lib() -> ctypes.CDLL:
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_version.argtypes = []
     L.dsa_version.restype = ctypes.c_int
+    L.dsa_profile_start.argtypes = []
+    L.dsa_profile_start.restype = ctypes.c_int
+    L.dsa_profile_stop.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+    L.dsa_profile_stop.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -161,3 +171,16 @@ def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float,
                                  ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
                                  _stream(stream)))
     return out, lse
+
+
+def dsa_profile_start() -> None:
+    _check(lib().dsa_profile_start())
+
+
+def dsa_profile_stop() -> dict:
+    """{kernel name: (launches, total GPU ms)} recorded since dsa_profile_start()."""
+    buf = (KernelTime * 64)()
+    n = lib().dsa_profile_stop(buf, 64)
+    if n < 0:
+        raise DsaError(6, "dsa_profile_stop: HIP error")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}

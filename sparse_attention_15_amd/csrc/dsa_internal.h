@@ -8,6 +8,20 @@
 
 namespace dsa {
 
+// Brackets one kernel launch with profiling events when dsa_profile_start() is active.
+class LaunchScope {
+ public:
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  LaunchScope(const LaunchScope&) = delete;
+  LaunchScope& operator=(const LaunchScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t stop_;
+};
+
 // Workspace carving and grid sizes of one dsa_indexer_topk call.
 struct IndexerPlan {
   int rows = 0;          // batch * T query rows

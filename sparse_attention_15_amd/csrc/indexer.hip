@@ -490,7 +490,10 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   const size_t hist_words = (size_t)p.rows * kBins;
   const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
-  hipLaunchKernelGGL(li_zero_hist, dim3(zgrid), dim3(256), 0, st, hist, hist_words);
+  {
+    LaunchScope ls("li_zero_hist", st);
+    hipLaunchKernelGGL(li_zero_hist, dim3(zgrid), dim3(256), 0, st, hist, hist_words);
+  }
 
   ScoreArgs s;
   s.q = static_cast<const unsigned char*>(a.q);
@@ -507,6 +510,7 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.max_seq_len = a.max_seq_len;
   const int grid = a.B * p.n_qtiles * p.n_chunks;
   if (grid > 0) {
+    LaunchScope ls("li_score", st);
     switch (a.heads * 1000 + a.dim) {
       case 8064: launch_score_dt<8, 64>(s, a.fp8, p.tq, grid, st); break;
       case 8128: launch_score_dt<8, 128>(s, a.fp8, p.tq, grid, st); break;
@@ -529,8 +533,14 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   sa.idx_out = a.idx_out;
   sa.T = a.T; sa.max_pages = a.max_pages; sa.K = a.top_k; sa.n_slices = p.n_slices;
   sa.row_stride = p.row_stride; sa.gt_cap = p.gt_cap; sa.max_seq_len = a.max_seq_len;
-  hipLaunchKernelGGL(li_select_split, dim3(p.rows, p.n_slices), dim3(kThreads), 0, st, sa);
-  hipLaunchKernelGGL(li_select_final, dim3(p.rows), dim3(kThreads), 0, st, sa);
+  {
+    LaunchScope ls("li_select_split", st);
+    hipLaunchKernelGGL(li_select_split, dim3(p.rows, p.n_slices), dim3(kThreads), 0, st, sa);
+  }
+  {
+    LaunchScope ls("li_select_final", st);
+    hipLaunchKernelGGL(li_select_final, dim3(p.rows), dim3(kThreads), 0, st, sa);
+  }
   return hipGetLastError();
 }
 

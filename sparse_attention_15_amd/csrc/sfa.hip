@@ -338,6 +338,8 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   s.scale_log2 = a.sm_scale * kLog2e;
   const int rows = a.B * a.T;
   const dim3 grid(rows, p.n_splits);
+  {
+  LaunchScope ls("sfa_main", st);
   switch (p.waves) {
     case 1: hipLaunchKernelGGL(sfa_main<1>, grid, dim3(128), 0, st, s); break;
     case 2: hipLaunchKernelGGL(sfa_main<2>, grid, dim3(256), 0, st, s); break;
@@ -345,7 +347,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
     case 4: hipLaunchKernelGGL(sfa_main<4>, grid, dim3(512), 0, st, s); break;
     default: return hipErrorInvalidValue;
   }
+  }
   if (p.n_splits > 1) {
+    LaunchScope ls("sfa_combine", st);
     CombineArgs c;
     c.part_ml = s.part_ml; c.part_o = s.part_o; c.out = s.out; c.lse = a.lse;
     c.H = a.heads; c.n_splits = p.n_splits; c.waves = p.waves;
