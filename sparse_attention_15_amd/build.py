@@ -12,8 +12,11 @@ SOURCES = ["indexer.hip", "sfa.hip", "dsa_api.cpp", "dsa_profile.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU ops stay disabled: the compiler would otherwise form v_pk_*_f32 from plain
 # float code.
+# MFMA accumulators are selected in VGPR form: with AGPR-form selection the register allocator
+# shuttled the attention accumulator between register files on every tile.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

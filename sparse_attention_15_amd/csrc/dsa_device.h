@@ -26,6 +26,19 @@ __device__ __forceinline__ f32x16 mfma_fp8(long a, long b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Workgroup barrier that drains only this wave's LDS operations.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would serialise a load pipeline that keeps data
+// for later tiles in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Waits until at most N of this wave's global loads (including direct-to-LDS loads) are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
 // Order-preserving map float -> uint32 (larger float -> larger key); -0 is folded onto +0 so the
 // two compare equal.
 __device__ __forceinline__ uint32_t float_key(float f) {

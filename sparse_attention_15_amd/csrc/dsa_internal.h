@@ -53,7 +53,9 @@ bool indexer_supported(int heads, int dim);
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t stream);
 
 struct AttnPlan {
-  int waves = 1;         // waves per workgroup (32 heads each)
+  int waves = 1;         // 32-head groups of the row (each handled by a pair of waves)
+  int groups_per_wg = 1; // head groups per workgroup
+  int head_chunks = 1;   // workgroups per (row, split) along the heads
   int n_splits = 1;      // workgroups per query row along the selected set
   int keys_per_split = 0;
   size_t off_ml = 0, off_part = 0, total = 0;

@@ -191,9 +191,9 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
 
   issue(0);
   for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();
+    lds_barrier();
     commit(tile);
-    __syncthreads();
+    lds_barrier();
     if (tile + 1 < ntiles) issue(tile + 1);
     const int ts = s_begin + tile * kTileKeys;
     if (qvalid) {
@@ -245,35 +245,271 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Decode / verify (T <= 4 query rows per sequence): a persistent, load-balanced grid.  The work is
+// the flattened list of (sequence, KT-key tile) pairs over sequences that have more than K keys;
+// workgroup g takes the contiguous share [g*N/G, (g+1)*N/G).  Each workgroup rebuilds the per-
+// sequence tile offsets from seq_lens (no host round trip).  Loads run two tiles ahead in
+// registers and the LDS tile is double-buffered, so one barrier per tile suffices.
+constexpr int kMaxSeqPersist = 512;
+constexpr int kMaxPagesPersist = 512;
+
+template <int TQ>
+struct PTile { static constexpr int KT = TQ == 1 ? 128 : 64; };
+
+template <int HI, int DI, bool FP8, int TQ>
+struct PCfg {
+  static constexpr int KT = PTile<TQ>::KT;         // keys per tile
+  static constexpr int MB = (HI + 31) / 32;
+  static constexpr int KS = DI / 16;
+  static constexpr int ELT = FP8 ? 1 : 2;
+  static constexpr int ROWB = DI * ELT;
+  static constexpr int CPK = ROWB / 16;
+  static constexpr int TILEB = KT * ROWB;
+  static constexpr int LPT = TILEB / 16 / kThreads;
+  static constexpr int WPQ = 4 / TQ;                // waves per query row
+  static constexpr int NBW = (KT / 32) / WPQ;       // 32-key column blocks per wave per tile
+  static_assert(LPT >= 1 && NBW >= 1, "tile shape");
+};
+
+template <int HI, int DI, bool FP8, int TQ>
+__global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
+  using C = PCfg<HI, DI, FP8, TQ>;
+  typedef typename AFrag<FP8>::T frag_t;
+  __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][C::TILEB];
+  __shared__ uint32_t lds_hist[TQ * kBins];
+  __shared__ float lds_ksc[2][C::KT / kPage > 0 ? C::KT / kPage : 1];
+  __shared__ int lds_tstart[kMaxSeqPersist + 1];
+  __shared__ int lds_len[kMaxSeqPersist];       // clamped sequence length (= visible keys of the last query row)
+  __shared__ int lds_page[kMaxPagesPersist];    // physical pages of this workgroup's tiles, in order
+  __shared__ uint32_t sh[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 31, hh = lane >> 5;
+  const int cap = a.max_seq_len;
+
+  // flattened work list: tiles per sequence, exclusive prefix in LDS
+  int carry = 0;
+  for (int base = 0; base < a.B; base += kThreads) {
+    const int b = base + tid;
+    int v = 0;
+    if (b < a.B) {
+      const int nmax = row_visible(a.seq_lens, b, a.T, a.T - 1, cap);
+      lds_len[b] = nmax;
+      v = nmax > a.K ? (nmax + C::KT - 1) / C::KT : 0;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<kThreads>((uint32_t)v, sh, tot);
+    if (b < a.B) lds_tstart[b] = carry + (int)ex;
+    carry += (int)tot;
+  }
+  if (tid == 0) lds_tstart[a.B] = carry;
+  __syncthreads();
+  const int total = carry;
+  const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
+  const int hi = (int)((long long)(blockIdx.x + 1) * total / gridDim.x);
+  const int n_items = hi - lo;
+  if (n_items <= 0) return;
+
+  auto locate = [&](int f) -> int {   // sequence holding flat tile f
+    int l = 0, h = a.B;
+    while (h - l > 1) {
+      const int m = (l + h) >> 1;
+      if (lds_tstart[m] <= f) l = m; else h = m;
+    }
+    return l;
+  };
+  // physical page ids of this workgroup's tiles (one round of block-table loads, off the
+  // per-tile critical path); a range longer than the LDS table reads the block table directly
+  constexpr int PPT = C::KT / kPage > 0 ? C::KT / kPage : 1;   // pages per tile
+  const bool page_cached = n_items * PPT <= kMaxPagesPersist;
+  if (page_cached) {
+    for (int i = tid; i < n_items * PPT; i += kThreads) {
+      const int f = lo + i / PPT;
+      const int b = locate(f);
+      const int lp = (f - lds_tstart[b]) * PPT + i % PPT;
+      lds_page[i] = lp * kPage < lds_len[b]
+          ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : 0;
+    }
+  }
+  __syncthreads();
+  auto page_of = [&](int f, int b, int lp) -> int {
+    if (page_cached) return lds_page[(f - lo) * PPT + (lp % PPT)];
+    return clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages);
+  };
+
+  const int qi = wave / C::WPQ, nsub = wave % C::WPQ;
+  const bool qvalid = qi < a.T;
+  frag_t afrag[C::MB][C::KS];
+  float wreg[C::MB][16];
+  auto load_q = [&](int b) {
+    const size_t row = (size_t)b * a.T + (qvalid ? qi : 0);
+#pragma unroll
+    for (int m = 0; m < C::MB; ++m) {
+      const int head = 32 * m + nl;
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        if (head < HI) {
+          const unsigned char* src = a.q + ((row * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
+          if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
+          else afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+        } else {
+          if constexpr (FP8) afrag[m][kk] = 0;
+          else afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hd = 32 * m + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float wv = 0.f;
+        if (hd < HI) {
+          wv = a.w[row * HI + hd];
+          if constexpr (FP8) wv *= a.q_scale[row * HI + hd];
+        }
+        wreg[m][r] = wv;
+      }
+    }
+  };
+  auto flush = [&](int b) {
+    for (int i = tid; i < TQ * kBins; i += kThreads) {
+      const int t2 = i / kBins;
+      const uint32_t v = lds_hist[i];
+      if (v != 0u && t2 < a.T) atomicAdd(&a.hist[((size_t)b * a.T + t2) * kBins + (i % kBins)], v);
+      lds_hist[i] = 0u;
+    }
+  };
+
+  u32x4 pre0[C::LPT], pre1[C::LPT];
+  int pb0 = 0, pj0 = 0, pb1 = 0, pj1 = 0;
+  auto issue = [&](int f, u32x4 (&pre)[C::LPT], int& pb, int& pj) {
+    const int b = locate(f);
+    const int j = f - lds_tstart[b];
+    pb = b; pj = j;
+    const int nmax = lds_len[b];
+    const int ts = j * C::KT;
+#pragma unroll
+    for (int q = 0; q < C::LPT; ++q) {
+      const int i = tid + kThreads * q;
+      const int key = i / C::CPK, c = i % C::CPK;
+      const int lp = ts / kPage + key / kPage;
+      if (lp * kPage < nmax) {
+        const int phys = page_of(f, b, lp);
+        pre[q] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
+      }
+    }
+  };
+  auto commit = [&](const u32x4 (&pre)[C::LPT], int buf, int b, int j) {
+#pragma unroll
+    for (int q = 0; q < C::LPT; ++q) {
+      const int i = tid + kThreads * q;
+      const int key = i / C::CPK, c = i % C::CPK;
+      *reinterpret_cast<u32x4*>(lds_k[buf] + key * C::ROWB + 16 * (c ^ (key & (C::CPK - 1)))) = pre[q];
+    }
+    if constexpr (FP8) {
+      if (tid < PPT) {
+        const int lp = j * C::KT / kPage + tid;
+        lds_ksc[buf][tid] = (lp * kPage < lds_len[b]) ? a.k_scale[page_of(lds_tstart[b] + j, b, lp)] : 0.f;
+      }
+    }
+  };
+  auto compute = [&](int buf, int b, int j) {
+    if (!qvalid) return;
+    const int n_me = lds_len[b] - (a.T - 1 - qi);     // visible keys of query row qi
+    if (n_me <= a.K) return;
+    const size_t row = (size_t)b * a.T + qi;
+#pragma unroll
+    for (int jb = 0; jb < C::NBW; ++jb) {
+      const int kt = (nsub + jb * C::WPQ) * 32 + nl;
+      f32x16 acc[C::MB];
+#pragma unroll
+      for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        if constexpr (FP8) {
+          const long bf = *reinterpret_cast<const long*>(
+              lds_k[buf] + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) acc[m] = mfma_fp8(afrag[m][kk], bf, acc[m]);
+        } else {
+          const bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+              lds_k[buf] + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bf, acc[m]);
+        }
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], fmaxf(acc[m][r], 0.f), part);
+      part += __shfl_xor(part, 32, 64);
+      if constexpr (FP8) part *= lds_ksc[buf][kt / kPage];
+      const int s = j * C::KT + kt;
+      if (hh == 0 && s < n_me) {
+        const uint32_t key = float_key(part);
+        a.keys[row * a.row_stride + s] = key;
+        atomicAdd(&lds_hist[qi * kBins + (key >> 21)], 1u);
+      }
+    }
+  };
+
+  for (int i = tid; i < TQ * kBins; i += kThreads) lds_hist[i] = 0u;
+  issue(lo, pre0, pb0, pj0);
+  if (n_items > 1) issue(lo + 1, pre1, pb1, pj1);
+  int b_cur = -1;
+  auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, int buf) {
+    commit(pre, buf, pb, pj);
+    const int b = pb, j = pj;
+    lds_barrier();                    // keeps the next tile's loads in flight
+    if (b != b_cur) {                 // new sequence: publish the old histogram, load new q
+      if (b_cur >= 0) flush(b_cur);
+      load_q(b);
+      b_cur = b;
+      lds_barrier();
+    }
+    if (i + 2 < n_items) issue(lo + i + 2, pre, pb, pj);
+    compute(buf, b, j);
+  };
+  for (int i = 0; i < n_items; i += 2) {
+    step(i, pre0, pb0, pj0, 0);
+    if (i + 1 < n_items) step(i + 1, pre1, pb1, pj1, 1);
+  }
+  __syncthreads();
+  flush(b_cur);
+}
+
+// ------------------------------------------------------------------------------------------------
 // Finds the bin holding the need-th largest element of a histogram of NB bins (bins ordered by
 // key).  Returns the bin and, through `above`, the number of elements in higher bins.  All threads
 // of the workgroup get the result.  `sh` needs kThreads/64 + 2 words.
-template <int NB>
+template <int NB, int NT = kThreads>
 __device__ __forceinline__ int find_bin(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t& above) {
-  constexpr int PER = NB / kThreads;   // bins per thread; thread 0 owns the highest bins
+  constexpr int PER = NB / NT;          // bins per thread; thread 0 owns the highest bins
+  static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
   const int tid = threadIdx.x;
   const int hi = NB - PER * tid;       // exclusive upper end of my bins
   uint32_t mine = 0;
-  if (tid == 0) { sh[kThreads / 64] = 0u; sh[kThreads / 64 + 1] = 0u; }
+  if (tid == 0) { sh[NT / 64] = 0u; sh[NT / 64 + 1] = 0u; }
 #pragma unroll
   for (int i = 1; i <= PER; ++i) mine += hist[hi - i];
   uint32_t tot;
-  const uint32_t pre = block_exclusive_scan<kThreads>(mine, sh, tot);
+  const uint32_t pre = block_exclusive_scan<NT>(mine, sh, tot);
   if (pre < need && pre + mine >= need) {
     uint32_t run = pre;
 #pragma unroll
     for (int i = 1; i <= PER; ++i) {
       const uint32_t h = hist[hi - i];
       if (run < need && run + h >= need) {
-        sh[kThreads / 64] = hi - i;
-        sh[kThreads / 64 + 1] = run;
+        sh[NT / 64] = hi - i;
+        sh[NT / 64 + 1] = run;
       }
       run += h;
     }
   }
   __syncthreads();
-  const int bin = (int)sh[kThreads / 64];
-  above = sh[kThreads / 64 + 1];
+  const int bin = (int)sh[NT / 64];
+  above = sh[NT / 64 + 1];
   __syncthreads();
   return bin;
 }
@@ -299,12 +535,7 @@ __global__ __launch_bounds__(256) void li_select_split(SelectArgs a) {
   if (n <= a.K || slice * kSlice >= n) return;
   const uint32_t kp = (uint32_t)min(a.K, n);
 
-  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = a.hist[(size_t)row * kBins + i];
-  __syncthreads();
-  uint32_t above;
-  const uint32_t b1 = (uint32_t)find_bin<kBins>(sh_hist, kp, sh, above);
-
-  // ordered compaction of this slice: 16 consecutive keys per thread
+  // the slice's keys (16 consecutive per thread) load while the histogram is scanned
   constexpr int PT = kSlice / kThreads;
   const int s0 = slice * kSlice + tid * PT;
   uint32_t kv[PT];
@@ -313,6 +544,12 @@ __global__ __launch_bounds__(256) void li_select_split(SelectArgs a) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(a.keys + (size_t)row * a.row_stride + s0 + 4 * j);
     kv[4 * j] = v[0]; kv[4 * j + 1] = v[1]; kv[4 * j + 2] = v[2]; kv[4 * j + 3] = v[3];
   }
+  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = a.hist[(size_t)row * kBins + i];
+  __syncthreads();
+  uint32_t above;
+  const uint32_t b1 = (uint32_t)find_bin<kBins>(sh_hist, kp, sh, above);
+
+  // ordered compaction of this slice
   uint32_t ngt = 0, nc = 0;
 #pragma unroll
   for (int j = 0; j < PT; ++j) {
@@ -350,25 +587,31 @@ __device__ __forceinline__ int lower_bound_lds(const int32_t* v, int n, int x) {
   return lo;
 }
 
-__global__ __launch_bounds__(256) void li_select_final(SelectArgs a) {
+constexpr int kSelThreads = 1024;
+constexpr int kCandCap = 8192;     // candidates staged in LDS; more fall back to global reads
+
+__global__ __launch_bounds__(1024) void li_select_final(SelectArgs a) {
+  constexpr int NT = kSelThreads;
   __shared__ uint32_t sh_hist[kBins];
-  __shared__ uint32_t sh[8];
+  __shared__ uint32_t sh[NT / 64 + 2];
   __shared__ int32_t off_g[kMaxSlices + 1], off_c[kMaxSlices + 1];
   __shared__ int32_t gt_list[DSA_MAX_TOP_K];
   __shared__ int32_t sel_list[DSA_MAX_TOP_K];
+  __shared__ uint32_t c_key[kCandCap];
+  __shared__ int32_t c_pos[kCandCap];
   const int tid = threadIdx.x;
   const int row = blockIdx.x;
   const int b = row / a.T, t = row % a.T;
   const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
   int32_t* out = a.idx_out + (size_t)row * a.K;
   if (n <= a.K) {
-    for (int j = tid; j < a.K; j += kThreads) out[j] = j < n ? j : -1;
+    for (int j = tid; j < a.K; j += NT) out[j] = j < n ? j : -1;
     return;
   }
   const int kp = a.K;   // n > K
   const int S = (n + kSlice - 1) / kSlice;
 
-  // slice offsets (S <= kMaxSlices <= kThreads)
+  // slice offsets (S <= kMaxSlices <= NT)
   uint32_t g = 0, c = 0;
   if (tid < S) {
     const size_t sl = (size_t)row * a.n_slices + tid;
@@ -376,74 +619,95 @@ __global__ __launch_bounds__(256) void li_select_final(SelectArgs a) {
     c = (uint32_t)a.cnt[sl * 2 + 1];
   }
   uint32_t G, Cn;
-  const uint32_t og = block_exclusive_scan<kThreads>(g, sh, G);
-  const uint32_t oc = block_exclusive_scan<kThreads>(c, sh, Cn);
+  const uint32_t og = block_exclusive_scan<NT>(g, sh, G);
+  const uint32_t oc = block_exclusive_scan<NT>(c, sh, Cn);
   if (tid < S) { off_g[tid] = (int32_t)og; off_c[tid] = (int32_t)oc; }
   if (tid == 0) { off_g[S] = (int32_t)G; off_c[S] = (int32_t)Cn; }
   __syncthreads();
+  auto slice_of = [&](const int32_t* off, int i) -> int {   // largest slice with off[slice] <= i
+    int lo = 0, hi = S;
+    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (off[mid] <= i) lo = mid; else hi = mid; }
+    return lo;
+  };
   const uint2* cand = a.cand + (size_t)row * a.n_slices * kSlice;
-  auto cand_at = [&](int i) -> uint2 {   // i-th candidate in position order
-    int lo = 0, hi = S;                  // largest slice with off_c[slice] <= i
-    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (off_c[mid] <= i) lo = mid; else hi = mid; }
-    return cand[(size_t)lo * kSlice + (i - off_c[lo])];
+  const bool staged = Cn <= (uint32_t)kCandCap;
+  // one pass: candidates (position order) and the positions above the threshold bin into LDS
+  if (staged) {
+    for (int i = tid; i < (int)Cn; i += NT) {
+      const int sl = slice_of(off_c, i);
+      const uint2 e = cand[(size_t)sl * kSlice + (i - off_c[sl])];
+      c_key[i] = e.x;
+      c_pos[i] = (int32_t)e.y;
+    }
+  }
+  for (int i = tid; i < (int)G && i < DSA_MAX_TOP_K; i += NT) {
+    const int sl = slice_of(off_g, i);
+    gt_list[i] = a.gt_pos[((size_t)row * a.n_slices + sl) * a.gt_cap + (i - off_g[sl])];
+  }
+  for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
+  __syncthreads();
+  auto key_at = [&](int i) -> uint32_t {
+    if (staged) return c_key[i];
+    const int sl = slice_of(off_c, i);
+    return cand[(size_t)sl * kSlice + (i - off_c[sl])].x;
+  };
+  auto pos_at = [&](int i) -> int32_t {
+    if (staged) return c_pos[i];
+    const int sl = slice_of(off_c, i);
+    return (int32_t)cand[(size_t)sl * kSlice + (i - off_c[sl])].y;
   };
 
   // refine the threshold: digit 2 = bits 20..10, digit 3 = bits 9..0
   uint32_t need = (uint32_t)kp - G;
-  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < (int)Cn; i += kThreads) atomicAdd(&sh_hist[(cand_at(i).x >> 10) & 2047u], 1u);
+  for (int i = tid; i < (int)Cn; i += NT) atomicAdd(&sh_hist[(key_at(i) >> 10) & 2047u], 1u);
   __syncthreads();
   uint32_t above;
-  const uint32_t b2 = (uint32_t)find_bin<kBins>(sh_hist, need, sh, above);
+  const uint32_t b2 = (uint32_t)find_bin<kBins, NT>(sh_hist, need, sh, above);
   need -= above;
-  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = 0u;
+  for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
   __syncthreads();
-  uint32_t b1 = 0;
-  for (int i = tid; i < (int)Cn; i += kThreads) {
-    const uint32_t k = cand_at(i).x;
+  for (int i = tid; i < (int)Cn; i += NT) {
+    const uint32_t k = key_at(i);
     if (((k >> 10) & 2047u) == b2) atomicAdd(&sh_hist[k & 1023u], 1u);
   }
-  if (Cn > 0) b1 = cand_at(0).x >> 21;
+  const uint32_t b1 = Cn > 0 ? key_at(0) >> 21 : 0u;
   __syncthreads();
-  const uint32_t b3 = (uint32_t)find_bin<1024>(sh_hist, need, sh, above);
+  const uint32_t b3 = (uint32_t)find_bin<1024, NT>(sh_hist, need, sh, above);
   need -= above;                           // ties of the threshold key to keep (>= 1)
   const uint32_t theta = (b1 << 21) | (b2 << 10) | b3;
 
   // candidates above theta, plus the first `need` ties in position order
   uint32_t run_sel = 0, run_tie = 0;
-  for (int base = 0; base < (int)Cn; base += kThreads) {
+  for (int base = 0; base < (int)Cn; base += NT) {
     const int i = base + tid;
-    uint32_t k = 0, s = 0;
-    if (i < (int)Cn) { const uint2 e = cand_at(i); k = e.x; s = e.y; }
+    uint32_t k = 0;
+    int32_t p = 0;
+    if (i < (int)Cn) { k = key_at(i); p = pos_at(i); }
     const bool tie = i < (int)Cn && k == theta;
-    uint32_t ntie;
-    const uint32_t rank = run_tie + block_exclusive_scan<kThreads>(tie ? 1u : 0u, sh, ntie);
-    const bool sel = i < (int)Cn && (k > theta || (tie && rank < need));
-    uint32_t nsel;
-    const uint32_t pos = run_sel + block_exclusive_scan<kThreads>(sel ? 1u : 0u, sh, nsel);
-    if (sel && pos < DSA_MAX_TOP_K) sel_list[pos] = (int32_t)s;
-    run_sel += nsel;
-    run_tie += ntie;
-  }
-  // positions above the threshold bin, concatenated in slice (= position) order
-  for (int sl = 0; sl < S; ++sl) {
-    const int cnt = off_g[sl + 1] - off_g[sl];
-    const int32_t* src = a.gt_pos + ((size_t)row * a.n_slices + sl) * a.gt_cap;
-    for (int j = tid; j < cnt; j += kThreads)
-      if (off_g[sl] + j < DSA_MAX_TOP_K) gt_list[off_g[sl] + j] = src[j];
+    const bool above_t = i < (int)Cn && k > theta;
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan<NT>((tie ? 1u : 0u) | (above_t ? 0x10000u : 0u), sh, tot);
+    const uint32_t rank = run_tie + (pre & 0xFFFFu);          // ties before this one
+    const uint32_t n_above = pre >> 16;                       // above-theta before this one (tile)
+    const bool sel = above_t || (tie && rank < need);
+    // selected before this one in the tile: all above-theta ones, plus ties with rank < need
+    const uint32_t ties_sel_before = min(rank, need) - min(run_tie, need);
+    const uint32_t pos = run_sel + n_above + ties_sel_before;
+    if (sel && pos < DSA_MAX_TOP_K) sel_list[pos] = p;
+    run_sel += (tot >> 16) + (min(run_tie + (tot & 0xFFFFu), need) - min(run_tie, need));
+    run_tie += tot & 0xFFFFu;
   }
   __syncthreads();
   const int ng = min((int)G, a.K), ns = min((int)run_sel, a.K - ng);   // ng + ns == K
-  for (int i = tid; i < ng; i += kThreads) {
+  for (int i = tid; i < ng; i += NT) {
     const int p = gt_list[i];
     out[i + lower_bound_lds(sel_list, ns, p)] = p;
   }
-  for (int j = tid; j < ns; j += kThreads) {
+  for (int j = tid; j < ns; j += NT) {
     const int p = sel_list[j];
     out[j + lower_bound_lds(gt_list, ng, p)] = p;
   }
-  for (int j = ng + ns + tid; j < a.K; j += kThreads) out[j] = -1;
+  for (int j = ng + ns + tid; j < a.K; j += NT) out[j] = -1;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -473,16 +737,35 @@ bool indexer_supported(int heads, int dim) {
 }
 
 template <int HI, int DI, bool FP8>
-static void launch_score(const ScoreArgs& s, int tq, int grid, hipStream_t st) {
+static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, hipStream_t st) {
+  if (persist) {
+    if (tq == 1) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 1>), dim3(grid), dim3(kThreads), 0, st, s);
+    else if (tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
+    else hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 4>), dim3(grid), dim3(kThreads), 0, st, s);
+    return;
+  }
   if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, FP8, 1>), dim3(grid), dim3(kThreads), 0, st, s);
   else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
   else hipLaunchKernelGGL((li_score<HI, DI, FP8, 4>), dim3(grid), dim3(kThreads), 0, st, s);
 }
 
 template <int HI, int DI>
-static void launch_score_dt(const ScoreArgs& s, bool fp8, int tq, int grid, hipStream_t st) {
-  if (fp8) launch_score<HI, DI, true>(s, tq, grid, st);
-  else launch_score<HI, DI, false>(s, tq, grid, st);
+static void launch_score_dt(const ScoreArgs& s, bool fp8, int tq, int grid, bool persist, hipStream_t st) {
+  if (fp8) launch_score<HI, DI, true>(s, tq, grid, persist, st);
+  else launch_score<HI, DI, false>(s, tq, grid, persist, st);
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t st) {
@@ -508,18 +791,24 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.B = a.B; s.T = a.T; s.max_pages = a.max_pages; s.num_pages = a.num_pages; s.K = a.top_k;
   s.n_chunks = p.n_chunks; s.n_qtiles = p.n_qtiles; s.row_stride = p.row_stride;
   s.max_seq_len = a.max_seq_len;
-  const int grid = a.B * p.n_qtiles * p.n_chunks;
+  const bool persist = a.T <= 4 && a.B <= kMaxSeqPersist;
+  int grid = a.B * p.n_qtiles * p.n_chunks;
+  if (persist) {
+    const int kt = p.tq == 1 ? 128 : 64;
+    const long long max_tiles = (long long)a.B * ((a.max_seq_len + kt - 1) / kt);
+    grid = (int)std::max<long long>(1, std::min<long long>(2LL * device_cus(), (max_tiles + 1) / 2));
+  }
   if (grid > 0) {
     LaunchScope ls("li_score", st);
     switch (a.heads * 1000 + a.dim) {
-      case 8064: launch_score_dt<8, 64>(s, a.fp8, p.tq, grid, st); break;
-      case 8128: launch_score_dt<8, 128>(s, a.fp8, p.tq, grid, st); break;
-      case 16064: launch_score_dt<16, 64>(s, a.fp8, p.tq, grid, st); break;
-      case 16128: launch_score_dt<16, 128>(s, a.fp8, p.tq, grid, st); break;
-      case 32064: launch_score_dt<32, 64>(s, a.fp8, p.tq, grid, st); break;
-      case 32128: launch_score_dt<32, 128>(s, a.fp8, p.tq, grid, st); break;
-      case 64064: launch_score_dt<64, 64>(s, a.fp8, p.tq, grid, st); break;
-      case 64128: launch_score_dt<64, 128>(s, a.fp8, p.tq, grid, st); break;
+      case 8064: launch_score_dt<8, 64>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 8128: launch_score_dt<8, 128>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 16064: launch_score_dt<16, 64>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 16128: launch_score_dt<16, 128>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 32064: launch_score_dt<32, 64>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 32128: launch_score_dt<32, 128>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 64064: launch_score_dt<64, 64>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 64128: launch_score_dt<64, 128>(s, a.fp8, p.tq, grid, persist, st); break;
       default: return hipErrorInvalidValue;
     }
   }
@@ -539,7 +828,7 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   }
   {
     LaunchScope ls("li_select_final", st);
-    hipLaunchKernelGGL(li_select_final, dim3(p.rows), dim3(kThreads), 0, st, sa);
+    hipLaunchKernelGGL(li_select_final, dim3(p.rows), dim3(kSelThreads), 0, st, sa);
   }
   return hipGetLastError();
 }
