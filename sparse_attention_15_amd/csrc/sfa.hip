@@ -138,20 +138,16 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
   // gather tile `tile` into ring slot `buf`: this wave's loads are chunks 64*q + lane of the tile,
   // q = wave, wave + NW, ...; slot position p holds row p / 72, chunk (p % 72) ^ swz(row)
   constexpr int kDmaMax = (kDmaPerTile + NW - 1) / NW;
-  int dma_rc[kDmaMax];                        // per load: row | chunk << 8 (fixed for all tiles)
-#pragma unroll
-  for (int u = 0; u < kDmaMax; ++u) {
-    const int p = 64 * (wave + u * NW) + lane;
-    const int r = p / 72;
-    dma_rc[u] = (r & 31) | (((p % 72) ^ swz(r & 31)) << 8);
-  }
   auto issue = [&](int tile, int buf) {
 #pragma unroll
     for (int u = 0; u < kDmaMax; ++u) {
       const int q = wave + u * NW;
       if (q < kDmaPerTile) {
-        const int prow = lds_rows[tile * kBK + (dma_rc[u] & 31)];
-        const unsigned char* src = a.kv + (size_t)(prow < 0 ? 0 : prow) * kRowBytes + 16 * (dma_rc[u] >> 8);
+        const int p = 64 * q + lane;
+        const int r = p / 72;
+        const int c = (p % 72) ^ swz(r);
+        const int prow = lds_rows[tile * kBK + r];
+        const unsigned char* src = a.kv + (size_t)(prow < 0 ? 0 : prow) * kRowBytes + 16 * c;
         __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_kv[buf] + 1024 * q), 16, 0, 0);
       }
     }
@@ -182,8 +178,7 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
   float m_run = -1e30f, l_run = 0.f;
 
   float* sx_mine = lds_sx + ((g * 2 + hf) * 16) * 64 + lane;
-  const float* sx_0 = lds_sx + ((g * 2 + 0) * 16) * 64 + lane;
-  const float* sx_1 = lds_sx + ((g * 2 + 1) * 16) * 64 + lane;
+  const float* sx_other = lds_sx + ((g * 2 + (hf ^ 1)) * 16) * 64 + lane;
 
   // Per-lane LDS byte offsets.  XOR with swz() only touches the low three bits of a chunk index,
   // so offsets repeat every 8 chunks: four bases per operand plus immediate strides cover a tile.
@@ -231,9 +226,10 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sx_mine[r * 64] = s[r];
     lds_barrier();
-    // both waves of the pair form the same full score, summing the halves in a fixed order
+    // both waves of the pair form the same full score (one addition of the two halves, which is
+    // commutative, so both waves get the same bits)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = sx_0[r * 64] + sx_1[r * 64];
+    for (int r = 0; r < 16; ++r) s[r] += sx_other[r * 64];
 
     // online softmax over the 16 keys this lane holds (+ the other half-wave's 16)
     float mx = -INFINITY;
