@@ -51,8 +51,21 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts within each 16-lane row, then the
+// last lane of row 0 is added to row 1 and of row 2 to row 3, then lane 31 to rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64).  `sh` holds NT/64
-// words of LDS.  Returns this thread's exclusive prefix and the workgroup total.
+// words of LDS.  Returns this thread's exclusive prefix and the workgroup total.  Its barriers
+// leave global loads in flight.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -63,7 +76,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     if (lane >= o) x += y;
   }
   if (lane == 63) sh[wid] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < NT / 64; ++i) {
@@ -71,7 +84,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     pre += (i < wid) ? s : 0u;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return pre + x - v;
 }

@@ -26,12 +26,11 @@ class LaunchScope {
 struct IndexerPlan {
   int rows = 0;          // batch * T query rows
   int row_stride = 0;    // u32 keys per row in the score scratch
-  int n_slices = 0;      // select-phase-1 slices per row
-  int gt_cap = 0;        // per-slice capacity of the "above the threshold bin" list
-  int n_chunks = 0;      // key chunks per sequence in the score grid
+  int n_chunks = 0;      // key chunks per sequence in the chunked (prefill) score grid
   int tq = 1;            // query rows sharing one pass over the keys (1, 2 or 4)
   int n_qtiles = 0;      // ceil(T / tq)
-  size_t off_hist = 0, off_keys = 0, off_gt = 0, off_cand = 0, off_cnt = 0, total = 0;
+  int n_seg = 1;         // select workgroups per row (grid y)
+  size_t off_hist = 0, off_keys = 0, off_gt = 0, off_cand = 0, total = 0;
 };
 
 struct IndexerArgs {

@@ -16,12 +16,11 @@
 //                   the chunk's pages (page-table resolved) through LDS, MFMA score GEMM
 //                   [heads x dim] x [dim x keys], ReLU and head-weight reduction in registers,
 //                   order-preserving u32 keys to the row scratch, LDS histogram -> global.
-//   li_select_split one workgroup per (row, slice of 4096 keys): from the row histogram finds the
-//                   bin holding the K'-th key, then an ordered compaction of its slice emits the
-//                   positions above that bin and the (key, position) candidates inside it.
-//   li_select_final one workgroup per row: refines the threshold key over the candidates (two
-//                   more radix digits), picks candidates above it plus the lowest-position ties up
-//                   to the quota, and merges them with the above-bin positions into idx_out.
+//   li_select       one workgroup per row: resolves the K'-th key digit by digit (first digit from
+//                   the row histogram), stages the positions above the threshold range and the
+//                   (key, position) candidates inside it in LDS with one ordered pass over the
+//                   row, finishes the threshold in LDS, keeps candidates above it plus the
+//                   lowest-position ties up to the quota, and merges both lists into idx_out.
 // A row with n <= K selects every visible position and skips the score scratch.
 #include <algorithm>
 
@@ -33,8 +32,6 @@ namespace dsa {
 constexpr int kTileKeys = 128;    // keys staged in LDS per step (two pages)
 constexpr int kChunkKeys = 1024;  // keys per score workgroup
 constexpr int kBins = 2048;       // first radix digit: key bits 31..21
-constexpr int kSlice = 4096;      // keys per select-phase-1 workgroup
-constexpr int kMaxSlices = 256;   // rows up to 1M keys
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------------------------------------
@@ -480,234 +477,369 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Finds the bin holding the need-th largest element of a histogram of NB bins (bins ordered by
-// key).  Returns the bin and, through `above`, the number of elements in higher bins.  All threads
-// of the workgroup get the result.  `sh` needs kThreads/64 + 2 words.
-template <int NB, int NT = kThreads>
-__device__ __forceinline__ int find_bin(const uint32_t* hist, uint32_t need, uint32_t* sh, uint32_t& above) {
-  constexpr int PER = NB / NT;          // bins per thread; thread 0 owns the highest bins
-  static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
-  const int tid = threadIdx.x;
-  const int hi = NB - PER * tid;       // exclusive upper end of my bins
-  uint32_t mine = 0;
-  if (tid == 0) { sh[NT / 64] = 0u; sh[NT / 64 + 1] = 0u; }
+// Top-K selection.  Workgroups of 1024 threads; a row of n keys is cut into segments of
+// seg_len(n) keys, one workgroup each.
+struct SelectArgs {
+  const uint32_t* keys;     // [rows, row_stride] order-preserving score keys
+  const uint32_t* hist;     // [rows, kBins] histogram of key bits 31..21
+  uint32_t* ctl;            // [rows, 4] zeroed per call: segments done, gt cursor, candidate cursor
+  int32_t* g_gt;            // [rows, DSA_MAX_TOP_K] positions above the threshold range
+  uint2* g_cand;            // [rows, kCandCap] (key, position) inside the threshold range
+  const int32_t* seq_lens;
+  int32_t* idx_out;         // [rows, K]
+  int T, K, row_stride, max_seq_len;
+};
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kCandCap = 8192;                       // candidates staged in LDS
+constexpr int kSelVec = 4;                           // 16-byte loads per thread per scan step
+constexpr int kSelPer = 4 * kSelVec;                 // consecutive keys per thread per step (16)
+constexpr int kSelChunk = kSelThreads * kSelPer;     // keys per scan step (16384)
+constexpr int kMaxSeg = 32;                          // workgroups per row at most
+constexpr int kMapWords = 2 * kSelThreads;           // bitmap words per emit chunk
+constexpr int kMapBits = 32 * kMapWords;             // positions per emit chunk (65536)
+
+// Keys per segment: whole scan steps, at most kMaxSeg segments.
+__host__ __device__ __forceinline__ int seg_len_of(int n) {
+  const int steps = (n + kSelChunk - 1) / kSelChunk;
+  return kSelChunk * ((steps + kMaxSeg - 1) / kMaxSeg);
+}
+
+struct SelScratch {
+  uint32_t wave_tot[2][kSelWaves];   // per-wave totals, alternating halves between scans
+  uint32_t res[3];                   // bin search result: bin, count above it, count in it
+  uint32_t cursor;                   // LDS list fill: gt count | candidate count << 16
+  uint32_t pub[3];                   // global list offsets of this segment, segments done before
+};
+
+// Exclusive prefix sum over the 1024-thread workgroup with a single barrier: wave totals go to
+// alternating halves of `wave_tot`, so the next scan never overwrites totals still being read.
+__device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch& S, uint32_t& phase, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t x = wave_inclusive_scan(v);
+  if (lane == 63) S.wave_tot[phase][wid] = x;
+  lds_barrier();
+  uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int i = 1; i <= PER; ++i) mine += hist[hi - i];
+  for (int i = 0; i < kSelWaves; ++i) {
+    const uint32_t t = S.wave_tot[phase][i];
+    pre += i < wid ? t : 0u;
+    tot += t;
+  }
+  phase ^= 1u;
+  total = tot;
+  return pre + x - v;
+}
+
+// Bin holding the need-th largest element of a histogram of NB bins (higher bin = larger keys);
+// returns it with the count in higher bins (`above`) and in the bin itself (`count`).  1 <= need
+// <= total is required.  Thread 0 owns the highest bins.
+template <int NB>
+__device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t need, SelScratch& S,
+                                                 uint32_t& phase, uint32_t& above, uint32_t& count) {
+  constexpr int PER = NB / kSelThreads;
+  static_assert(PER >= 1 && NB % kSelThreads == 0, "bins per thread");
+  const int hi = NB - PER * (int)threadIdx.x;
+  uint32_t h[PER], mine = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) { h[i] = hist[hi - 1 - i]; mine += h[i]; }
   uint32_t tot;
-  const uint32_t pre = block_exclusive_scan<NT>(mine, sh, tot);
+  const uint32_t pre = sel_scan(mine, S, phase, tot);
   if (pre < need && pre + mine >= need) {
     uint32_t run = pre;
 #pragma unroll
-    for (int i = 1; i <= PER; ++i) {
-      const uint32_t h = hist[hi - i];
-      if (run < need && run + h >= need) {
-        sh[NT / 64] = hi - i;
-        sh[NT / 64 + 1] = run;
-      }
-      run += h;
+    for (int i = 0; i < PER; ++i) {
+      if (run < need && run + h[i] >= need) { S.res[0] = hi - 1 - i; S.res[1] = run; S.res[2] = h[i]; }
+      run += h[i];
     }
   }
-  __syncthreads();
-  const int bin = (int)sh[NT / 64];
-  above = sh[NT / 64 + 1];
-  __syncthreads();
-  return bin;
+  lds_barrier();
+  above = S.res[1];
+  count = S.res[2];
+  return S.res[0];
 }
 
-struct SelectArgs {
-  const uint32_t* keys;
-  const uint32_t* hist;
-  const int32_t* seq_lens;
-  int32_t* gt_pos;      // [rows, n_slices, gt_cap]
-  uint2* cand;          // [rows, n_slices, kSlice]  (key, position)
-  int32_t* cnt;         // [rows, n_slices, 2]
-  int32_t* idx_out;     // [rows, K]
-  int T, max_pages, K, n_slices, row_stride, gt_cap, max_seq_len;
-};
+// Radix digits of a key: digit 0 = bits 31..21 (histogrammed by the score kernel), digit 1 =
+// bits 20..10, digit 2 = bits 9..0.  With `resolved` digits known, the unresolved low bits number:
+__device__ __forceinline__ int unresolved_bits(int resolved) {
+  return resolved == 1 ? 21 : (resolved == 2 ? 10 : 0);
+}
 
-__global__ __launch_bounds__(256) void li_select_split(SelectArgs a) {
-  __shared__ uint32_t sh_hist[kBins];
-  __shared__ uint32_t sh[8];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x, slice = blockIdx.y;
-  const int b = row / a.T, t = row % a.T;
-  const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
-  if (n <= a.K || slice * kSlice >= n) return;
-  const uint32_t kp = (uint32_t)min(a.K, n);
-
-  // the slice's keys (16 consecutive per thread) load while the histogram is scanned
-  constexpr int PT = kSlice / kThreads;
-  const int s0 = slice * kSlice + tid * PT;
-  uint32_t kv[PT];
-#pragma unroll
-  for (int j = 0; j < PT / 4; ++j) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.keys + (size_t)row * a.row_stride + s0 + 4 * j);
-    kv[4 * j] = v[0]; kv[4 * j + 1] = v[1]; kv[4 * j + 2] = v[2]; kv[4 * j + 3] = v[3];
-  }
-  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = a.hist[(size_t)row * kBins + i];
-  __syncthreads();
-  uint32_t above;
-  const uint32_t b1 = (uint32_t)find_bin<kBins>(sh_hist, kp, sh, above);
-
-  // ordered compaction of this slice
-  uint32_t ngt = 0, nc = 0;
-#pragma unroll
-  for (int j = 0; j < PT; ++j) {
-    const bool ok = s0 + j < n;
-    const uint32_t d = kv[j] >> 21;
-    ngt += (ok && d > b1) ? 1u : 0u;
-    nc += (ok && d == b1) ? 1u : 0u;
-  }
+// Emits, in ascending order, the positions of one chunk whose bits are set in `sel` (taken) or in
+// `tie` (taken while fewer than `need` ties of the row were seen before).  Thread t holds the two
+// bitmap words of positions base + 64t .. base + 64t + 63.  run_out / run_tie carry the row's
+// emitted count and tie count across chunks.
+__device__ __forceinline__ void emit_words(const uint32_t (&sel)[2], const uint32_t (&tie)[2], int base,
+                                           uint32_t need, int K, int32_t* out, SelScratch& S,
+                                           uint32_t& phase, uint32_t& run_out, uint32_t& run_tie) {
+  const uint32_t cs = __popc(sel[0]) + __popc(sel[1]);
+  const uint32_t ct = __popc(tie[0]) + __popc(tie[1]);
   uint32_t tot;
-  const uint32_t pre = block_exclusive_scan<kThreads>(ngt | (nc << 16), sh, tot);
-  uint32_t og = pre & 0xFFFFu, oc = pre >> 16;
-  const size_t sl = (size_t)row * a.n_slices + slice;
-  int32_t* gt_out = a.gt_pos + sl * a.gt_cap;
-  uint2* c_out = a.cand + sl * kSlice;
+  // taken positions per chunk < K <= 2048 fit 12 bits; ties per chunk <= 65536 fit the other 20
+  const uint32_t pre = sel_scan(cs | (ct << 12), S, phase, tot);
+  uint32_t rank = run_tie + (pre >> 12);
+  uint32_t o = run_out + (pre & 0xFFFu) + (min(rank, need) - min(run_tie, need));
+  const int p0 = base + 64 * (int)threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < PT; ++j) {
-    const int s = s0 + j;
-    const bool ok = s < n;
-    const uint32_t d = kv[j] >> 21;
-    if (ok && d > b1 && og < (uint32_t)a.gt_cap) gt_out[og++] = s;
-    if (ok && d == b1 && oc < (uint32_t)kSlice) c_out[oc++] = make_uint2(kv[j], (uint32_t)s);
+  for (int w = 0; w < 2; ++w) {
+    uint32_t m = sel[w] | tie[w];
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1u;
+      bool take = true;
+      if (!((sel[w] >> j) & 1u)) { take = rank < need; ++rank; }
+      if (take) {
+        if (o < (uint32_t)K) out[o] = p0 + 32 * w + j;
+        ++o;
+      }
+    }
   }
-  if (tid == 0) {
-    a.cnt[sl * 2] = (int32_t)(tot & 0xFFFFu);
-    a.cnt[sl * 2 + 1] = (int32_t)(tot >> 16);
-  }
+  run_out += (tot & 0xFFFu) + (min(run_tie + (tot >> 12), need) - min(run_tie, need));
+  run_tie += tot >> 12;
 }
 
-__device__ __forceinline__ int lower_bound_lds(const int32_t* v, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (v[mid] < x) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-constexpr int kSelThreads = 1024;
-constexpr int kCandCap = 8192;     // candidates staged in LDS; more fall back to global reads
-
-__global__ __launch_bounds__(1024) void li_select_final(SelectArgs a) {
+// The threshold key theta (the K-th largest of the row's n > K keys) is resolved digit by digit,
+// digit 0 from the row histogram.  When the keys sharing the resolved prefix (the "candidates")
+// fit in LDS, each segment's workgroup collects, from its keys, the positions above the prefix
+// range and the (key, position) candidates; with several segments the lists go to global memory
+// and the workgroup that finishes last gathers them.  It resolves the remaining digits over the
+// candidates, then emits every key > theta plus the first `need` keys == theta in position order
+// through per-chunk bitmaps.  A prefix range too big for LDS falls back to one workgroup for the
+// row, which resolves more digits with histogram passes over the row, and, if even the exact key
+// theta has too many ties, emits straight from the keys.
+__global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   constexpr int NT = kSelThreads;
-  __shared__ uint32_t sh_hist[kBins];
-  __shared__ uint32_t sh[NT / 64 + 2];
-  __shared__ int32_t off_g[kMaxSlices + 1], off_c[kMaxSlices + 1];
+  __shared__ uint32_t h1[kBins];           // digit-1 histogram
+  __shared__ uint32_t h2[1024];            // digit-2 histogram
   __shared__ int32_t gt_list[DSA_MAX_TOP_K];
-  __shared__ int32_t sel_list[DSA_MAX_TOP_K];
   __shared__ uint32_t c_key[kCandCap];
   __shared__ int32_t c_pos[kCandCap];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x;
+  __shared__ uint32_t bm_sel[kMapWords], bm_tie[kMapWords];
+  __shared__ SelScratch S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int row = blockIdx.x, seg = blockIdx.y;
   const int b = row / a.T, t = row % a.T;
   const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
   int32_t* out = a.idx_out + (size_t)row * a.K;
   if (n <= a.K) {
-    for (int j = tid; j < a.K; j += NT) out[j] = j < n ? j : -1;
+    if (seg == 0)
+      for (int j = tid; j < a.K; j += NT) out[j] = j < n ? j : -1;
     return;
   }
-  const int kp = a.K;   // n > K
-  const int S = (n + kSlice - 1) / kSlice;
+  const int seg_len = seg_len_of(n);
+  int nseg = (n + seg_len - 1) / seg_len;
+  if (seg >= nseg) return;
+  int lo = seg * seg_len, hi = min(n, lo + seg_len);
+  const uint32_t* keys = a.keys + (size_t)row * a.row_stride;
+  uint32_t phase = 0;
 
-  // slice offsets (S <= kMaxSlices <= NT)
-  uint32_t g = 0, c = 0;
-  if (tid < S) {
-    const size_t sl = (size_t)row * a.n_slices + tid;
-    g = (uint32_t)a.cnt[sl * 2];
-    c = (uint32_t)a.cnt[sl * 2 + 1];
-  }
-  uint32_t G, Cn;
-  const uint32_t og = block_exclusive_scan<NT>(g, sh, G);
-  const uint32_t oc = block_exclusive_scan<NT>(c, sh, Cn);
-  if (tid < S) { off_g[tid] = (int32_t)og; off_c[tid] = (int32_t)oc; }
-  if (tid == 0) { off_g[S] = (int32_t)G; off_c[S] = (int32_t)Cn; }
-  __syncthreads();
-  auto slice_of = [&](const int32_t* off, int i) -> int {   // largest slice with off[slice] <= i
-    int lo = 0, hi = S;
-    while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (off[mid] <= i) lo = mid; else hi = mid; }
-    return lo;
+  // Pass over [lo, hi) in steps of kSelChunk keys: per_step(v, s0) gets this thread's kSelPer
+  // consecutive keys from position s0 on (entries at positions >= hi are zero or stale and must
+  // be masked).  The next step loads while the current one is processed.  A 16-byte load is
+  // issued only if it starts below hi <= n; the row stride is a multiple of 4, so none leaves the
+  // row.
+  auto load_step = [&](u32x4 (&v)[kSelVec], int s0) {
+#pragma unroll
+    for (int u = 0; u < kSelVec; ++u)
+      if (s0 + 4 * u < hi) v[u] = *reinterpret_cast<const u32x4*>(keys + s0 + 4 * u);
   };
-  const uint2* cand = a.cand + (size_t)row * a.n_slices * kSlice;
-  const bool staged = Cn <= (uint32_t)kCandCap;
-  // one pass: candidates (position order) and the positions above the threshold bin into LDS
-  if (staged) {
-    for (int i = tid; i < (int)Cn; i += NT) {
-      const int sl = slice_of(off_c, i);
-      const uint2 e = cand[(size_t)sl * kSlice + (i - off_c[sl])];
-      c_key[i] = e.x;
-      c_pos[i] = (int32_t)e.y;
+  u32x4 cur[kSelVec];
+#pragma unroll
+  for (int u = 0; u < kSelVec; ++u) cur[u] = u32x4{0u, 0u, 0u, 0u};
+  load_step(cur, lo + tid * kSelPer);      // the first step is requested before anything else
+  auto scan_keys = [&](auto&& per_step) {   // runs once per workgroup
+    u32x4 nxt[kSelVec];
+#pragma unroll
+    for (int u = 0; u < kSelVec; ++u) nxt[u] = u32x4{0u, 0u, 0u, 0u};
+    for (int base = lo; base < hi; base += kSelChunk) {
+      const int s0 = base + tid * kSelPer;
+      if (base + kSelChunk < hi) load_step(nxt, s0 + kSelChunk);
+      per_step(cur, s0);
+#pragma unroll
+      for (int u = 0; u < kSelVec; ++u) cur[u] = nxt[u];
+    }
+  };
+  auto key_of = [](const u32x4 (&v)[kSelVec], int j) -> uint32_t { return v[j >> 2][j & 3]; };
+
+  for (int i = tid; i < kBins; i += NT) h1[i] = 0u;
+  h2[tid] = 0u;
+  if (tid == 0) S.cursor = 0u;
+  uint32_t above, C;
+  uint32_t prefix = sel_find_bin<kBins>(a.hist + (size_t)row * kBins, (uint32_t)a.K, S, phase, above, C);
+  uint32_t need = (uint32_t)a.K - above;  // keys still to take from the current prefix range
+  const uint32_t G = above;               // keys above the digit-0 range
+  int resolved = 1;
+  uint32_t G2 = G;                        // keys above the final prefix range (fallback only)
+
+  if (C > (uint32_t)kCandCap) {
+    // one workgroup takes the whole row; more digits from histogram passes over it
+    if (seg != 0) return;
+    nseg = 1; lo = 0; hi = n;
+    while (C > (uint32_t)kCandCap && resolved < 3) {
+      const int sh = unresolved_bits(resolved);
+      uint32_t* hh = resolved == 1 ? h1 : h2;
+      for (int s = tid * 4; s < n; s += NT * 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(keys + s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (s + j < n && (v[j] >> sh) == prefix)
+            atomicAdd(&hh[resolved == 1 ? ((v[j] >> 10) & 2047u) : (v[j] & 1023u)], 1u);
+      }
+      lds_barrier();
+      const uint32_t d = resolved == 1 ? sel_find_bin<kBins>(hh, need, S, phase, above, C)
+                                       : sel_find_bin<1024>(hh, need, S, phase, above, C);
+      need -= above;
+      G2 += above;
+      prefix = (prefix << (resolved == 1 ? 11 : 10)) | d;
+      ++resolved;
     }
   }
-  for (int i = tid; i < (int)G && i < DSA_MAX_TOP_K; i += NT) {
-    const int sl = slice_of(off_g, i);
-    gt_list[i] = a.gt_pos[((size_t)row * a.n_slices + sl) * a.gt_cap + (i - off_g[sl])];
-  }
-  for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
-  __syncthreads();
-  auto key_at = [&](int i) -> uint32_t {
-    if (staged) return c_key[i];
-    const int sl = slice_of(off_c, i);
-    return cand[(size_t)sl * kSlice + (i - off_c[sl])].x;
-  };
-  auto pos_at = [&](int i) -> int32_t {
-    if (staged) return c_pos[i];
-    const int sl = slice_of(off_c, i);
-    return (int32_t)cand[(size_t)sl * kSlice + (i - off_c[sl])].y;
-  };
 
-  // refine the threshold: digit 2 = bits 20..10, digit 3 = bits 9..0
-  uint32_t need = (uint32_t)kp - G;
-  for (int i = tid; i < (int)Cn; i += NT) atomicAdd(&sh_hist[(key_at(i) >> 10) & 2047u], 1u);
-  __syncthreads();
-  uint32_t above;
-  const uint32_t b2 = (uint32_t)find_bin<kBins, NT>(sh_hist, need, sh, above);
-  need -= above;
-  for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
-  __syncthreads();
-  for (int i = tid; i < (int)Cn; i += NT) {
-    const uint32_t k = key_at(i);
-    if (((k >> 10) & 2047u) == b2) atomicAdd(&sh_hist[k & 1023u], 1u);
+  uint32_t run_out = 0, run_tie = 0;
+  if (C <= (uint32_t)kCandCap) {
+    const int shift = unresolved_bits(resolved);
+    const uint32_t hi_key = shift ? ((prefix << shift) | ((1u << shift) - 1u)) : prefix;
+    // collect positions above the prefix range and candidates inside it (any order); each wave
+    // reserves its slots with one LDS atomic
+    scan_keys([&](const u32x4 (&v)[kSelVec], int s0) {
+      uint32_t gm = 0, cm = 0;
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) {
+        const uint32_t k = key_of(v, j);
+        const bool ok = s0 + j < hi;
+        gm |= (ok && k > hi_key) ? (1u << j) : 0u;
+        cm |= (ok && (k >> shift) == prefix) ? (1u << j) : 0u;
+      }
+      const uint32_t mine = __popc(gm) | ((uint32_t)__popc(cm) << 16);
+      const uint32_t incl = wave_inclusive_scan(mine);
+      uint32_t wbase = 0;
+      if (lane == 63) wbase = atomicAdd(&S.cursor, incl);
+      wbase = __builtin_amdgcn_readlane(wbase, 63);
+      const uint32_t off = wbase + incl - mine;
+      uint32_t og = off & 0xFFFFu, oc = off >> 16;
+      while (gm) {
+        const int j = __ffs(gm) - 1;
+        gm &= gm - 1u;
+        if (og < DSA_MAX_TOP_K) gt_list[og] = s0 + j;
+        ++og;
+      }
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j)
+        if ((cm >> j) & 1u) {
+          if (oc < (uint32_t)kCandCap) { c_key[oc] = key_of(v, j); c_pos[oc] = s0 + j; }
+          ++oc;
+        }
+    });
+    lds_barrier();
+    if (nseg > 1) {
+      // publish this segment's lists; the last segment to finish carries on with the row
+      const uint32_t cnt = S.cursor;
+      const uint32_t ng = min(cnt & 0xFFFFu, (uint32_t)DSA_MAX_TOP_K), nc = min(cnt >> 16, (uint32_t)kCandCap);
+      uint32_t* ctl = a.ctl + (size_t)row * 4;
+      if (tid == 0) {
+        S.pub[0] = atomicAdd(&ctl[1], ng);
+        S.pub[1] = atomicAdd(&ctl[2], nc);
+      }
+      lds_barrier();
+      const uint32_t gb = S.pub[0], cb = S.pub[1];
+      int32_t* g_gt = a.g_gt + (size_t)row * DSA_MAX_TOP_K;
+      uint2* g_c = a.g_cand + (size_t)row * kCandCap;
+      // The lists travel through device-coherent (agent-scope) stores and loads, which go past
+      // the per-XCD L2s, so finishing the stores (vmcnt) before the counter update is enough to
+      // publish them; a full release/acquire fence would write back and invalidate the whole L2
+      // for every segment.
+      for (uint32_t i = tid; i < ng; i += NT)
+        if (gb + i < DSA_MAX_TOP_K)
+          __hip_atomic_store(&g_gt[gb + i], gt_list[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = tid; i < nc; i += NT)
+        if (cb + i < (uint32_t)kCandCap) {
+          const uint64_t e = (uint64_t)c_key[i] | ((uint64_t)(uint32_t)c_pos[i] << 32);
+          __hip_atomic_store(reinterpret_cast<uint64_t*>(&g_c[cb + i]), e, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tid == 0) S.pub[2] = atomicAdd(&ctl[0], 1u);
+      lds_barrier();
+      if (S.pub[2] != (uint32_t)(nseg - 1)) return;
+      for (uint32_t i = tid; i < G; i += NT)
+        gt_list[i] = __hip_atomic_load(&g_gt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint32_t i = tid; i < C; i += NT) {
+        const uint64_t e = __hip_atomic_load(reinterpret_cast<uint64_t*>(&g_c[i]), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        c_key[i] = (uint32_t)e;
+        c_pos[i] = (int32_t)(e >> 32);
+      }
+      lds_barrier();
+    }
+    const int ng = (int)min(G2, (uint32_t)DSA_MAX_TOP_K), nc = (int)C;
+    // remaining digits over the candidates (each digit's histogram is used once)
+    if (resolved == 1) {
+      for (int i = tid; i < nc; i += NT) atomicAdd(&h1[(c_key[i] >> 10) & 2047u], 1u);
+      lds_barrier();
+      uint32_t cnt;
+      const uint32_t d = sel_find_bin<kBins>(h1, need, S, phase, above, cnt);
+      need -= above;
+      prefix = (prefix << 11) | d;
+      resolved = 2;
+    }
+    if (resolved == 2) {
+      for (int i = tid; i < nc; i += NT) {
+        const uint32_t k = c_key[i];
+        if ((k >> 10) == prefix) atomicAdd(&h2[k & 1023u], 1u);
+      }
+      lds_barrier();
+      uint32_t cnt;
+      const uint32_t d = sel_find_bin<1024>(h2, need, S, phase, above, cnt);
+      need -= above;
+      prefix = (prefix << 10) | d;
+    }
+    const uint32_t theta = prefix;       // the exact threshold key; `need` of its ties are kept
+    for (int c0 = 0; c0 < n; c0 += kMapBits) {
+      const int c1 = min(n, c0 + kMapBits);
+      bm_sel[2 * tid] = 0u; bm_sel[2 * tid + 1] = 0u;
+      bm_tie[2 * tid] = 0u; bm_tie[2 * tid + 1] = 0u;
+      lds_barrier();
+      for (int i = tid; i < ng; i += NT) {
+        const int p = gt_list[i];
+        if (p >= c0 && p < c1) atomicOr(&bm_sel[(p - c0) >> 5], 1u << ((p - c0) & 31));
+      }
+      for (int i = tid; i < nc; i += NT) {
+        const int p = c_pos[i];
+        const uint32_t k = c_key[i];
+        if (p >= c0 && p < c1 && k >= theta)
+          atomicOr(k > theta ? &bm_sel[(p - c0) >> 5] : &bm_tie[(p - c0) >> 5], 1u << ((p - c0) & 31));
+      }
+      lds_barrier();
+      const uint32_t sw[2] = {bm_sel[2 * tid], bm_sel[2 * tid + 1]};
+      const uint32_t tw[2] = {bm_tie[2 * tid], bm_tie[2 * tid + 1]};
+      emit_words(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
+    }
+  } else {
+    // theta is exact (all digits resolved) and its ties exceed the staging space: the bitmap
+    // words come straight from the keys
+    const uint32_t theta = prefix;
+    for (int c0 = 0; c0 < n; c0 += kMapBits) {
+      uint32_t sw[2] = {0u, 0u}, tw[2] = {0u, 0u};
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int p0 = c0 + 64 * tid + 32 * w;
+        for (int u = 0; u < 8; ++u) {
+          if (p0 + 4 * u >= n) break;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(keys + p0 + 4 * u);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool ok = p0 + 4 * u + j < n;
+            sw[w] |= (ok && v[j] > theta) ? (1u << (4 * u + j)) : 0u;
+            tw[w] |= (ok && v[j] == theta) ? (1u << (4 * u + j)) : 0u;
+          }
+        }
+      }
+      emit_words(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
+    }
   }
-  const uint32_t b1 = Cn > 0 ? key_at(0) >> 21 : 0u;
-  __syncthreads();
-  const uint32_t b3 = (uint32_t)find_bin<1024, NT>(sh_hist, need, sh, above);
-  need -= above;                           // ties of the threshold key to keep (>= 1)
-  const uint32_t theta = (b1 << 21) | (b2 << 10) | b3;
-
-  // candidates above theta, plus the first `need` ties in position order
-  uint32_t run_sel = 0, run_tie = 0;
-  for (int base = 0; base < (int)Cn; base += NT) {
-    const int i = base + tid;
-    uint32_t k = 0;
-    int32_t p = 0;
-    if (i < (int)Cn) { k = key_at(i); p = pos_at(i); }
-    const bool tie = i < (int)Cn && k == theta;
-    const bool above_t = i < (int)Cn && k > theta;
-    uint32_t tot;
-    const uint32_t pre = block_exclusive_scan<NT>((tie ? 1u : 0u) | (above_t ? 0x10000u : 0u), sh, tot);
-    const uint32_t rank = run_tie + (pre & 0xFFFFu);          // ties before this one
-    const uint32_t n_above = pre >> 16;                       // above-theta before this one (tile)
-    const bool sel = above_t || (tie && rank < need);
-    // selected before this one in the tile: all above-theta ones, plus ties with rank < need
-    const uint32_t ties_sel_before = min(rank, need) - min(run_tie, need);
-    const uint32_t pos = run_sel + n_above + ties_sel_before;
-    if (sel && pos < DSA_MAX_TOP_K) sel_list[pos] = p;
-    run_sel += (tot >> 16) + (min(run_tie + (tot & 0xFFFFu), need) - min(run_tie, need));
-    run_tie += tot & 0xFFFFu;
-  }
-  __syncthreads();
-  const int ng = min((int)G, a.K), ns = min((int)run_sel, a.K - ng);   // ng + ns == K
-  for (int i = tid; i < ng; i += NT) {
-    const int p = gt_list[i];
-    out[i + lower_bound_lds(sel_list, ns, p)] = p;
-  }
-  for (int j = tid; j < ns; j += NT) {
-    const int p = sel_list[j];
-    out[j + lower_bound_lds(gt_list, ng, p)] = p;
-  }
-  for (int j = ng + ns + tid; j < a.K; j += NT) out[j] = -1;
+  for (int j = (int)run_out + tid; j < a.K; j += NT) out[j] = -1;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -716,18 +848,20 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S) {
   IndexerPlan p;
   p.rows = L.batch * S.T;
-  p.row_stride = (int)align_up((size_t)L.max_seq_len, kSlice);
-  p.n_slices = p.row_stride / kSlice;
-  p.gt_cap = S.top_k < kSlice ? S.top_k : kSlice;
+  p.row_stride = (int)align_up((size_t)L.max_seq_len, 64);
   p.n_chunks = (L.max_seq_len + kChunkKeys - 1) / kChunkKeys;
   p.tq = S.T == 1 ? 1 : (S.T == 2 ? 2 : 4);
   p.n_qtiles = (S.T + p.tq - 1) / p.tq;
   size_t off = 0;
-  p.off_hist = off; off = align_up(off + (size_t)p.rows * kBins * 4, 256);
+  // the select's per-row control words follow the histograms so one clear covers both
+  p.off_hist = off; off = align_up(off + (size_t)p.rows * (kBins + 4) * 4, 256);
   p.off_keys = off; off = align_up(off + (size_t)p.rows * p.row_stride * 4, 256);
-  p.off_gt = off;   off = align_up(off + (size_t)p.rows * p.n_slices * p.gt_cap * 4, 256);
-  p.off_cand = off; off = align_up(off + (size_t)p.rows * p.n_slices * kSlice * 8, 256);
-  p.off_cnt = off;  off = align_up(off + (size_t)p.rows * p.n_slices * 2 * 4, 256);
+  p.n_seg = (L.max_seq_len + seg_len_of(L.max_seq_len) - 1) / seg_len_of(L.max_seq_len);
+  p.off_gt = p.off_cand = 0;
+  if (p.n_seg > 1) {
+    p.off_gt = off; off = align_up(off + (size_t)p.rows * DSA_MAX_TOP_K * 4, 256);
+    p.off_cand = off; off = align_up(off + (size_t)p.rows * kCandCap * 8, 256);
+  }
   p.total = off;
   return p;
 }
@@ -771,7 +905,7 @@ static int device_cus() {
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t st) {
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
-  const size_t hist_words = (size_t)p.rows * kBins;
+  const size_t hist_words = (size_t)p.rows * (kBins + 4);   // histograms + select control words
   const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
   {
     LaunchScope ls("li_zero_hist", st);
@@ -815,20 +949,15 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   SelectArgs sa;
   sa.keys = s.keys;
   sa.hist = hist;
+  sa.ctl = hist + (size_t)p.rows * kBins;
+  sa.g_gt = reinterpret_cast<int32_t*>(ws + p.off_gt);
+  sa.g_cand = reinterpret_cast<uint2*>(ws + p.off_cand);
   sa.seq_lens = a.seq_lens;
-  sa.gt_pos = reinterpret_cast<int32_t*>(ws + p.off_gt);
-  sa.cand = reinterpret_cast<uint2*>(ws + p.off_cand);
-  sa.cnt = reinterpret_cast<int32_t*>(ws + p.off_cnt);
   sa.idx_out = a.idx_out;
-  sa.T = a.T; sa.max_pages = a.max_pages; sa.K = a.top_k; sa.n_slices = p.n_slices;
-  sa.row_stride = p.row_stride; sa.gt_cap = p.gt_cap; sa.max_seq_len = a.max_seq_len;
+  sa.T = a.T; sa.K = a.top_k; sa.row_stride = p.row_stride; sa.max_seq_len = a.max_seq_len;
   {
-    LaunchScope ls("li_select_split", st);
-    hipLaunchKernelGGL(li_select_split, dim3(p.rows, p.n_slices), dim3(kThreads), 0, st, sa);
-  }
-  {
-    LaunchScope ls("li_select_final", st);
-    hipLaunchKernelGGL(li_select_final, dim3(p.rows), dim3(kSelThreads), 0, st, sa);
+    LaunchScope ls("li_select", st);
+    hipLaunchKernelGGL(li_select, dim3(p.rows, p.n_seg), dim3(kSelThreads), 0, st, sa);
   }
   return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
 
-Sizes span several score chunks (1024 keys), select slices (4096 keys), attention tiles (32 rows)
+Sizes span several score chunks (1024 keys), select scan steps (16384 keys), attention tiles (32 rows)
 and splits, with ragged tails (lengths not multiples of 64).  Exact-arithmetic cases (integer grids,
 exact fp8 grid) must match the oracle's indices bit for bit; Gaussian cases use the near-tie band.
 Attention is always compared on one shared index tensor (the GPU's own indices).
@@ -73,6 +73,54 @@ def test_wide_grid_exact(T, lens):
 
 def test_tie_heavy_exact():
     spec = W.custom("ties_wide", 2, 1, (3500, 6000), 64, 128, 2048, 128, values="ties")
+    _run(spec, exact=True, check_sfa=False)
+
+
+def _key_u32(x):
+    """Order-preserving uint32 image of float32 values (-0 folded onto +0)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).copy()
+    u[(u << 1) == 0] = 0
+    return np.where((u & 0x80000000) != 0, ~u, u | 0x80000000).astype(np.uint32)
+
+
+def _threshold_populations(extra, rows):
+    """Per row: keys sharing the K'-th key's top 11 bits, top 22 bits, and all 32 bits."""
+    out = []
+    for r in rows:
+        sc, th = extra[r]
+        k, kt = _key_u32(sc), _key_u32([th])[0]
+        out.append(tuple(int(np.sum((k >> s) == (kt >> s))) for s in (21, 10, 0)))
+    return out
+
+
+# Scores squeezed into one coarse bin (17 exact values, thousands of ties each) and a two-value
+# tie flood: the threshold bin exceeds the 8192 candidates the select stages in LDS, so it takes
+# the extra histogram passes (narrow at 70001 keys needs two); ties2 rows 0 and 70000 keep more
+# than 8192 exact ties at the threshold, so the selection is emitted straight from the keys.
+@pytest.mark.parametrize("values,lens,expect", [
+    ("narrow", (60000, 30000), [lambda p: p[0] > 8192 and p[1] <= 8192] * 2),
+    ("ties2", (20000, 12000), [lambda p: p[2] > 8192, lambda p: p[0] <= 8192]),
+    ("ties2", (70000,), [lambda p: p[2] > 8192]),
+    ("narrow", (70001,), [lambda p: p[1] > 8192 and p[2] <= 8192]),
+])
+def test_select_crowded_threshold_exact(values, lens, expect):
+    spec = W.custom(values, len(lens), 1, lens, 64, 128, 2048, 16, values=values)
+    print(f"[case] {spec.name} lens={lens}", flush=True)
+    c = W.make_case(spec)
+    d = Dev(c)
+    idx = to_np(d.indexer())
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=2048, dtype="bf16",
+                                         return_scores=True)
+    pops = _threshold_populations(extra, [(b, 0) for b in range(len(lens))])
+    assert all(f(p) for f, p in zip(expect, pops)), pops
+    assert np.array_equal(idx, ref)
+
+
+# Rows longer than one select segment (16384 keys) are split over several workgroups whose lists
+# meet in global memory; rows longer than 65536 keys are emitted in several bitmap chunks.
+@pytest.mark.parametrize("T,lens", [(1, (16384, 16385, 40000, 70000)), (4, (33000, 20000))])
+def test_multi_segment_rows_exact(T, lens):
+    spec = W.custom("grid8_long", len(lens), T, lens, 64, 128, 2048, 16, values="grid8")
     _run(spec, exact=True, check_sfa=False)
 
 

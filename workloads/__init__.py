@@ -49,7 +49,7 @@ class CaseSpec:
     K: int                 # top-k
     H: int                 # attention heads
     idx_dtype: str = "bf16"   # "bf16" | "fp8"
-    values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "fp8grid" | "sharp"
+    values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "ties2" | "narrow" | "fp8grid" | "sharp"
     sharp_c: float = 1.0
     variant: int = 0
     spare_pages: int = 1
@@ -213,17 +213,24 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
 
     # ---- indexer q / k / w
     if spec.idx_dtype == "bf16":
-        if v in ("grid", "grid8", "ties"):
+        if v in ("grid", "grid8", "ties", "ties2", "narrow"):
             # grid: multiples of 1/16 in [-1, 1]; grid8: in [-1/2, 1/2], which keeps the wide
             # (64 heads x 128 dims) scores below 2^11 so fp32 sums are exact in any order
-            lim = 8 if v in ("grid8", "ties") else 16
+            lim = 16 if v == "grid" else 8
             q_idx = _grid_bf16(rngq, (B, T, HI, DI), -lim, lim)
-            if v == "ties":
+            if v in ("ties", "ties2"):
                 # few distinct key rows copied to many positions: many exact score ties
-                base = _grid_bf16(rngk, (7, DI), -lim, lim)
-                k_cache = base[rngk.integers(0, 7, size=(P, PAGE))]
+                nd = 7 if v == "ties" else 2
+                base = _grid_bf16(rngk, (nd, DI), -lim, lim)
+                k_cache = base[rngk.integers(0, nd, size=(P, PAGE))]
             else:
                 k_cache = _grid_bf16(rngk, (P, PAGE, DI), -lim, lim)
+            if v == "narrow":
+                # every q and k row is 1/2 in all but the last dim: all scores sit in a narrow
+                # band (one coarse histogram bin) with a few exact values, each tied many times
+                half = f32_to_bf16_bits(np.float32(0.5))
+                q_idx[..., :-1] = half
+                k_cache[..., :-1] = half
             w = (rngw.integers(0, 16, size=(B, T, HI), endpoint=True) / 16.0).astype(np.float32)
         else:
             q_idx = _gauss_bf16(key0 + [2], (B, T, HI, DI), 1.0 / np.sqrt(DI))
@@ -260,7 +267,7 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
         raise ValueError(spec.idx_dtype)
 
     # ---- attention q / kv
-    if v in ("grid", "grid8", "ties", "fp8grid"):
+    if v in ("grid", "grid8", "ties", "ties2", "narrow", "fp8grid"):
         q_attn = _grid_bf16(rngs, (B, T, H, DQK))
         kv_cache = _grid_bf16(rngv, (P, PAGE, DQK))
     elif v == "sharp":
