@@ -12,12 +12,13 @@ SOURCES = ["indexer.hip", "sfa.hip", "dsa_api.cpp", "dsa_profile.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU ops stay disabled: the compiler would otherwise form v_pk_*_f32 from plain
 # float code.
-# MFMA accumulators are selected in VGPR form: with AGPR-form selection the register allocator
-# shuttled the attention accumulator between register files on every tile.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# The score kernel's MFMA accumulators are selected in VGPR form (its weighted reduction reads
+# them with VALU every tile).  The attention kernel keeps its 256-register output accumulator in
+# the accumulation registers, so it uses the default selection.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def build_library(verbose: bool = False, extra_flags=()) -> str:
@@ -28,7 +29,8 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     def compile_one(src):
         obj = os.path.join(objdir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra_flags, *lang, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)

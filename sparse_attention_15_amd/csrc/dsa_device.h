@@ -33,6 +33,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Direct-to-LDS load of 16 bytes per lane: lane i's 16 bytes from `src` land at LDS byte address
+// lds_base + 16*i (lds_base wave-uniform).  Written as inline assembly on purpose: the compiler
+// treats its builtin form as an unknown write to LDS and makes every later LDS read wait for all
+// outstanding global loads (vmcnt(0)), which serialises a ring of tiles kept in flight.  Callers
+// count these loads themselves (wait_vmcnt) and put a barrier between landing and reading.
+__device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base), "v"(src)
+               : "memory", "m0");
+}
+
 // Waits until at most N of this wave's global loads (including direct-to-LDS loads) are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

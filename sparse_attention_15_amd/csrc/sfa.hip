@@ -5,17 +5,19 @@
 // K3.1 Pro Sparse Attention Inference", "Inheritance and Extension of Core Operators" (blockwise
 // attention over fixed-size KV blocks, reduced across blocks without a global softmax).
 //
-// One workgroup handles one query row, up to 128 heads (32 per wave) and a contiguous range of
-// the row's selected indices (a "split").  Per 32-index tile it gathers the 1152-byte latent rows
-// (page-table resolved) into LDS twice: row-major for the score product and transposed (first
-// 512 columns) for the value product.  With the key tile as MFMA operand A and the wave's query
-// rows (held in registers) as operand B it computes S^T = X q^T, so each lane ends up owning one
-// head and 16 keys: the online-softmax row max and sum need one cross-half exchange, and the
-// probabilities feed the value product O^T += V^T P^T as operand B without leaving the lane.  The
-// accumulator O^T (512 x 32 per wave) stays in registers; the running max is kept in the log2
-// domain (exp2 with log2(e) folded into the scale).  With one split the workgroup normalises and
-// writes bf16 output and the natural-log LSE; with several, each writes (m, l, O) partials and
-// sfa_combine merges them: M = max m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+// One workgroup handles one query row, up to 128 heads (one wave per 32 heads) and a contiguous
+// range of the row's selected indices (a "split").  Per 32-index tile it gathers the 1152-byte
+// latent rows (page-table resolved) into an LDS ring with direct-to-LDS loads, so every KV row is
+// fetched once for all heads.  With the key tile as MFMA operand A and the wave's query rows (all
+// 576 columns, held in VGPRs) as operand B it computes S^T = X q^T: each lane owns one head and
+// 16 of the tile's keys, the other 16 sit in the lane 32 apart, so the online-softmax max and sum
+// need one cross-half exchange, and the probabilities feed the value product O^T += V^T P^T as
+// operand B without leaving the lane.  The value product reads V^T straight from the row-major
+// tile with transposed LDS reads.  The accumulator O^T (512 x 32 per wave, 256 registers) lives in
+// the accumulation registers; the running max is kept in the log2 domain (exp2 with log2(e) folded
+// into the scale).  With one split the workgroup normalises and writes bf16 output and the
+// natural-log LSE; with several, each writes (m, l, O) partials and sfa_combine merges them:
+// M = max m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -31,7 +33,8 @@ constexpr int kQSteps = kDimQK / 16;        // 36 MFMA K steps for the score pro
 constexpr int kVBlocks = kDimV / 32;        // 16 M blocks of the value product
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.f;        // lazy-rescale threshold (log2 units)
+constexpr float kRefMargin = 64.f;         // reference max = first tile's max + this (log2 units)
+constexpr float kRefLimit = 100.f;         // a logit above reference + this restarts the split
 
 struct SfaArgs {
   const unsigned char* q;       // [rows, H, 576] bf16
@@ -42,7 +45,7 @@ struct SfaArgs {
   __bf16* out;                  // [rows, H, 512]
   float* lse;                   // [rows, H] or null
   float* part_ml;               // [rows, splits, H, 2]
-  float* part_o;                // [rows, splits, waves, 16, 16, 64]
+  float* part_o;                // [rows, splits, head groups, 16, 16, 64]
   int T, H, K, max_pages, num_pages, n_splits, keys_per_split, max_seq_len;
   float scale_log2;             // sm_scale * log2(e)
 };
@@ -72,45 +75,34 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
 constexpr int kTileBytes = kBK * kRowBytes;          // 36864
 constexpr int kDmaPerTile = kTileBytes / 1024;       // 36 wave-wide 16-byte-per-lane loads
-constexpr int kStages = 3;                           // gather ring depth (the main loop is unrolled by it)
+constexpr int kStages = 4;                           // gather ring depth (the main loop is unrolled by it)
 constexpr int kMaxSplitKeys = DSA_MAX_TOP_K;
 
-template <int NW, int W>
-__device__ __forceinline__ void wait_tile_dma(bool next_pending) {
-  // loads this wave issues per tile; the ring keeps at most one later tile in flight
-  constexpr int n = (kDmaPerTile - W + NW - 1) / NW;
-  if (next_pending) wait_vmcnt<n>(); else wait_vmcnt<0>();
+// Waits until this wave's loads of the tile being consumed have landed; `later` of its later
+// tiles (n loads each) may stay in flight.
+template <int n>
+__device__ __forceinline__ void wait_ring(int later) {
+  if (later >= 2) wait_vmcnt<(2 * n > 63 ? 63 : 2 * n)>();   // the counter saturates at 63
+  else if (later == 1) wait_vmcnt<n>();
+  else wait_vmcnt<0>();
 }
 
 template <int NW>
-__device__ __forceinline__ void wait_tile(int wave, bool next_pending) {
-  // dispatch the per-wave count to an immediate
-  if constexpr (NW == 8) {
-    if (wave < kDmaPerTile % 8) wait_tile_dma<8, 0>(next_pending); else wait_tile_dma<8, 7>(next_pending);
-  } else if constexpr (NW == 6) {
-    wait_tile_dma<6, 0>(next_pending);
-  } else if constexpr (NW == 4) {
-    wait_tile_dma<4, 0>(next_pending);
-  } else {
-    wait_tile_dma<2, 0>(next_pending);
-  }
-}
-
-template <int NG>
-__global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
-  constexpr int NT = NG * 128;              // two waves per 32-head group
-  constexpr int NW = NG * 2;
-  static_assert(kDmaPerTile % NW == 0 || NW == 8, "per-wave load count must be uniform or split 2-way");
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sfa_main(SfaArgs a) {
+  constexpr int NT = NW * 64;               // one wave per 32-head group
+  constexpr int kDmaWave = kDmaPerTile / NW;
+  static_assert(kDmaPerTile % NW == 0, "per-wave load count must be uniform");
+  static_assert(kStages - 2 <= 2, "wait_ring handles up to two later tiles");
   __shared__ __attribute__((aligned(1024))) unsigned char lds_kv[kStages][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float lds_sx[NG * 2 * 16 * 64];   // partial-score exchange
   __shared__ int lds_rows[kMaxSplitKeys];   // physical row of each selected index, -1 = skip
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS DMA bases stay in SGPRs
   const int nl = lane & 31, hh = lane >> 5;
-  const int g = wave % NG, hf = wave / NG;  // head group, half (of the contraction / of V)
   const int row = blockIdx.x, split = blockIdx.y;
   const int NGT = (a.H + 31) / 32;          // 32-head groups over all workgroups of a row
-  const int gg = blockIdx.z * NG + g;       // this wave's global head group
+  const int gg = blockIdx.z * NW + wave;    // this wave's global head group
   const int b = row / a.T, t = row % a.T;
   const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
   const int k_begin = split * a.keys_per_split;
@@ -120,116 +112,144 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
   const int head = gg * 32 + nl;
   const bool hvalid = head < a.H;
 
-  // row table for this split (one round of idx + block-table loads for the whole split)
+  // B operand of the score product: this lane's head row of q (36 K steps of 16 columns).  Lanes
+  // of a head beyond H read head 0 and their results are never stored.  Issued first: nothing
+  // waits for these loads before the first score product.
+  bf16x8 qf[kQSteps];
+  {
+    const unsigned char* src = a.q + ((size_t)row * a.H + (hvalid ? head : 0)) * kRowBytes + 16 * hh;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * ks));
+  }
+
+  // Row table for this split (one round of idx + block-table loads): lds_rows[j] = physical row
+  // of selected index j, -1 if it is not a visible position; lds_valid[tile] = its 32-bit mask.
+  __shared__ int lds_fill;                  // first j with a visible position
+  __shared__ uint32_t lds_valid[kMaxSplitKeys / kBK];
+  __shared__ int lds_epoch;                 // restarts requested by any wave (see below)
+  if (tid == 0) { lds_fill = kMaxSplitKeys; lds_epoch = 0; }
+  lds_barrier();
   {
     const int32_t* idx = a.idx + (size_t)row * a.K + k_begin;
     const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-    for (int j = tid; j < ntiles * kBK; j += NT) {
+    for (int j = tid; j < ntiles * kBK; j += NT) {   // NT is a multiple of 64: whole waves
       int r = -1;
       if (j < nkeys) {
         const int s = idx[j];
         if (s >= 0 && s < n) r = clamp_page(bt[s / kPage], a.num_pages) * kPage + (s % kPage);
       }
       lds_rows[j] = r;
+      const uint64_t bal = __ballot(r >= 0);
+      if ((lane & 31) == 0) lds_valid[j >> 5] = (uint32_t)(bal >> (lane & 32));
+      if (r >= 0) atomicMin(&lds_fill, j);
     }
   }
-  __syncthreads();
+  // The query rows and the row table have landed before the gathers start.  A compiler-visible
+  // wait (vmcnt 0), so it knows no ordinary load is outstanding inside the main loop: it does not
+  // count the direct-to-LDS loads, and would otherwise place waits for q there that also stall on
+  // the tiles in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
+  // Keys that are not selected are gathered from the split's first selected row (finite data, so
+  // their zero probabilities never meet a NaN); a split without any selected key skips its tiles.
+  const int fill_j = lds_fill;
+  const int fill_row = fill_j < kMaxSplitKeys ? lds_rows[fill_j] : 0;
+  const int ntiles_run = fill_j < kMaxSplitKeys ? ntiles : 0;
 
   // gather tile `tile` into ring slot `buf`: this wave's loads are chunks 64*q + lane of the tile,
-  // q = wave, wave + NW, ...; slot position p holds row p / 72, chunk (p % 72) ^ swz(row)
-  constexpr int kDmaMax = (kDmaPerTile + NW - 1) / NW;
+  // q = wave, wave + NW, ...; slot position p holds row p / 72, chunk (p % 72) ^ swz(row).  The
+  // per-lane coordinates are recomputed on every call (a few VALU ops) instead of being held in
+  // registers across the main loop, and all row-table reads go out before the first load.  Every
+  // wave issues the same number of loads per tile, which the ring's counter waits rely on.
   auto issue = [&](int tile, int buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int prow[kDmaWave];
 #pragma unroll
-    for (int u = 0; u < kDmaMax; ++u) {
-      const int q = wave + u * NW;
-      if (q < kDmaPerTile) {
-        const int p = 64 * q + lane;
-        const int r = p / 72;
-        const int c = (p % 72) ^ swz(r);
-        const int prow = lds_rows[tile * kBK + r];
-        const unsigned char* src = a.kv + (size_t)(prow < 0 ? 0 : prow) * kRowBytes + 16 * c;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds_kv[buf] + 1024 * q), 16, 0, 0);
-      }
+    for (int u = 0; u < kDmaWave; ++u) prow[u] = lds_rows[tile * kBK + (64 * (wave + u * NW) + ln) / 72];
+#pragma unroll
+    for (int u = 0; u < kDmaWave; ++u) {
+      const int p = 64 * (wave + u * NW) + ln;
+      const int c = (p % 72) ^ swz(p / 72);
+      const int pr = prow[u] < 0 ? fill_row : prow[u];
+      const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 16 * c;
+      lds_dma16(src, lds_kv[buf] + 1024 * (wave + u * NW));
     }
   };
 
-  // B operand of the score product: this lane's head row of q over this wave's half of the
-  // 576 latent columns (18 K steps of 16)
-  bf16x8 qf[kQSteps / 2];
-  {
-    const unsigned char* src = a.q + ((size_t)row * a.H + (hvalid ? head : 0)) * kRowBytes +
-                               hf * (kRowBytes / 2) + 16 * hh;
-    const uint32_t keep = hvalid ? 0xFFFFFFFFu : 0u;
+  // O^T: 512 latent columns (16 blocks of 32) x 32 heads
+  f32x16 o[kVBlocks];
 #pragma unroll
-    for (int ks = 0; ks < kQSteps / 2; ++ks) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(src + 32 * ks);
-      v[0] &= keep; v[1] &= keep; v[2] &= keep; v[3] &= keep;
-      qf[ks] = as_bf16x8(v);
-    }
-  }
-  // O^T for this wave's 256 latent columns (8 blocks of 32) x 32 heads
-  f32x16 o[kVBlocks / 2];
-#pragma unroll
-  for (int mb = 0; mb < kVBlocks / 2; ++mb)
+  for (int mb = 0; mb < kVBlocks; ++mb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
-  // running max in log2 units; a finite floor keeps masked (-inf) logits at probability 0
-  // without special cases (the first valid tile always moves the reference)
-  float m_run = -1e30f, l_run = 0.f;
-
-  float* sx_mine = lds_sx + ((g * 2 + hf) * 16) * 64 + lane;
-  const float* sx_other = lds_sx + ((g * 2 + (hf ^ 1)) * 16) * 64 + lane;
+  // Fixed softmax reference per head (log2 units), set from the first tile with a valid key:
+  // its max plus kRefMargin.  Probabilities 2^(s - m_ref) stay below 2^kRefLimit as long as no
+  // logit exceeds m_ref + kRefLimit, so the accumulator never needs rescaling.  A logit beyond
+  // that (a spread of more than 164 log2 units inside the row) raises the reference and restarts
+  // the split from its first tile.  The finite floor keeps masked (-inf) logits at probability 0.
+  constexpr float kNoRef = -1e30f;
+  float m_run = kNoRef, l_run = 0.f;
+  int epoch = 0;                            // restarts seen by this wave
 
   // Per-lane LDS byte offsets.  XOR with swz() only touches the low three bits of a chunk index,
   // so offsets repeat every 8 chunks: four bases per operand plus immediate strides cover a tile.
-  // Score A operand: row nl, chunk c = 36*hf + 2*ks + hh; ks = 4u + v -> base[v] + 128*u.
+  // Score A operand: row nl, chunk c = 2*ks + hh; ks = 4u + v -> base[v] + 128*u.
   int qk_off[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int c = 36 * hf + 2 * v + hh;
-    qk_off[v] = nl * kRowBytes + 16 * ((c & ~7) | ((c & 7) ^ swz(nl)));
-  }
+  for (int v = 0; v < 4; ++v) qk_off[v] = nl * kRowBytes + 16 * ((2 * v + hh) ^ swz(nl));
   // Value A operand (transposed reads): key = 16*k2 + 8*q + kq, column = dim0 + 32*mb with
-  // mb = 2u + v; swz(key) = swz(kq) ^ 4q, so the offset is base[q][v] + 16*8*u + 16*kRowBytes*k2.
+  // mb = 2u + v; swz(key) = swz(kq) ^ 4q, so the offset is base[q][v] + 128*u + 16*kRowBytes*k2.
   const int kq = 4 * hh + ((lane & 15) >> 2);
-  const int dim0 = hf * (kDimV / 2) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int dim0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int pv_off[2][2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int key = 8 * q + kq;
-      const int c = (dim0 >> 3) + 4 * v;
-      pv_off[q][v] = key * kRowBytes + 16 * ((c & ~7) | ((c & 7) ^ swz(key))) + 2 * (dim0 & 7);
+      const int c = (dim0 >> 3) + 4 * v;    // < 8
+      pv_off[q][v] = key * kRowBytes + 16 * (c ^ swz(key)) + 2 * (dim0 & 7);
     }
 
   // One tile of the main loop.  The ring slot is a compile-time constant (the loop is unrolled by
   // the ring depth), so every LDS address below is a per-lane base plus an immediate offset.
   auto step = [&](int it, auto slot) {
     constexpr int buf = decltype(slot)::value;
-    wait_tile<NW>(wave, it + 1 < ntiles);
-    lds_barrier();                          // tile `it` landed for every wave; slot it+2 is free
-    if (it + 2 < ntiles) issue(it + 2, (buf + 2) % kStages);
+    wait_ring<kDmaWave>(min(kStages - 2, ntiles_run - 1 - it));
+    lds_barrier();                          // tile `it` landed for every wave; slot it-1 is free
+    if (it + kStages - 1 < ntiles_run) issue(it + kStages - 1, (buf + kStages - 1) % kStages);
     const unsigned char* tile = lds_kv[buf];
-    const uint32_t valid = (uint32_t)__ballot(lane < kBK && lds_rows[it * kBK + (lane & 31)] >= 0);
+    const uint32_t valid = lds_valid[it];
 
-    // partial S^T = X q^T over this wave's 288 columns: rows = the tile's 32 keys, cols = heads
+    // S^T = X q^T: rows = the tile's 32 keys, columns = this wave's 32 heads.  The A fragments
+    // stream through a 4-deep register ring: the read for step ks + 4 is issued right behind the
+    // MFMA of step ks, so LDS latency hides under the MFMAs in between.
+    auto a_frag = [&](int ks) {
+      return *reinterpret_cast<const u32x4*>(tile + qk_off[ks & 3] + 128 * (ks >> 2));
+    };
+    auto v_frag = [&](int j, int q) {     // j = 16*k2 + mb
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+          tile + pv_off[q][j & 1] + 128 * ((j & 15) >> 1) + 16 * kRowBytes * (j >> 4)));
+    };
+    constexpr int kRing = 4;
+    u32x4 aring[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) aring[j] = a_frag(j);
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kQSteps / 2; ++ks) {
-      const bf16x8 af = as_bf16x8(*reinterpret_cast<const u32x4*>(tile + qk_off[ks & 3] + 128 * (ks >> 2)));
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const bf16x8 af = as_bf16x8(aring[ks % kRing]);
+      if (ks + kRing < kQSteps) aring[ks % kRing] = a_frag(ks + kRing);
       s = mfma_bf16(af, qf[ks], s);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first value-product fragments load while the softmax runs
+    s16x4 vring[kRing][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sx_mine[r * 64] = s[r];
-    lds_barrier();
-    // both waves of the pair form the same full score (one addition of the two halves, which is
-    // commutative, so both waves get the same bits)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] += sx_other[r * 64];
+    for (int j = 0; j < kRing; ++j) { vring[j][0] = v_frag(j, 0); vring[j][1] = v_frag(j, 1); }
 
     // online softmax over the 16 keys this lane holds (+ the other half-wave's 16)
     float mx = -INFINITY;
@@ -249,18 +269,10 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    // Lazy rescale: the reference max moves only when a logit exceeds it by more than 2^8, so
-    // probabilities stay <= 256 and the accumulator is rescaled rarely (exact either way, the
-    // final normalisation uses the same reference).
-    const bool grow = mx > m_run + kRescaleLog2;
-    if (__any(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;   // first tile: 0
-      m_run = grow ? mx : m_run;
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks / 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+    if (m_run == kNoRef && mx > -INFINITY) m_run = mx + kRefMargin;
+    if (mx > m_run + kRefLimit) {           // too far above the reference: restart with a new one
+      m_run = mx + kRefMargin;
+      lds_epoch = epoch + 1;
     }
     float psum = 0.f;
 #pragma unroll
@@ -280,39 +292,52 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
       for (int e = 0; e < 4; ++e) v[e] = pack_bf16(s[8 * k2 + 2 * e], s[8 * k2 + 2 * e + 1]);
       pf[k2] = as_bf16x8(v);
     }
-    // O^T += V^T P^T over this wave's 256 latent columns.  The A operand (latent column m, the
-    // same 8 keys) comes from two transposed reads of the row-major tile: a 16-lane group reading
-    // 8 bytes (4 columns) of 4 consecutive keys hands lane i the 4 keys of column i.
-    // consecutive MFMAs go to different accumulators (block-major inner loop)
+    // O^T += V^T P^T.  The A operand (latent column m, the same 8 keys) comes from two transposed
+    // reads of the row-major tile: a 16-lane group reading 8 bytes (4 columns) of 4 consecutive
+    // keys hands lane i the 4 keys of column i.  Same 4-deep ring as the score product;
+    // consecutive MFMAs go to different accumulators.
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks / 2; ++mb) {
-        s16x4 part[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          part[q] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-              tile + pv_off[q][mb & 1] + 128 * (mb >> 1) + 16 * kRowBytes * k2));
-        }
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mb] = mfma_bf16(vf, pf[k2], o[mb]);
-        if ((mb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < 2 * kVBlocks; ++j) {
+      const int k2 = j >> 4, mb = j & 15;
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vring[j % kRing][0], vring[j % kRing][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (j + kRing < 2 * kVBlocks) {
+        vring[j % kRing][0] = v_frag(j + kRing, 0);
+        vring[j % kRing][1] = v_frag(j + kRing, 1);
       }
+      o[mb] = mfma_bf16(vf, pf[k2], o[mb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  if (ntiles > 0) issue(0, 0);
-  if (ntiles > 1) issue(1, 1);
-  for (int it = 0; it < ntiles; it += kStages) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
-    if (it + 2 < ntiles) step(it + 2, std::integral_constant<int, 2>{});
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < ntiles_run) issue(i, i);
+    for (int it = 0; it < ntiles_run; it += kStages) {
+      step(it, std::integral_constant<int, 0>{});
+      if (it + 1 < ntiles_run) step(it + 1, std::integral_constant<int, 1>{});
+      if (it + 2 < ntiles_run) step(it + 2, std::integral_constant<int, 2>{});
+      if (it + 3 < ntiles_run) step(it + 3, std::integral_constant<int, 3>{});
+    }
+    static_assert(kStages == 4, "the main loop above is unrolled for a 4-slot ring");
+    // every wave sees the same restart request after the barrier; the gathers of this pass have
+    // all been waited for (the last step waits for vmcnt 0)
+    lds_barrier();
+    const int req = lds_epoch;
+    if (req == epoch) break;
+    epoch = req;                            // raised references stay; accumulation starts over
+    l_run = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+    lds_barrier();                          // all waves read the request before slot 0 is refilled
   }
   if (a.n_splits == 1) {
     if (hvalid) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + hf * (kDimV / 2);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV;
 #pragma unroll
-      for (int mb = 0; mb < kVBlocks / 2; ++mb)
+      for (int mb = 0; mb < kVBlocks; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = 32 * mb + 8 * j + 4 * hh;
@@ -321,20 +346,20 @@ __global__ __launch_bounds__(NG * 128) void sfa_main(SfaArgs a) {
           v.y = pack_bf16(o[mb][4 * j + 2] * inv, o[mb][4 * j + 3] * inv);
           *reinterpret_cast<uint2*>(dst + d) = v;
         }
-      if (a.lse != nullptr && hh == 0 && hf == 0)
+      if (a.lse != nullptr && hh == 0)
         a.lse[(size_t)row * a.H + head] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
     }
   } else {
     const size_t ps = (size_t)row * a.n_splits + split;
-    if (hvalid && hh == 0 && hf == 0) {
+    if (hvalid && hh == 0) {
       a.part_ml[(ps * a.H + head) * 2] = m_run;
       a.part_ml[(ps * a.H + head) * 2 + 1] = l_run;
     }
-    // partial O in the accumulator's own lane order: [half][head group][block][register][lane]
+    // partial O in the accumulator's own lane order: [head group][block][register][lane]
     if (gg >= NGT) return;
-    float* dst = a.part_o + (((ps * 2 + hf) * NGT + gg) * (kVBlocks / 2)) * 16 * 64;
+    float* dst = a.part_o + ((ps * NGT + gg) * kVBlocks) * 16 * 64;
 #pragma unroll
-    for (int mb = 0; mb < kVBlocks / 2; ++mb)
+    for (int mb = 0; mb < kVBlocks; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dst[(mb * 16 + r) * 64 + lane] = o[mb][r];
   }
@@ -380,11 +405,11 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
       a.lse[(size_t)row * a.H + head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  // this thread's 4 floats: e = index into the group's [hf][mb][r][lane] block of 16384 floats
+  // this thread's 4 floats: e = index into the group's [mb][r][lane] block of 16384 floats
   const int e = (chunk * 256 + tid) * 4;
-  const int lane0 = e & 63, r = (e >> 6) & 15, mb = (e >> 10) & 7, hf = e >> 13;
-  const size_t blk = (size_t)(hf * NG + g) * (kVBlocks / 2) * 16 * 64 + (size_t)(mb * 16 + r) * 64 + lane0;
-  const size_t per_split = (size_t)2 * NG * (kVBlocks / 2) * 16 * 64;
+  const int lane0 = e & 63, r = (e >> 6) & 15, mb = e >> 10;
+  const size_t blk = (size_t)g * kVBlocks * 16 * 64 + (size_t)(mb * 16 + r) * 64 + lane0;
+  const size_t per_split = (size_t)NG * kVBlocks * 16 * 64;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const float* src = a.part_o + (size_t)row * S * per_split + blk;
   const int nl0 = lane0 & 31, hh = lane0 >> 5;
@@ -395,7 +420,7 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
     acc.z += wgt[sp][nl0 + 2] * v.z;
     acc.w += wgt[sp][nl0 + 3] * v.w;
   }
-  const int d = 256 * hf + 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
+  const int d = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
   const float vals[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
@@ -411,7 +436,7 @@ static size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
 AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   AttnPlan p;
   p.waves = (S.heads + 31) / 32;                       // 32-head groups
-  p.groups_per_wg = p.waves >= 2 ? 2 : 1;
+  p.groups_per_wg = p.waves >= 4 ? 4 : (p.waves >= 2 ? 2 : 1);
   p.head_chunks = (p.waves + p.groups_per_wg - 1) / p.groups_per_wg;
   const int rows = L.batch * S.T;
   // splits: enough workgroups (rows x head chunks x splits) to cover the GPU's 256 compute units,
@@ -426,7 +451,7 @@ AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   size_t off = 0;
   if (p.n_splits > 1) {
     p.off_ml = off; off = align_up(off + (size_t)rows * p.n_splits * S.heads * 2 * 4, 256);
-    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kVBlocks * 16 * 64 * 4, 256);  // 2 waves x 8 blocks per group
+    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kVBlocks * 16 * 64 * 4, 256);
   }
   p.total = off;
   return p;
@@ -451,8 +476,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const dim3 grid(rows, p.n_splits, p.head_chunks);
   {
     LaunchScope ls("sfa_main", st);
-    if (p.groups_per_wg == 2) hipLaunchKernelGGL(sfa_main<2>, grid, dim3(256), 0, st, s);
-    else hipLaunchKernelGGL(sfa_main<1>, grid, dim3(128), 0, st, s);
+    if (p.groups_per_wg == 4) hipLaunchKernelGGL(sfa_main<4>, grid, dim3(256), 0, st, s);
+    else if (p.groups_per_wg == 2) hipLaunchKernelGGL(sfa_main<2>, grid, dim3(128), 0, st, s);
+    else hipLaunchKernelGGL(sfa_main<1>, grid, dim3(64), 0, st, s);
   }
   if (p.n_splits > 1) {
     LaunchScope ls("sfa_combine", st);
