@@ -42,6 +42,10 @@ __global__ __launch_bounds__(256) void li_zero_hist(uint32_t* __restrict__ hist,
     p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// max(x, 0) as one integer max on the bits: a non-negative float compares as a non-negative
+// integer, a negative one as a negative integer (avoids the NaN-quieting fmaxf expansion).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ------------------------------------------------------------------------------------------------
 struct ScoreArgs {
   const unsigned char* q;       // [B,T,HI,DI] bf16 | e4m3
@@ -202,25 +206,28 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
         for (int m = 0; m < C::MB; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+        // all B fragments of the key column are read before the first MFMA
+        frag_t bfr[C::KS];
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
-          if constexpr (FP8) {
-            const long bf = *reinterpret_cast<const long*>(
-                lds_k + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
-#pragma unroll
-            for (int m = 0; m < C::MB; ++m) acc[m] = mfma_fp8(afrag[m][kk], bf, acc[m]);
-          } else {
-            const bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          if constexpr (FP8)
+            bfr[kk] = *reinterpret_cast<const long*>(lds_k + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
+          else
+            bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
                 lds_k + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
-#pragma unroll
-            for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bf, acc[m]);
-          }
         }
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) {
+            if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+            else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+          }
         float part = 0.f;
 #pragma unroll
         for (int m = 0; m < C::MB; ++m)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], fmaxf(acc[m][r], 0.f), part);
+          for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
         part += __shfl_xor(part, 32, 64);
         if constexpr (FP8) part *= lds_ksc[kt / kPage];
         const int s = ts + kt;
@@ -375,23 +382,32 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
     }
   };
 
+  // Tile prefetch into registers.  Every call issues exactly LPT loads per thread (pages past the
+  // sequence end and tiles past the range read page 0 instead), so the compiler can wait for one
+  // tile while the next stays in flight: a load that is skipped on some path would make it wait
+  // for all of them.
   u32x4 pre0[C::LPT], pre1[C::LPT];
   int pb0 = 0, pj0 = 0, pb1 = 0, pj1 = 0;
-  auto issue = [&](int f, u32x4 (&pre)[C::LPT], int& pb, int& pj) {
-    const int b = locate(f);
-    const int j = f - lds_tstart[b];
+  int b_iss = locate(lo);             // sequence of the last tile issued (tiles go in order)
+  // A dummy call (live == false, past the end of the range) reads page 0 only and leaves the
+  // sequence cursor alone; its buffer is never committed.
+  auto issue = [&](int f, bool live, u32x4 (&pre)[C::LPT], int& pb, int& pj) {
+    int b = b_iss, j = 0;
+    if (live) {
+      while (b + 1 < a.B && lds_tstart[b + 1] <= f) ++b;
+      b_iss = b;
+      j = f - lds_tstart[b];            // 0 <= j < tiles of sequence b
+    }
     pb = b; pj = j;
-    const int nmax = lds_len[b];
+    const int nmax = live ? lds_len[b] : 0;
     const int ts = j * C::KT;
 #pragma unroll
     for (int q = 0; q < C::LPT; ++q) {
       const int i = tid + kThreads * q;
       const int key = i / C::CPK, c = i % C::CPK;
-      const int lp = ts / kPage + key / kPage;
-      if (lp * kPage < nmax) {
-        const int phys = page_of(f, b, lp);
-        pre[q] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
-      }
+      const int lp = ts / kPage + key / kPage;   // >= 0
+      const int phys = lp * kPage < nmax ? page_of(f, b, lp) : 0;
+      pre[q] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
     }
   };
   auto commit = [&](const u32x4 (&pre)[C::LPT], int buf, int b, int j) {
@@ -421,25 +437,28 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       for (int m = 0; m < C::MB; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+      // all B fragments of the key column are read before the first MFMA
+      frag_t bfr[C::KS];
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk) {
-        if constexpr (FP8) {
-          const long bf = *reinterpret_cast<const long*>(
-              lds_k[buf] + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
-#pragma unroll
-          for (int m = 0; m < C::MB; ++m) acc[m] = mfma_fp8(afrag[m][kk], bf, acc[m]);
-        } else {
-          const bf16x8 bf = as_bf16x8(*reinterpret_cast<const u32x4*>(
+        if constexpr (FP8)
+          bfr[kk] = *reinterpret_cast<const long*>(lds_k[buf] + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
+        else
+          bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
               lds_k[buf] + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
-#pragma unroll
-          for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bf, acc[m]);
-        }
       }
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+        for (int m = 0; m < C::MB; ++m) {
+          if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+          else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+        }
       float part = 0.f;
 #pragma unroll
       for (int m = 0; m < C::MB; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], fmaxf(acc[m][r], 0.f), part);
+        for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
       part += __shfl_xor(part, 32, 64);
       if constexpr (FP8) part *= lds_ksc[buf][kt / kPage];
       const int s = j * C::KT + kt;
@@ -452,8 +471,8 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   };
 
   for (int i = tid; i < TQ * kBins; i += kThreads) lds_hist[i] = 0u;
-  issue(lo, pre0, pb0, pj0);
-  if (n_items > 1) issue(lo + 1, pre1, pb1, pj1);
+  issue(lo, true, pre0, pb0, pj0);
+  issue(n_items > 1 ? lo + 1 : lo, n_items > 1, pre1, pb1, pj1);
   int b_cur = -1;
   auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, int buf) {
     commit(pre, buf, pb, pj);
@@ -463,9 +482,13 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       if (b_cur >= 0) flush(b_cur);
       load_q(b);
       b_cur = b;
+      // compiler-visible wait for q and w (vmcnt 0): without it the compiler keeps them pending
+      // on every path and waits for them inside compute, behind the tiles in flight
+      __builtin_amdgcn_s_waitcnt(0x0F70);
       lds_barrier();
     }
-    if (i + 2 < n_items) issue(lo + i + 2, pre, pb, pj);
+    const bool live = i + 2 < n_items;
+    issue(live ? lo + i + 2 : lo, live, pre, pb, pj);
     compute(buf, b, j);
   };
   for (int i = 0; i < n_items; i += 2) {

@@ -198,6 +198,29 @@ def test_attn_empty_rows_and_equal_logits():
     np.testing.assert_allclose(l[1], np.log(7.0), rtol=1e-5)
 
 
+def test_attn_logit_spread_restarts():
+    """Logits that jump far above the first tile's max inside one split (the softmax reference
+    has to move twice) still give the exact softmax."""
+    B, L, K = 64, 3000, 2048
+    c = W.make_case(W.custom("attn_spread", B, 1, (L,) * B, 8, 64, K, 32, values="sharp",
+                             sharp_c=1.0))
+    one = W.f32_to_bf16_bits(np.float32(1.0))
+    big = {1300: 8.0, 1400: 64.0, 700: 2.0}   # logits 8*576/24, 64*576/24, 2*576/24
+    for b in (0, 1):
+        c.q_attn[b, 0] = one
+        for pos, v in big.items():
+            c.kv_cache[c.block_table[b, pos // 64], pos % 64] = W.f32_to_bf16_bits(np.float32(v))
+    idx = np.broadcast_to(np.arange(K, dtype=np.int32), (B, 1, K)).copy()
+    d = Dev(c)
+    out, lse = d.attn(idx)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (1, 0), (2, 0)]
+    o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
+                                          c.spec.sm_scale, rows=rows)
+    check_attn(to_np(out)[:3], to_np(lse)[:3], o_ref[:3], l_ref[:3])
+    assert np.all(to_np(out)[:2] == 64.0)
+
+
 @pytest.mark.parametrize("B,K", [(1, 2048), (3, 1000), (300, 64)])
 def test_attn_random_index_sets_sharp(B, K):
     """Random unique index sets (several splits when B is small, none when B is large)."""
