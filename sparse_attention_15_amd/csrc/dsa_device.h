@@ -44,6 +44,15 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) 
                : "memory", "m0");
 }
 
+// Same, for 16-byte chunks of one row: lane i's 16 bytes come from sbase + voff (sbase
+// wave-uniform, held in SGPRs; voff a 32-bit per-lane byte offset).
+__device__ __forceinline__ void lds_dma16_rows(const void* sbase, uint32_t voff, const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff),
+               "s"(sbase)
+               : "memory", "m0");
+}
+
 // Waits until at most N of this wave's global loads (including direct-to-LDS loads) are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

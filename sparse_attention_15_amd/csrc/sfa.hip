@@ -16,8 +16,8 @@
 // tile with transposed LDS reads.  The accumulator O^T (512 x 32 per wave, 256 registers) lives in
 // the accumulation registers; the running max is kept in the log2 domain (exp2 with log2(e) folded
 // into the scale).  With one split the workgroup normalises and writes bf16 output and the
-// natural-log LSE; with several, each writes (m, l, O) partials and sfa_combine merges them:
-// M = max m_i, O = sum_i 2^(m_i - M) O_i / sum_i 2^(m_i - M) l_i.
+// natural-log LSE; with several, each writes (m, l, O / l) partials and sfa_combine merges them:
+// M = max m_i, w_i = 2^(m_i - M) l_i, O = sum_i w_i (O_i / l_i) / sum_i w_i.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -45,24 +45,24 @@ struct SfaArgs {
   __bf16* out;                  // [rows, H, 512]
   float* lse;                   // [rows, H] or null
   float* part_ml;               // [rows, splits, H, 2]
-  float* part_o;                // [rows, splits, head groups, 16, 16, 64]
+  uint32_t* part_o;             // [rows, splits, head groups, 16, 8, 64] bf16 pairs
   int T, H, K, max_pages, num_pages, n_splits, keys_per_split, max_seq_len;
   float scale_log2;             // sm_scale * log2(e)
 };
 
-// LDS layout of a gathered tile: 32 rows of 1152 bytes (72 chunks of 16 bytes), no padding; the
-// 16-byte chunk c of row r is stored at chunk c ^ swz(r).  swz keeps both read patterns free of
-// bank conflicts: 16 rows reading the same chunk (the score product's A operand) land on 16
-// distinct 16-byte bank slots, and the transposed 8-byte reads of the value product (8 rows x 64
-// bytes) put at most two requests on a slot.  XOR on the low three bits keeps a chunk inside its
-// aligned group of eight, so every swizzled chunk stays inside the 72-chunk row.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2); }
+// LDS layout of a gathered tile (36864 bytes) in two regions:
+//   A: the 512 value columns of each row, 1024 bytes (64 chunks of 16 bytes), row r at 1024*r;
+//   B: the 64 rope columns, 128 bytes (8 chunks), row r at kRegionB + 128*r.
+// Chunk c of row r sits at slot c ^ swa(r) in A and c ^ swb(r) in B.  A region-A row is exactly
+// one wave-wide direct-to-LDS load (64 lanes x 16 bytes), so a gather is one scalar-addressed load
+// per row.  The XORs keep the reads free of bank conflicts (16-byte slots, 16 per 256-byte bank
+// cycle): the score product's 16 lanes read one chunk of 16 consecutive rows, and swa is a
+// permutation of the row's low four bits; the value product's transposed 8-byte reads take 2
+// chunks (c, c^1) of 4 consecutive rows, and swa >> 1 differs between those rows.
+constexpr int kRegionB = 32768;
+__device__ __forceinline__ int swa(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int swb(int r) { return (r >> 1) & 7; }
 
-__device__ __forceinline__ uint16_t bf16_bits_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
 constexpr int kTileBytes = kBK * kRowBytes;          // 36864
-constexpr int kDmaPerTile = kTileBytes / 1024;       // 36 wave-wide 16-byte-per-lane loads
+constexpr int kDmaPerTile = kTileBytes / 1024;       // 36 wave-wide loads: 32 value rows + 4 rope blocks
 constexpr int kStages = 4;                           // gather ring depth (the main loop is unrolled by it)
 constexpr int kMaxSplitKeys = DSA_MAX_TOP_K;
 
@@ -112,15 +112,10 @@ void sfa_main(SfaArgs a) {
   const int head = gg * 32 + nl;
   const bool hvalid = head < a.H;
 
-  // B operand of the score product: this lane's head row of q (36 K steps of 16 columns).  Lanes
-  // of a head beyond H read head 0 and their results are never stored.  Issued first: nothing
-  // waits for these loads before the first score product.
+  // B operand of the score product: this lane's head row of q (36 K steps of 16 columns), loaded
+  // after the first gathers are in flight.  Lanes of a head beyond H read head 0 and their
+  // results are never stored.
   bf16x8 qf[kQSteps];
-  {
-    const unsigned char* src = a.q + ((size_t)row * a.H + (hvalid ? head : 0)) * kRowBytes + 16 * hh;
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * ks));
-  }
 
   // Row table for this split (one round of idx + block-table loads): lds_rows[j] = physical row
   // of selected index j, -1 if it is not a visible position; lds_valid[tile] = its 32-bit mask.
@@ -144,11 +139,6 @@ void sfa_main(SfaArgs a) {
       if (r >= 0) atomicMin(&lds_fill, j);
     }
   }
-  // The query rows and the row table have landed before the gathers start.  A compiler-visible
-  // wait (vmcnt 0), so it knows no ordinary load is outstanding inside the main loop: it does not
-  // count the direct-to-LDS loads, and would otherwise place waits for q there that also stall on
-  // the tiles in flight.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
   // Keys that are not selected are gathered from the split's first selected row (finite data, so
   // their zero probabilities never meet a NaN); a split without any selected key skips its tiles.
@@ -156,24 +146,32 @@ void sfa_main(SfaArgs a) {
   const int fill_row = fill_j < kMaxSplitKeys ? lds_rows[fill_j] : 0;
   const int ntiles_run = fill_j < kMaxSplitKeys ? ntiles : 0;
 
-  // gather tile `tile` into ring slot `buf`: this wave's loads are chunks 64*q + lane of the tile,
-  // q = wave, wave + NW, ...; slot position p holds row p / 72, chunk (p % 72) ^ swz(row).  The
-  // per-lane coordinates are recomputed on every call (a few VALU ops) instead of being held in
-  // registers across the main loop, and all row-table reads go out before the first load.  Every
+  // Gather tile `tile` into ring slot `buf`.  This wave loads the value columns of rows
+  // wave, wave + NW, ... (one load per row: the row id is wave-uniform, so the row's address is a
+  // scalar base and each lane adds its own swizzled 16-byte chunk) and the rope blocks
+  // wave, wave + NW, ... < 4 (8 rows x 8 chunks per load, lane i: row 8k + i/8, slot i%8).  Every
   // wave issues the same number of loads per tile, which the ring's counter waits rely on.
   auto issue = [&](int tile, int buf) {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    int prow[kDmaWave];
+    constexpr int kRows = kBK / NW, kRope = 4 / NW;
+    int prow[kRows];
 #pragma unroll
-    for (int u = 0; u < kDmaWave; ++u) prow[u] = lds_rows[tile * kBK + (64 * (wave + u * NW) + ln) / 72];
+    for (int u = 0; u < kRows; ++u) prow[u] = lds_rows[tile * kBK + wave + u * NW];
 #pragma unroll
-    for (int u = 0; u < kDmaWave; ++u) {
-      const int p = 64 * (wave + u * NW) + ln;
-      const int c = (p % 72) ^ swz(p / 72);
-      const int pr = prow[u] < 0 ? fill_row : prow[u];
-      const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 16 * c;
-      lds_dma16(src, lds_kv[buf] + 1024 * (wave + u * NW));
+    for (int u = 0; u < kRope; ++u) {
+      const int k = wave + u * NW;
+      const int r = 8 * k + (lane >> 3);
+      int pr = lds_rows[tile * kBK + r];
+      pr = pr < 0 ? fill_row : pr;
+      const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r));
+      lds_dma16(src, lds_kv[buf] + kRegionB + 1024 * k);
+    }
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int r = wave + u * NW;
+      int pr = __builtin_amdgcn_readfirstlane(prow[u]);
+      pr = pr < 0 ? fill_row : pr;
+      lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
+                     lds_kv[buf] + 1024 * r);
     }
   };
 
@@ -192,25 +190,24 @@ void sfa_main(SfaArgs a) {
   float m_run = kNoRef, l_run = 0.f;
   int epoch = 0;                            // restarts seen by this wave
 
-  // Per-lane LDS byte offsets.  XOR with swz() only touches the low three bits of a chunk index,
-  // so offsets repeat every 8 chunks: four bases per operand plus immediate strides cover a tile.
-  // Score A operand: row nl, chunk c = 2*ks + hh; ks = 4u + v -> base[v] + 128*u.
-  int qk_off[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) qk_off[v] = nl * kRowBytes + 16 * ((2 * v + hh) ^ swz(nl));
-  // Value A operand (transposed reads): key = 16*k2 + 8*q + kq, column = dim0 + 32*mb with
-  // mb = 2u + v; swz(key) = swz(kq) ^ 4q, so the offset is base[q][v] + 128*u + 16*kRowBytes*k2.
+  // Per-lane LDS byte offsets.  Score A operand: row nl, chunk c = 2*ks + hh.  For ks < 32
+  // (region A) write ks = 8g + v: the slot is 16g + ((2v + hh) ^ swa), i.e. byte
+  // 256g + 16*((hh ^ swa) & 1) + 32*(v ^ (swa >> 1)); the last term only uses bits 5-7, so the
+  // address is qa ^ 32v (+ 256g).  Region B likewise: qb ^ 32v' for ks = 32 + v'.
+  const int sa_nl = swa(nl), sb_nl = swb(nl);
+  const int qa = 1024 * nl + 16 * ((hh ^ sa_nl) & 1) + 32 * (sa_nl >> 1);
+  const int qb = kRegionB + 128 * nl + 16 * ((hh ^ sb_nl) & 1) + 32 * (sb_nl >> 1);
+  // Value A operand (transposed 8-byte reads): key = 16*k2 + 8*q + kq, columns 8*cl + 4*(lane&1)
+  // + 32*mb, cl = chunk within the 32-column block.  With mb = 4g + m' the byte offset is
+  // 16384*k2 + 256g + (pv[q] ^ 64m'): swa(key) only sees key bits 0-3 = 8q + kq.
   const int kq = 4 * hh + ((lane & 15) >> 2);
-  const int dim0 = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int pv_off[2][2];
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int pv[2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) {
-      const int key = 8 * q + kq;
-      const int c = (dim0 >> 3) + 4 * v;    // < 8
-      pv_off[q][v] = key * kRowBytes + 16 * (c ^ swz(key)) + 2 * (dim0 & 7);
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int sa = swa(8 * q + kq);
+    pv[q] = 1024 * (8 * q + kq) + 16 * (cl ^ (sa & 3)) + 64 * (sa >> 2) + 8 * (lane & 1);
+  }
 
   // One tile of the main loop.  The ring slot is a compile-time constant (the loop is unrolled by
   // the ring depth), so every LDS address below is a per-lane base plus an immediate offset.
@@ -225,12 +222,18 @@ void sfa_main(SfaArgs a) {
     // S^T = X q^T: rows = the tile's 32 keys, columns = this wave's 32 heads.  The A fragments
     // stream through a 4-deep register ring: the read for step ks + 4 is issued right behind the
     // MFMA of step ks, so LDS latency hides under the MFMAs in between.
+    // The XOR-ed offsets are formed per read (one VALU op each) from bases the compiler may not
+    // hoist: precomputing all 36 + 64 of them would hold that many registers across the loop.
+    int qa_t = qa, qb_t = qb, pv0 = pv[0], pv1 = pv[1];
+    asm volatile("" : "+v"(qa_t), "+v"(qb_t), "+v"(pv0), "+v"(pv1));
     auto a_frag = [&](int ks) {
-      return *reinterpret_cast<const u32x4*>(tile + qk_off[ks & 3] + 128 * (ks >> 2));
+      const int off = ks < 32 ? (qa_t ^ (32 * (ks & 7))) + 256 * (ks >> 3) : qb_t ^ (32 * (ks - 32));
+      return *reinterpret_cast<const u32x4*>(tile + off);
     };
     auto v_frag = [&](int j, int q) {     // j = 16*k2 + mb
+      const int mb = j & 15;
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-          tile + pv_off[q][j & 1] + 128 * ((j & 15) >> 1) + 16 * kRowBytes * (j >> 4)));
+          tile + ((q ? pv1 : pv0) ^ (64 * (mb & 3))) + 256 * (mb >> 2) + 16384 * (j >> 4)));
     };
     constexpr int kRing = 4;
     u32x4 aring[kRing];
@@ -308,10 +311,20 @@ void sfa_main(SfaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (;;) {
+  // First gathers, then q: the two latencies overlap.  The compiler-visible wait (vmcnt 0) lets
+  // it know no ordinary load is outstanding inside the main loop (it does not count the
+  // direct-to-LDS loads and would otherwise place waits for q there that also stall on the tiles
+  // in flight); it also covers the first tiles.
 #pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-      if (i < ntiles_run) issue(i, i);
+  for (int i = 0; i < kStages - 1; ++i)
+    if (i < ntiles_run) issue(i, i);
+  {
+    const unsigned char* src = a.q + ((size_t)row * a.H + (hvalid ? head : 0)) * kRowBytes + 16 * hh;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * ks));
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (;;) {
     for (int it = 0; it < ntiles_run; it += kStages) {
       step(it, std::integral_constant<int, 0>{});
       if (it + 1 < ntiles_run) step(it + 1, std::integral_constant<int, 1>{});
@@ -331,6 +344,9 @@ void sfa_main(SfaArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
     lds_barrier();                          // all waves read the request before slot 0 is refilled
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < ntiles_run) issue(i, i);
   }
   if (a.n_splits == 1) {
     if (hvalid) {
@@ -355,33 +371,39 @@ void sfa_main(SfaArgs a) {
       a.part_ml[(ps * a.H + head) * 2] = m_run;
       a.part_ml[(ps * a.H + head) * 2 + 1] = l_run;
     }
-    // partial O in the accumulator's own lane order: [head group][block][register][lane]
+    // Normalised partial O / l as bf16 pairs (registers 2k, 2k+1) in the accumulator's own lane
+    // order, [head group][block][register pair][lane]: half the bytes of fp32 partials, whose
+    // rounding (2^-9 of the split's own output range) stays far inside the output tolerance.
     if (gg >= NGT) return;
-    float* dst = a.part_o + ((ps * NGT + gg) * kVBlocks) * 16 * 64;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint32_t* dst = a.part_o + ((ps * NGT + gg) * kVBlocks) * 8 * 64;
 #pragma unroll
     for (int mb = 0; mb < kVBlocks; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(mb * 16 + r) * 64 + lane] = o[mb][r];
+      for (int k = 0; k < 8; ++k) dst[(mb * 8 + k) * 64 + lane] = pack_bf16(o[mb][2 * k] * inv, o[mb][2 * k + 1] * inv);
   }
 }
 
-// Merges the split partials.  Grid (query row, 32-head group, chunk): each of the 16 chunks of a
-// (row, group) handles 1024 of its 16384 partial-O floats, 4 consecutive accumulator lanes per
-// thread; every workgroup first rebuilds the per-head merge weights of its group.
-constexpr int kCombineChunks = 16;
+// Merges the split partials.  Grid (query row, 32-head group, chunk): each of the 8 chunks of a
+// (row, group) handles 1024 of its 8192 bf16 pairs, 4 consecutive accumulator lanes (heads) per
+// thread; every workgroup first rebuilds the per-head merge weights of its group.  With
+// normalised partials O_i / l_i the weight of split i is 2^(m_i - M) l_i / L.
+constexpr int kCombineChunks = 8;
 
 struct CombineArgs {
   const float* part_ml;
-  const float* part_o;
+  const uint32_t* part_o;
   __bf16* out;
   float* lse;
   int H, n_splits, waves;
 };
 
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
 __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
   constexpr int kMaxSplits = 64;
   __shared__ float wgt[kMaxSplits][32];
-  __shared__ float inv_l[32];
   const int tid = threadIdx.x;
   const int row = blockIdx.x, g = blockIdx.y, chunk = blockIdx.z;
   const int S = a.n_splits, NG = a.waves;
@@ -395,38 +417,43 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
       float w = 0.f;
       if (head < a.H && M != -INFINITY) {
         const size_t e = (((size_t)row * S + i) * a.H + head) * 2;
-        w = exp2f(a.part_ml[e] - M);
-        L += w * a.part_ml[e + 1];
+        w = exp2f(a.part_ml[e] - M) * a.part_ml[e + 1];
+        L += w;
       }
       wgt[i][tid] = w;
     }
-    inv_l[tid] = L > 0.f ? 1.f / L : 0.f;
+    const float inv_L = L > 0.f ? 1.f / L : 0.f;
+    for (int i = 0; i < S; ++i) wgt[i][tid] *= inv_L;
     if (a.lse != nullptr && head < a.H && chunk == 0)
       a.lse[(size_t)row * a.H + head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  // this thread's 4 floats: e = index into the group's [mb][r][lane] block of 16384 floats
-  const int e = (chunk * 256 + tid) * 4;
-  const int lane0 = e & 63, r = (e >> 6) & 15, mb = e >> 10;
-  const size_t blk = (size_t)g * kVBlocks * 16 * 64 + (size_t)(mb * 16 + r) * 64 + lane0;
-  const size_t per_split = (size_t)NG * kVBlocks * 16 * 64;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* src = a.part_o + (size_t)row * S * per_split + blk;
+  // this thread's 4 pairs: u = index into the group's [mb][pair][lane] block of 8192 pairs
+  const int u = (chunk * 256 + tid) * 4;
+  const int lane0 = u & 63, rp = (u >> 6) & 7, mb = u >> 9;
+  const size_t blk = (size_t)g * kVBlocks * 8 * 64 + (size_t)(mb * 8 + rp) * 64 + lane0;
+  const size_t per_split = (size_t)NG * kVBlocks * 8 * 64;
+  float acc[4][2] = {};
+  const uint32_t* src = a.part_o + (size_t)row * S * per_split + blk;
   const int nl0 = lane0 & 31, hh = lane0 >> 5;
   for (int sp = 0; sp < S; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(src + sp * per_split);
-    acc.x += wgt[sp][nl0] * v.x;
-    acc.y += wgt[sp][nl0 + 1] * v.y;
-    acc.z += wgt[sp][nl0 + 2] * v.z;
-    acc.w += wgt[sp][nl0 + 3] * v.w;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + sp * per_split);
+    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float wq = wgt[sp][nl0 + q];
+      acc[q][0] = fmaf(wq, bf16_lo(vv[q]), acc[q][0]);
+      acc[q][1] = fmaf(wq, bf16_hi(vv[q]), acc[q][1]);
+    }
   }
-  const int d = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-  uint16_t* out = reinterpret_cast<uint16_t*>(a.out);
-  const float vals[4] = {acc.x, acc.y, acc.z, acc.w};
+  // registers 2rp, 2rp + 1 are columns d, d + 1
+  const int d = 32 * mb + 8 * (rp >> 1) + 4 * hh + 2 * (rp & 1);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int head = g * 32 + nl0 + q;
-    if (head < a.H) out[((size_t)row * a.H + head) * kDimV + d] = bf16_bits_rne(vals[q] * inv_l[nl0 + q]);
+    if (head < a.H)
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + d) =
+          pack_bf16(acc[q][0], acc[q][1]);
   }
 }
 
@@ -451,7 +478,7 @@ AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   size_t off = 0;
   if (p.n_splits > 1) {
     p.off_ml = off; off = align_up(off + (size_t)rows * p.n_splits * S.heads * 2 * 4, 256);
-    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kVBlocks * 16 * 64 * 4, 256);
+    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kVBlocks * 8 * 64 * 4, 256);
   }
   p.total = off;
   return p;
@@ -468,7 +495,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   s.lse = a.lse;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   s.part_ml = p.n_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
-  s.part_o = p.n_splits > 1 ? reinterpret_cast<float*>(ws + p.off_part) : nullptr;
+  s.part_o = p.n_splits > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_part) : nullptr;
   s.T = a.T; s.H = a.heads; s.K = a.top_k; s.max_pages = a.max_pages; s.num_pages = a.num_pages;
   s.n_splits = p.n_splits; s.keys_per_split = p.keys_per_split; s.max_seq_len = a.max_seq_len;
   s.scale_log2 = a.sm_scale * kLog2e;
