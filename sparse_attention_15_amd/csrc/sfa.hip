@@ -384,11 +384,12 @@ void sfa_main(SfaArgs a) {
   }
 }
 
-// Merges the split partials.  Grid (query row, 32-head group, chunk): each of the 8 chunks of a
-// (row, group) handles 1024 of its 8192 bf16 pairs, 4 consecutive accumulator lanes (heads) per
-// thread; every workgroup first rebuilds the per-head merge weights of its group.  With
-// normalised partials O_i / l_i the weight of split i is 2^(m_i - M) l_i / L.
-constexpr int kCombineChunks = 8;
+// Merges the split partials.  Grid (query row, 32-head group, chunk): the 8*SG chunks of a
+// (row, group) share its 8192 bf16 pairs, 4 consecutive accumulator lanes (heads) per thread;
+// with SG > 1 the workgroup's SG thread groups take every SG-th split and are summed in LDS at
+// the end (more workgroups in flight when there are many splits).  Every workgroup first rebuilds
+// the per-head merge weights of its group.  With normalised partials O_i / l_i the weight of
+// split i is 2^(m_i - M) l_i / L.
 
 struct CombineArgs {
   const float* part_ml;
@@ -401,26 +402,35 @@ struct CombineArgs {
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+template <int SG>
 __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
   constexpr int kMaxSplits = 64;
   __shared__ float wgt[kMaxSplits][32];
+  __shared__ float sm[kMaxSplits][32];
   const int tid = threadIdx.x;
   const int row = blockIdx.x, g = blockIdx.y, chunk = blockIdx.z;
   const int S = a.n_splits, NG = a.waves;
+  // (m_i, l_i) of every split and head of the group: all loads in one round
+  for (int i = tid >> 5; i < S; i += 8) {
+    const int head = g * 32 + (tid & 31);
+    float m = -INFINITY, l = 0.f;
+    if (head < a.H) {
+      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((size_t)row * S + i) * a.H + head) * 2);
+      m = ml.x; l = ml.y;
+    }
+    sm[i][tid & 31] = m;
+    wgt[i][tid & 31] = l;
+  }
+  __syncthreads();
   if (tid < 32) {
     const int head = g * 32 + tid;
     float M = -INFINITY;
-    if (head < a.H)
-      for (int i = 0; i < S; ++i) M = fmaxf(M, a.part_ml[(((size_t)row * S + i) * a.H + head) * 2]);
+    for (int i = 0; i < S; ++i) M = fmaxf(M, sm[i][tid]);
     float L = 0.f;
     for (int i = 0; i < S; ++i) {
-      float w = 0.f;
-      if (head < a.H && M != -INFINITY) {
-        const size_t e = (((size_t)row * S + i) * a.H + head) * 2;
-        w = exp2f(a.part_ml[e] - M) * a.part_ml[e + 1];
-        L += w;
-      }
+      const float w = M != -INFINITY ? exp2f(sm[i][tid] - M) * wgt[i][tid] : 0.f;
       wgt[i][tid] = w;
+      L += w;
     }
     const float inv_L = L > 0.f ? 1.f / L : 0.f;
     for (int i = 0; i < S; ++i) wgt[i][tid] *= inv_L;
@@ -429,14 +439,17 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
   }
   __syncthreads();
   // this thread's 4 pairs: u = index into the group's [mb][pair][lane] block of 8192 pairs
-  const int u = (chunk * 256 + tid) * 4;
+  constexpr int TG = 256 / SG;              // threads per split group
+  const int sg = tid / TG, t64 = tid % TG;
+  const int u = (chunk * TG + t64) * 4;
   const int lane0 = u & 63, rp = (u >> 6) & 7, mb = u >> 9;
   const size_t blk = (size_t)g * kVBlocks * 8 * 64 + (size_t)(mb * 8 + rp) * 64 + lane0;
   const size_t per_split = (size_t)NG * kVBlocks * 8 * 64;
   float acc[4][2] = {};
   const uint32_t* src = a.part_o + (size_t)row * S * per_split + blk;
   const int nl0 = lane0 & 31, hh = lane0 >> 5;
-  for (int sp = 0; sp < S; ++sp) {
+#pragma unroll 4
+  for (int sp = sg; sp < S; sp += SG) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + sp * per_split);
     const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -445,6 +458,19 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
       acc[q][0] = fmaf(wq, bf16_lo(vv[q]), acc[q][0]);
       acc[q][1] = fmaf(wq, bf16_hi(vv[q]), acc[q][1]);
     }
+  }
+  if constexpr (SG > 1) {
+    __shared__ float red[SG - 1][TG][8];
+    if (sg > 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { red[sg - 1][t64][2 * q] = acc[q][0]; red[sg - 1][t64][2 * q + 1] = acc[q][1]; }
+    }
+    __syncthreads();
+    if (sg != 0) return;
+#pragma unroll
+    for (int k = 0; k < SG - 1; ++k)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { acc[q][0] += red[k][t64][2 * q]; acc[q][1] += red[k][t64][2 * q + 1]; }
   }
   // registers 2rp, 2rp + 1 are columns d, d + 1
   const int d = 32 * mb + 8 * (rp >> 1) + 4 * hh + 2 * (rp & 1);
@@ -512,7 +538,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
     CombineArgs c;
     c.part_ml = s.part_ml; c.part_o = s.part_o; c.out = s.out; c.lse = a.lse;
     c.H = a.heads; c.n_splits = p.n_splits; c.waves = p.waves;
-    hipLaunchKernelGGL(sfa_combine, dim3(rows, p.waves, kCombineChunks), dim3(256), 0, st, c);
+    if (p.n_splits > 16) hipLaunchKernelGGL(sfa_combine<4>, dim3(rows, p.waves, 32), dim3(256), 0, st, c);
+    else if (p.n_splits > 8) hipLaunchKernelGGL(sfa_combine<2>, dim3(rows, p.waves, 16), dim3(256), 0, st, c);
+    else hipLaunchKernelGGL(sfa_combine<1>, dim3(rows, p.waves, 8), dim3(256), 0, st, c);
   }
   return hipGetLastError();
 }
