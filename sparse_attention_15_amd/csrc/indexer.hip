@@ -500,6 +500,204 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
+// Decode, one query row per sequence.  The persistent grid walks the same flattened
+// (sequence, 128-key tile) list as li_score_persist, but each wave streams only its own 32-key
+// block of every tile, through a private two-slot LDS ring filled with direct-to-LDS loads (the
+// block lies in one page, so its address is a scalar base plus a per-lane offset).  Nothing in
+// the main loop waits for another wave: the waves meet only when the sequence changes, to publish
+// the shared row histogram and load the next query.
+template <int HI, int DI, bool FP8>
+__global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
+  using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles, 4 waves x 32 keys
+  typedef typename AFrag<FP8>::T frag_t;
+  constexpr int BLK = 32 * C::ROWB;                // one wave's block (bytes)
+  constexpr int NLD = BLK / 1024;                  // wave-wide loads per block
+  constexpr int KPL = 1024 / C::ROWB;              // keys per load
+  static_assert(NLD >= 1 && KPL * C::CPK == 64, "block shape");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][2][BLK];
+  __shared__ uint32_t lds_hist[kBins];
+  __shared__ int lds_tstart[kMaxSeqPersist + 1];
+  __shared__ int lds_len[kMaxSeqPersist];
+  __shared__ int lds_page[kMaxPagesPersist];
+  __shared__ uint32_t sh[8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 31, hh = lane >> 5;
+  const int cap = a.max_seq_len;
+
+  int carry = 0;
+  for (int base = 0; base < a.B; base += kThreads) {
+    const int b = base + tid;
+    int v = 0;
+    if (b < a.B) {
+      const int nmax = row_visible(a.seq_lens, b, 1, 0, cap);
+      lds_len[b] = nmax;
+      v = nmax > a.K ? (nmax + C::KT - 1) / C::KT : 0;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<kThreads>((uint32_t)v, sh, tot);
+    if (b < a.B) lds_tstart[b] = carry + (int)ex;
+    carry += (int)tot;
+  }
+  if (tid == 0) lds_tstart[a.B] = carry;
+  for (int i = tid; i < kBins; i += kThreads) lds_hist[i] = 0u;
+  __syncthreads();
+  const int total = carry;
+  const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
+  const int hi = (int)((long long)(blockIdx.x + 1) * total / gridDim.x);
+  const int n_items = hi - lo;
+  if (n_items <= 0) return;
+
+  auto locate = [&](int f) -> int {
+    int l = 0, h = a.B;
+    while (h - l > 1) {
+      const int m = (l + h) >> 1;
+      if (lds_tstart[m] <= f) l = m; else h = m;
+    }
+    return l;
+  };
+  constexpr int PPT = C::KT / kPage;
+  const bool page_cached = n_items * PPT <= kMaxPagesPersist;
+  if (page_cached) {
+    for (int i = tid; i < n_items * PPT; i += kThreads) {
+      const int f = lo + i / PPT;
+      const int b = locate(f);
+      const int lp = (f - lds_tstart[b]) * PPT + i % PPT;
+      lds_page[i] = lp * kPage < lds_len[b]
+          ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : 0;
+    }
+  }
+  __syncthreads();
+
+  frag_t afrag[C::MB][C::KS];
+  float wreg[C::MB][16];
+  auto load_q = [&](int b) {
+#pragma unroll
+    for (int m = 0; m < C::MB; ++m) {
+      const int head = 32 * m + nl;
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk) {
+        if (head < HI) {
+          const unsigned char* src = a.q + (((size_t)b * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
+          if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
+          else afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+        } else {
+          if constexpr (FP8) afrag[m][kk] = 0;
+          else afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int hd = 32 * m + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float wv = 0.f;
+        if (hd < HI) {
+          wv = a.w[(size_t)b * HI + hd];
+          if constexpr (FP8) wv *= a.q_scale[(size_t)b * HI + hd];
+        }
+        wreg[m][r] = wv;
+      }
+    }
+  };
+  auto flush = [&](int b) {
+    for (int i = tid; i < kBins; i += kThreads) {
+      const uint32_t v = lds_hist[i];
+      if (v != 0u) atomicAdd(&a.hist[(size_t)b * kBins + i], v);
+      lds_hist[i] = 0u;
+    }
+  };
+
+  // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i, into ring slot i & 1.
+  // Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key % CPK), so the slot holds
+  // key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block past the sequence end
+  // (or past the range) reads page 0; its keys are never stored.
+  int b_iss = locate(lo);
+  int pb[2] = {0, 0}, pj[2] = {0, 0};
+  float pks[2] = {1.f, 1.f};
+  auto issue = [&](int i, int slot) {
+    const int f = lo + i;
+    int b = b_iss;
+    while (b + 1 < a.B && lds_tstart[b + 1] <= f) ++b;
+    b_iss = b;
+    const int j = f - lds_tstart[b];
+    pb[slot] = b; pj[slot] = j;
+    const int key0 = j * C::KT + 32 * wave;
+    const int lp = key0 / kPage;
+    int phys = 0;
+    if (lp * kPage < lds_len[b])
+      phys = page_cached ? lds_page[(f - lo) * PPT + (lp % PPT)]
+                         : clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages);
+    phys = __builtin_amdgcn_readfirstlane(phys);
+    if constexpr (FP8) pks[slot] = lp * kPage < lds_len[b] ? a.k_scale[phys] : 0.f;
+    const unsigned char* base = a.kc + ((size_t)phys * kPage + (key0 % kPage)) * C::ROWB;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int key = KPL * u + lane / C::CPK;
+      const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
+      lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), lds_k[wave][slot] + 1024 * u);
+    }
+  };
+
+  int b_cur = -1;
+  issue(0, 0);
+  if (n_items > 1) issue(1, 1);
+  for (int i = 0; i < n_items; ++i) {
+    const int slot = i & 1;
+    if (i + 1 < n_items) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+    const int b = pb[slot], j = pj[slot];
+    if (b != b_cur) {                 // new sequence: publish the histogram, load the query
+      __syncthreads();
+      if (b_cur >= 0) flush(b_cur);
+      load_q(b);
+      // compiler-visible wait (vmcnt 0) for q and w, so no wait for them lands in the main loop
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      b_cur = b;
+    }
+    const int n_me = lds_len[b];
+    const float kscale = pks[slot];   // read before issue() below refills this slot's record
+    const unsigned char* blk = lds_k[wave][slot];
+    frag_t bfr[C::KS];
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk) {
+      if constexpr (FP8)
+        bfr[kk] = *reinterpret_cast<const long*>(blk + nl * C::ROWB + 16 * (kk ^ (nl & (C::CPK - 1))) + 8 * hh);
+      else
+        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blk + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
+    }
+    f32x16 acc[C::MB];
+#pragma unroll
+    for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+      for (int m = 0; m < C::MB; ++m) {
+        if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+        else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+      }
+    // the slot's reads are complete (the MFMAs consumed them): refill it
+    if (i + 2 < n_items) issue(i + 2, slot);
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
+    part += __shfl_xor(part, 32, 64);
+    if constexpr (FP8) part *= kscale;
+    const int s = j * C::KT + 32 * wave + nl;
+    if (hh == 0 && s < n_me) {
+      const uint32_t key = float_key(part);
+      a.keys[(size_t)b * a.row_stride + s] = key;
+      atomicAdd(&lds_hist[key >> 21], 1u);
+    }
+  }
+  __syncthreads();
+  flush(b_cur);
+}
+
+// ------------------------------------------------------------------------------------------------
 // Top-K selection.  Workgroups of 1024 threads; a row of n keys is cut into segments of
 // seg_len(n) keys, one workgroup each.
 struct SelectArgs {
@@ -896,7 +1094,7 @@ bool indexer_supported(int heads, int dim) {
 template <int HI, int DI, bool FP8>
 static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, hipStream_t st) {
   if (persist) {
-    if (tq == 1) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 1>), dim3(grid), dim3(kThreads), 0, st, s);
+    if (tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, FP8>), dim3(grid), dim3(kThreads), 0, st, s);
     else if (tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
     else hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 4>), dim3(grid), dim3(kThreads), 0, st, s);
     return;
