@@ -506,6 +506,8 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 // block lies in one page, so its address is a scalar base plus a per-lane offset).  Nothing in
 // the main loop waits for another wave: the waves meet only when the sequence changes, to publish
 // the shared row histogram and load the next query.
+constexpr int kDecodeMaxItems = 256;   // tiles per decode workgroup (the grid is sized for it)
+
 template <int HI, int DI, bool FP8>
 __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles, 4 waves x 32 keys
@@ -513,13 +515,17 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   constexpr int BLK = 32 * C::ROWB;                // one wave's block (bytes)
   constexpr int NLD = BLK / 1024;                  // wave-wide loads per block
   constexpr int KPL = 1024 / C::ROWB;              // keys per load
-  static_assert(NLD >= 1 && KPL * C::CPK == 64, "block shape");
+  static_assert(NLD >= 1 && KPL * C::CPK == 64 && C::KT / kPage == 2, "block shape");
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][2][BLK];
   __shared__ uint32_t lds_hist[kBins];
-  __shared__ int lds_tstart[kMaxSeqPersist + 1];
-  __shared__ int lds_len[kMaxSeqPersist];
-  __shared__ int lds_page[kMaxPagesPersist];
+  // per tile of this workgroup: sequence | tile index << 9, the physical pages of its two halves
+  // (-1 past the sequence end), and the sequence's visible length
+  __shared__ int4 lds_rec[kDecodeMaxItems];
   __shared__ uint32_t sh[8];
+  // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
+  static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
+  int* const lds_tstart = reinterpret_cast<int*>(&lds_k[0][0][0]);
+  int* const lds_len = lds_tstart + kMaxSeqPersist + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -546,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   const int total = carry;
   const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
   const int hi = (int)((long long)(blockIdx.x + 1) * total / gridDim.x);
-  const int n_items = hi - lo;
+  const int n_items = min(hi - lo, kDecodeMaxItems);   // the grid keeps hi - lo within the table
   if (n_items <= 0) return;
 
   auto locate = [&](int f) -> int {
@@ -557,18 +563,6 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     }
     return l;
   };
-  constexpr int PPT = C::KT / kPage;
-  const bool page_cached = n_items * PPT <= kMaxPagesPersist;
-  if (page_cached) {
-    for (int i = tid; i < n_items * PPT; i += kThreads) {
-      const int f = lo + i / PPT;
-      const int b = locate(f);
-      const int lp = (f - lds_tstart[b]) * PPT + i % PPT;
-      lds_page[i] = lp * kPage < lds_len[b]
-          ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : 0;
-    }
-  }
-  __syncthreads();
 
   frag_t afrag[C::MB][C::KS];
   float wreg[C::MB][16];
@@ -607,29 +601,35 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     }
   };
 
-  // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i, into ring slot i & 1.
-  // Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key % CPK), so the slot holds
-  // key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block past the sequence end
-  // (or past the range) reads page 0; its keys are never stored.
-  int b_iss = locate(lo);
-  int pb[2] = {0, 0}, pj[2] = {0, 0};
+  // the first sequence's query loads while the tile records are built
+  int b_cur = locate(lo);
+  load_q(b_cur);
+  for (int i = tid; i < n_items; i += kThreads) {
+    const int f = lo + i;
+    const int b = locate(f);
+    const int j = f - lds_tstart[b];
+    const int n = lds_len[b];
+    int pg[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lp = 2 * j + h;
+      pg[h] = lp * kPage < n ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : -1;
+    }
+    lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
+  }
+  __syncthreads();
+
+  // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i (page half wave / 2), into
+  // ring slot i & 1.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key % CPK),
+  // so the slot holds key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block past
+  // the sequence end reads page 0; its keys are never stored.
   float pks[2] = {1.f, 1.f};
   auto issue = [&](int i, int slot) {
-    const int f = lo + i;
-    int b = b_iss;
-    while (b + 1 < a.B && lds_tstart[b + 1] <= f) ++b;
-    b_iss = b;
-    const int j = f - lds_tstart[b];
-    pb[slot] = b; pj[slot] = j;
-    const int key0 = j * C::KT + 32 * wave;
-    const int lp = key0 / kPage;
-    int phys = 0;
-    if (lp * kPage < lds_len[b])
-      phys = page_cached ? lds_page[(f - lo) * PPT + (lp % PPT)]
-                         : clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages);
-    phys = __builtin_amdgcn_readfirstlane(phys);
-    if constexpr (FP8) pks[slot] = lp * kPage < lds_len[b] ? a.k_scale[phys] : 0.f;
-    const unsigned char* base = a.kc + ((size_t)phys * kPage + (key0 % kPage)) * C::ROWB;
+    const int4 r = lds_rec[i];
+    const int pg = __builtin_amdgcn_readfirstlane(wave < 2 ? r.y : r.z);
+    const int phys = pg < 0 ? 0 : pg;
+    if constexpr (FP8) pks[slot] = pg < 0 ? 0.f : a.k_scale[phys];
+    const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (wave & 1)) * C::ROWB;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int key = KPL * u + lane / C::CPK;
@@ -637,24 +637,27 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), lds_k[wave][slot] + 1024 * u);
     }
   };
-
-  int b_cur = -1;
   issue(0, 0);
   if (n_items > 1) issue(1, 1);
+  // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table loads, so no wait
+  // for them lands in the main loop (it also covers the first two blocks)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
   for (int i = 0; i < n_items; ++i) {
     const int slot = i & 1;
     if (i + 1 < n_items) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
-    const int b = pb[slot], j = pj[slot];
+    const int4 rec = lds_rec[i];
+    const int b = __builtin_amdgcn_readfirstlane(rec.x & 511);
+    const int j = __builtin_amdgcn_readfirstlane(rec.x >> 9);
+    const int n_me = __builtin_amdgcn_readfirstlane(rec.w);
     if (b != b_cur) {                 // new sequence: publish the histogram, load the query
       __syncthreads();
-      if (b_cur >= 0) flush(b_cur);
+      flush(b_cur);
       load_q(b);
-      // compiler-visible wait (vmcnt 0) for q and w, so no wait for them lands in the main loop
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       b_cur = b;
     }
-    const int n_me = lds_len[b];
     const float kscale = pks[slot];   // read before issue() below refills this slot's record
     const unsigned char* blk = lds_k[wave][slot];
     frag_t bfr[C::KS];
@@ -1152,6 +1155,8 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
     const int kt = p.tq == 1 ? 128 : 64;
     const long long max_tiles = (long long)a.B * ((a.max_seq_len + kt - 1) / kt);
     grid = (int)std::max<long long>(1, std::min<long long>(2LL * device_cus(), (max_tiles + 1) / 2));
+    // the decode kernel's per-workgroup tile table holds kDecodeMaxItems tiles
+    if (p.tq == 1) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
   }
   if (grid > 0) {
     LaunchScope ls("li_score", st);
