@@ -45,11 +45,15 @@ __device__ __forceinline__ void lds_dma16(const void* src, const void* lds_dst) 
 }
 
 // Same, for 16-byte chunks of one row: lane i's 16 bytes come from sbase + voff (sbase
-// wave-uniform, held in SGPRs; voff a 32-bit per-lane byte offset).
+// wave-uniform, made scalar here; voff a 32-bit per-lane byte offset).
 __device__ __forceinline__ void lds_dma16_rows(const void* sbase, uint32_t voff, const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  const uint64_t sb = reinterpret_cast<uintptr_t>(sbase);
+  // readfirstlane returns a signed int: widen each half through uint32_t (no sign extension)
+  const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sb >> 32)) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(base), "v"(voff),
-               "s"(sbase)
+               "s"(sbu)
                : "memory", "m0");
 }
 

@@ -112,67 +112,93 @@ void sfa_main(SfaArgs a) {
   const int head = gg * 32 + nl;
   const bool hvalid = head < a.H;
 
-  // B operand of the score product: this lane's head row of q (36 K steps of 16 columns), loaded
-  // after the first gathers are in flight.  Lanes of a head beyond H read head 0 and their
-  // results are never stored.
-  bf16x8 qf[kQSteps];
-
   // Row table for this split (one round of idx + block-table loads): lds_rows[j] = physical row
   // of selected index j, -1 if it is not a visible position; lds_valid[tile] = its 32-bit mask.
   __shared__ int lds_fill;                  // first j with a visible position
   __shared__ uint32_t lds_valid[kMaxSplitKeys / kBK];
   __shared__ int lds_epoch;                 // restarts requested by any wave (see below)
   if (tid == 0) { lds_fill = kMaxSplitKeys; lds_epoch = 0; }
-  lds_barrier();
+  const int32_t* idx = a.idx + (size_t)row * a.K + k_begin;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  // The first round of index loads goes out first: the index -> page-table chain then overlaps
+  // the q loads below.
+  const int s_first = tid < nkeys ? idx[tid] : -1;
+
+  // B operand of the score product: this lane's head row of q (36 K steps of 16 columns).  The
+  // workgroup's q rows (NW * 32 heads x 1152 bytes = NW ring slots, free until the first gathers)
+  // are first copied into LDS with direct-to-LDS loads that each read eight whole 128-byte lines;
+  // read straight into the MFMA layout, every load instruction would touch 32 rows, a quarter of
+  // a line each.  16-byte chunk c of head h sits at slot 72h + (c ^ ((h >> 1) & 7)): the XOR stays
+  // inside a 128-byte line and makes the fragment reads (16 lanes = 16 heads, one chunk) free of
+  // bank conflicts.  Heads beyond H copy head 0; their results are never stored.
+  bf16x8 qf[kQSteps];
+  unsigned char* const q_img = &lds_kv[0][0];
   {
-    const int32_t* idx = a.idx + (size_t)row * a.K + k_begin;
-    const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
-    for (int j = tid; j < ntiles * kBK; j += NT) {   // NT is a multiple of 64: whole waves
-      int r = -1;
-      if (j < nkeys) {
-        const int s = idx[j];
-        if (s >= 0 && s < n) r = clamp_page(bt[s / kPage], a.num_pages) * kPage + (s % kPage);
-      }
-      lds_rows[j] = r;
-      const uint64_t bal = __ballot(r >= 0);
-      if ((lane & 31) == 0) lds_valid[j >> 5] = (uint32_t)(bal >> (lane & 32));
-      if (r >= 0) atomicMin(&lds_fill, j);
+    const unsigned char* qrow = a.q + (size_t)row * a.H * kRowBytes;
+    const int head0 = blockIdx.z * NW * 32;
+#pragma unroll 4
+    for (int u = 0; u < kQSteps; ++u) {
+      const int i = wave * kQSteps + u;        // this load fills q image bytes 1024*i ..
+      const int sl = 64 * i + lane;
+      const int hl = sl / 72, cp = sl % 72;
+      const int hq = head0 + hl < a.H ? head0 + hl : 0;
+      lds_dma16(qrow + (size_t)hq * kRowBytes + 16 * (cp ^ ((hl >> 1) & 7)), q_img + 1024 * i);
     }
   }
+  lds_barrier();
+  for (int j = tid; j < ntiles * kBK; j += NT) {   // NT is a multiple of 64: whole waves
+    const int s = j == tid ? s_first : (j < nkeys ? idx[j] : -1);
+    const int r = s >= 0 && s < n ? clamp_page(bt[s / kPage], a.num_pages) * kPage + (s % kPage) : -1;
+    lds_rows[j] = r;
+    const uint64_t bal = __ballot(r >= 0);
+    if ((lane & 31) == 0) lds_valid[j >> 5] = (uint32_t)(bal >> (lane & 32));
+    if (r >= 0) atomicMin(&lds_fill, j);
+  }
+  // the table's loads and this wave's q image loads have landed (vmcnt 0) ... for every wave
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
   // Keys that are not selected are gathered from the split's first selected row (finite data, so
   // their zero probabilities never meet a NaN); a split without any selected key skips its tiles.
   const int fill_j = lds_fill;
   const int fill_row = fill_j < kMaxSplitKeys ? lds_rows[fill_j] : 0;
   const int ntiles_run = fill_j < kMaxSplitKeys ? ntiles : 0;
+  {
+    const int h = wave * 32 + nl;
+    const unsigned char* qh = q_img + h * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ((2 * ks + hh) ^ ((h >> 1) & 7))));
+  }
+  lds_barrier();                            // every wave holds its q: the ring is free
 
   // Gather tile `tile` into ring slot `buf`.  This wave loads the value columns of rows
   // wave, wave + NW, ... (one load per row: the row id is wave-uniform, so the row's address is a
   // scalar base and each lane adds its own swizzled 16-byte chunk) and the rope blocks
   // wave, wave + NW, ... < 4 (8 rows x 8 chunks per load, lane i: row 8k + i/8, slot i%8).  Every
   // wave issues the same number of loads per tile, which the ring's counter waits rely on.
-  auto issue = [&](int tile, int buf) {
-    constexpr int kRows = kBK / NW, kRope = 4 / NW;
-    int prow[kRows];
+  constexpr int kRows = kBK / NW, kRope = 4 / NW;
+  auto gather_row = [&](int pr, int buf, int u) __attribute__((always_inline)) {   // pr: physical row (wave-uniform) or -1
+    const int r = wave + u * NW;
+    pr = pr < 0 ? fill_row : pr;
+    lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
+                   lds_kv[buf] + 1024 * r);
+  };
+  auto gather_rope = [&](int pr, int buf, int u) __attribute__((always_inline)) {  // pr: this lane's row, read by rope_row()
+    const int k = wave + u * NW;
+    const int r = 8 * k + (lane >> 3);
+    pr = pr < 0 ? fill_row : pr;
+    const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r));
+    lds_dma16(src, lds_kv[buf] + kRegionB + 1024 * k);
+  };
+  auto rope_row = [&](int tile, int u) __attribute__((always_inline)) { return lds_rows[tile * kBK + 8 * (wave + u * NW) + (lane >> 3)]; };
+  auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
+    int prow[kRows];                        // read together, made scalar one at a time
 #pragma unroll
     for (int u = 0; u < kRows; ++u) prow[u] = lds_rows[tile * kBK + wave + u * NW];
 #pragma unroll
-    for (int u = 0; u < kRope; ++u) {
-      const int k = wave + u * NW;
-      const int r = 8 * k + (lane >> 3);
-      int pr = lds_rows[tile * kBK + r];
-      pr = pr < 0 ? fill_row : pr;
-      const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r));
-      lds_dma16(src, lds_kv[buf] + kRegionB + 1024 * k);
-    }
+    for (int u = 0; u < kRope; ++u) gather_rope(rope_row(tile, u), buf, u);
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      const int r = wave + u * NW;
-      int pr = __builtin_amdgcn_readfirstlane(prow[u]);
-      pr = pr < 0 ? fill_row : pr;
-      lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
-                     lds_kv[buf] + 1024 * r);
-    }
+    for (int u = 0; u < kRows; ++u) gather_row(__builtin_amdgcn_readfirstlane(prow[u]), buf, u);
   };
 
   // O^T: 512 latent columns (16 blocks of 32) x 32 heads
@@ -311,19 +337,10 @@ void sfa_main(SfaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // First gathers, then q: the two latencies overlap.  The compiler-visible wait (vmcnt 0) lets
-  // it know no ordinary load is outstanding inside the main loop (it does not count the
-  // direct-to-LDS loads and would otherwise place waits for q there that also stall on the tiles
-  // in flight); it also covers the first tiles.
+  // First gathers; the first step waits for tile 0 alone and computes while tiles 1 and 2 land.
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
     if (i < ntiles_run) issue(i, i);
-  {
-    const unsigned char* src = a.q + ((size_t)row * a.H + (hvalid ? head : 0)) * kRowBytes + 16 * hh;
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(src + 32 * ks));
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
   for (;;) {
     for (int it = 0; it < ntiles_run; it += kStages) {
       step(it, std::integral_constant<int, 0>{});
