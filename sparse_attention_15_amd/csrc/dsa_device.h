@@ -87,6 +87,19 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
   return x;
 }
 
+// x combined with the value of lane i ^ 32, as one VALU exchange (v_permlane32_swap) instead of
+// an LDS permute round trip.  The swap leaves lane i's value and its partner's in the two results,
+// whichever half moved; both operations are commutative, so every lane gets the same bits as
+// x op partner.
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64).  `sh` holds NT/64
 // words of LDS.  Returns this thread's exclusive prefix and the workgroup total.  Its barriers
 // leave global loads in flight.

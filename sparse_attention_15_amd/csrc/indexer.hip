@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
         for (int m = 0; m < C::MB; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
-        part += __shfl_xor(part, 32, 64);
+        part = xor32_sum(part);
         if constexpr (FP8) part *= lds_ksc[kt / kPage];
         const int s = ts + kt;
         if (emit && hh == 0 && s < n_me) {
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       for (int m = 0; m < C::MB; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
-      part += __shfl_xor(part, 32, 64);
+      part = xor32_sum(part);
       if constexpr (FP8) part *= lds_ksc[buf][kt / kPage];
       const int s = j * C::KT + kt;
       if (hh == 0 && s < n_me) {
@@ -687,7 +687,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     for (int m = 0; m < C::MB; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
-    part += __shfl_xor(part, 32, 64);
+    part = xor32_sum(part);
     if constexpr (FP8) part *= kscale;
     const int s = j * C::KT + 32 * wave + nl;
     if (hh == 0 && s < n_me) {

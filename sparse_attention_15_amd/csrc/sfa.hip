@@ -16,8 +16,8 @@
 // tile with transposed LDS reads.  The accumulator O^T (512 x 32 per wave, 256 registers) lives in
 // the accumulation registers; the running max is kept in the log2 domain (exp2 with log2(e) folded
 // into the scale).  With one split the workgroup normalises and writes bf16 output and the
-// natural-log LSE; with several, each writes (m, l, O / l) partials and sfa_combine merges them:
-// M = max m_i, w_i = 2^(m_i - M) l_i, O = sum_i w_i (O_i / l_i) / sum_i w_i.
+// natural-log LSE; with several, each writes (m, l, O) partials and sfa_combine merges them:
+// M = max m_i, L = sum_i 2^(m_i - M) l_i, O = sum_i 2^(m_i - M) O_i / L.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -45,7 +45,7 @@ struct SfaArgs {
   __bf16* out;                  // [rows, H, 512]
   float* lse;                   // [rows, H] or null
   float* part_ml;               // [rows, splits, H, 2]
-  uint32_t* part_o;             // [rows, splits, head groups, 16, 8, 64] bf16 pairs
+  uint32_t* part_o;             // [rows, splits, head groups, 16 blocks, 2 halves, 64 lanes, 4] bf16 pairs
   int T, H, K, max_pages, num_pages, n_splits, keys_per_split, max_seq_len;
   float scale_log2;             // sm_scale * log2(e)
 };
@@ -297,7 +297,7 @@ void sfa_main(SfaArgs a) {
         mx = fmaxf(mx, s[r]);
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = xor32_max(mx);
     if (m_run == kNoRef && mx > -INFINITY) m_run = mx + kRefMargin;
     if (mx > m_run + kRefLimit) {           // too far above the reference: restart with a new one
       m_run = mx + kRefMargin;
@@ -309,7 +309,7 @@ void sfa_main(SfaArgs a) {
       s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
       psum += s[r];
     }
-    psum += __shfl_xor(psum, 32, 64);
+    psum = xor32_sum(psum);
     l_run += psum;
     // P^T as the B operand of the value product: K step k2 covers keys 16*k2 .. 16*k2 + 15; this
     // lane's 8 values are keys 16*k2 + {0..3, 8..11} + 4*hh (accumulator rows of the score tile)
@@ -388,25 +388,34 @@ void sfa_main(SfaArgs a) {
       a.part_ml[(ps * a.H + head) * 2] = m_run;
       a.part_ml[(ps * a.H + head) * 2 + 1] = l_run;
     }
-    // Normalised partial O / l as bf16 pairs (registers 2k, 2k+1) in the accumulator's own lane
-    // order, [head group][block][register pair][lane]: half the bytes of fp32 partials, whose
-    // rounding (2^-9 of the split's own output range) stays far inside the output tolerance.
+    // Partial O (not divided by l: the combine folds 1/l into its weights) as bf16 pairs
+    // (registers 2k, 2k+1) in the accumulator's own lane order, [head group][block][half][lane]
+    // [4 pairs]: each store instruction writes 1 KB contiguous (16 bytes per lane).  Half the
+    // bytes of fp32 partials; bf16 keeps 2^-9 relative to each value, far inside the output
+    // tolerance, and its range covers the accumulator's (probabilities stay below 2^kRefLimit).
     if (gg >= NGT) return;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     uint32_t* dst = a.part_o + ((ps * NGT + gg) * kVBlocks) * 8 * 64;
 #pragma unroll
     for (int mb = 0; mb < kVBlocks; ++mb)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dst[(mb * 8 + k) * 64 + lane] = pack_bf16(o[mb][2 * k] * inv, o[mb][2 * k + 1] * inv);
+      for (int half = 0; half < 2; ++half) {
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int k = 4 * half + q;
+          v[q] = pack_bf16(o[mb][2 * k], o[mb][2 * k + 1]);
+        }
+        *reinterpret_cast<u32x4*>(dst + ((mb * 2 + half) * 64 + lane) * 4) = v;
+      }
   }
 }
 
 // Merges the split partials.  Grid (query row, 32-head group, chunk): the 8*SG chunks of a
-// (row, group) share its 8192 bf16 pairs, 4 consecutive accumulator lanes (heads) per thread;
+// (row, group) share its 8192 bf16 pairs, 4 pairs (one 16-byte load) of one head per thread;
 // with SG > 1 the workgroup's SG thread groups take every SG-th split and are summed in LDS at
 // the end (more workgroups in flight when there are many splits).  Every workgroup first rebuilds
-// the per-head merge weights of its group.  With normalised partials O_i / l_i the weight of
-// split i is 2^(m_i - M) l_i / L.
+// the per-head merge weights of its group: with unnormalised partials O_i the weight of split i
+// is 2^(m_i - M) / L, L = sum_i 2^(m_i - M) l_i.
 
 struct CombineArgs {
   const float* part_ml;
@@ -445,9 +454,9 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
     for (int i = 0; i < S; ++i) M = fmaxf(M, sm[i][tid]);
     float L = 0.f;
     for (int i = 0; i < S; ++i) {
-      const float w = M != -INFINITY ? exp2f(sm[i][tid] - M) * wgt[i][tid] : 0.f;
-      wgt[i][tid] = w;
-      L += w;
+      const float e = M != -INFINITY ? exp2f(sm[i][tid] - M) : 0.f;
+      L += e * wgt[i][tid];
+      wgt[i][tid] = e;
     }
     const float inv_L = L > 0.f ? 1.f / L : 0.f;
     for (int i = 0; i < S; ++i) wgt[i][tid] *= inv_L;
@@ -455,23 +464,24 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
       a.lse[(size_t)row * a.H + head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
   __syncthreads();
-  // this thread's 4 pairs: u = index into the group's [mb][pair][lane] block of 8192 pairs
+  // this thread's 16-byte unit u of the group's [mb][half][lane][4 pairs] block (8192 pairs):
+  // 4 register pairs of one head (accumulator lane), i.e. output columns d0 .. d0 + 3 and
+  // d0 + 8 .. d0 + 11
   constexpr int TG = 256 / SG;              // threads per split group
   const int sg = tid / TG, t64 = tid % TG;
-  const int u = (chunk * TG + t64) * 4;
-  const int lane0 = u & 63, rp = (u >> 6) & 7, mb = u >> 9;
-  const size_t blk = (size_t)g * kVBlocks * 8 * 64 + (size_t)(mb * 8 + rp) * 64 + lane0;
+  const int u = chunk * TG + t64;
+  const int lane = u & 63, half = (u >> 6) & 1, mb = u >> 7;
+  const int nl = lane & 31, hh = lane >> 5;
   const size_t per_split = (size_t)NG * kVBlocks * 8 * 64;
+  const uint32_t* src = a.part_o + (size_t)row * S * per_split + (size_t)g * kVBlocks * 8 * 64 + 4 * (size_t)u;
   float acc[4][2] = {};
-  const uint32_t* src = a.part_o + (size_t)row * S * per_split + blk;
-  const int nl0 = lane0 & 31, hh = lane0 >> 5;
 #pragma unroll 4
   for (int sp = sg; sp < S; sp += SG) {
     const uint4 v = *reinterpret_cast<const uint4*>(src + sp * per_split);
     const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+    const float wq = wgt[sp][nl];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float wq = wgt[sp][nl0 + q];
       acc[q][0] = fmaf(wq, bf16_lo(vv[q]), acc[q][0]);
       acc[q][1] = fmaf(wq, bf16_hi(vv[q]), acc[q][1]);
     }
@@ -489,14 +499,12 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) { acc[q][0] += red[k][t64][2 * q]; acc[q][1] += red[k][t64][2 * q + 1]; }
   }
-  // registers 2rp, 2rp + 1 are columns d, d + 1
-  const int d = 32 * mb + 8 * (rp >> 1) + 4 * hh + 2 * (rp & 1);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int head = g * 32 + nl0 + q;
-    if (head < a.H)
-      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + d) =
-          pack_bf16(acc[q][0], acc[q][1]);
+  // register pair k = 4*half + q holds columns 32mb + 8(k >> 1) + 4hh + 2(k & 1) + {0, 1}
+  const int head = g * 32 + nl;
+  if (head < a.H) {
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + 32 * mb + 16 * half + 4 * hh;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[1][0], acc[1][1]));
+    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(pack_bf16(acc[2][0], acc[2][1]), pack_bf16(acc[3][0], acc[3][1]));
   }
 }
 
