@@ -724,9 +724,12 @@ constexpr int kMaxSeg = 32;                          // workgroups per row at mo
 constexpr int kMapWords = 2 * kSelThreads;           // bitmap words per emit chunk
 constexpr int kMapBits = 32 * kMapWords;             // positions per emit chunk (65536)
 
-// Keys per segment: whole scan steps, at most kMaxSeg segments.
+// Keys per segment: whole scan steps, at most kMaxSeg segments.  A row of up to two steps stays in
+// one workgroup (its second, prefetched step costs less than the publish-and-reload round trip
+// between the workgroups of a split row); longer rows take one step per segment.
 __host__ __device__ __forceinline__ int seg_len_of(int n) {
   const int steps = (n + kSelChunk - 1) / kSelChunk;
+  if (steps <= 2) return 2 * kSelChunk;
   return kSelChunk * ((steps + kMaxSeg - 1) / kMaxSeg);
 }
 

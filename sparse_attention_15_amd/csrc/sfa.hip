@@ -76,6 +76,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 constexpr int kTileBytes = kBK * kRowBytes;          // 36864
 constexpr int kDmaPerTile = kTileBytes / 1024;       // 36 wave-wide loads: 32 value rows + 4 rope blocks
 constexpr int kStages = 4;                           // gather ring depth (the main loop is unrolled by it)
+constexpr int kRingA = 4;                            // score-product A fragments in flight (LDS reads)
+constexpr int kRingV = 4;                            // value-product A fragments in flight (deeper spills)
 constexpr int kMaxSplitKeys = DSA_MAX_TOP_K;
 
 // Waits until this wave's loads of the tile being consumed have landed; `later` of its later
@@ -261,32 +263,37 @@ void sfa_main(SfaArgs a) {
       return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
           tile + ((q ? pv1 : pv0) ^ (64 * (mb & 3))) + 256 * (mb >> 2) + 16384 * (j >> 4)));
     };
-    constexpr int kRing = 4;
-    u32x4 aring[kRing];
+    u32x4 aring[kRingA];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) aring[j] = a_frag(j);
+    for (int j = 0; j < kRingA; ++j) aring[j] = a_frag(j);
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
-      const bf16x8 af = as_bf16x8(aring[ks % kRing]);
-      if (ks + kRing < kQSteps) aring[ks % kRing] = a_frag(ks + kRing);
+      const bf16x8 af = as_bf16x8(aring[ks % kRingA]);
+      if (ks + kRingA < kQSteps) aring[ks % kRingA] = a_frag(ks + kRingA);
       s = mfma_bf16(af, qf[ks], s);
       __builtin_amdgcn_sched_barrier(0);
     }
     // the first value-product fragments load while the softmax runs
-    s16x4 vring[kRing][2];
+    s16x4 vring[kRingV][2];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) { vring[j][0] = v_frag(j, 0); vring[j][1] = v_frag(j, 1); }
+    for (int j = 0; j < kRingV; ++j) { vring[j][0] = v_frag(j, 0); vring[j][1] = v_frag(j, 1); }
 
-    // online softmax over the 16 keys this lane holds (+ the other half-wave's 16)
-    float mx = -INFINITY;
+    // Online softmax over the 16 keys this lane holds (+ the other half-wave's 16).  The
+    // probabilities 2^(s - m_ref) need only the fixed reference, not this tile's max, which serves
+    // the first tile (it sets the reference) and the restart check.  So the keys of the value
+    // product's first K step are exponentiated right away and the rest of the softmax (the other 8
+    // exponentials, the sums, the cross-half max) runs between its MFMAs, under the matrix pipe.
+    // A restart discards this pass, so a tile exponentiated against a reference it then raises
+    // never reaches the output.
+    float mloc = -INFINITY;
     if (valid == 0xFFFFFFFFu) {             // wave-uniform: every key of the tile is selected
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[r] *= a.scale_log2;
-        mx = fmaxf(mx, s[r]);
+        mloc = fmaxf(mloc, s[r]);
       }
     } else {
       const uint32_t vmask = valid >> (4 * hh);
@@ -294,33 +301,27 @@ void sfa_main(SfaArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int key = 8 * (r >> 2) + (r & 3);        // + 4*hh, folded into `vmask`
         s[r] = ((vmask >> key) & 1u) ? s[r] * a.scale_log2 : -INFINITY;
-        mx = fmaxf(mx, s[r]);
+        mloc = fmaxf(mloc, s[r]);
       }
     }
-    mx = xor32_max(mx);
-    if (m_run == kNoRef && mx > -INFINITY) m_run = mx + kRefMargin;
-    if (mx > m_run + kRefLimit) {           // too far above the reference: restart with a new one
-      m_run = mx + kRefMargin;
-      lds_epoch = epoch + 1;
+    // every lane sets its reference on the same tile (the first with a selected key): uniform
+    if (__builtin_amdgcn_readfirstlane(m_run == kNoRef ? 1 : 0)) {
+      const float m0 = xor32_max(mloc);
+      if (m0 > -INFINITY) m_run = m0 + kRefMargin;
     }
-    float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
-      psum += s[r];
-    }
-    psum = xor32_sum(psum);
-    l_run += psum;
+    for (int r = 0; r < 8; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
     // P^T as the B operand of the value product: K step k2 covers keys 16*k2 .. 16*k2 + 15; this
     // lane's 8 values are keys 16*k2 + {0..3, 8..11} + 4*hh (accumulator rows of the score tile)
-    bf16x8 pf[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
+    auto pack_p = [&](int k2) {
       u32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = pack_bf16(s[8 * k2 + 2 * e], s[8 * k2 + 2 * e + 1]);
-      pf[k2] = as_bf16x8(v);
-    }
+      return as_bf16x8(v);
+    };
+    bf16x8 pf[2];
+    pf[0] = pack_p(0);
+    float mx = mloc, psum = 0.f;
     // O^T += V^T P^T.  The A operand (latent column m, the same 8 keys) comes from two transposed
     // reads of the row-major tile: a 16-lane group reading 8 bytes (4 columns) of 4 consecutive
     // keys hands lane i the 4 keys of column i.  Same 4-deep ring as the score product;
@@ -328,12 +329,30 @@ void sfa_main(SfaArgs a) {
 #pragma unroll
     for (int j = 0; j < 2 * kVBlocks; ++j) {
       const int k2 = j >> 4, mb = j & 15;
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vring[j % kRing][0], vring[j % kRing][1], 0, 1, 2, 3, 4, 5, 6, 7));
-      if (j + kRing < 2 * kVBlocks) {
-        vring[j % kRing][0] = v_frag(j + kRing, 0);
-        vring[j % kRing][1] = v_frag(j + kRing, 1);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vring[j % kRingV][0], vring[j % kRingV][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (j + kRingV < 2 * kVBlocks) {
+        vring[j % kRingV][0] = v_frag(j + kRingV, 0);
+        vring[j % kRingV][1] = v_frag(j + kRingV, 1);
       }
       o[mb] = mfma_bf16(vf, pf[k2], o[mb]);
+      // the rest of the softmax, one slice after each MFMA of the first K step
+      if (j < 8) {
+        s[8 + j] = __builtin_amdgcn_exp2f(s[8 + j] - m_run);
+      } else if (j == 8) {
+        pf[1] = pack_p(1);
+      } else if (j == 9) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) psum += s[r];
+      } else if (j == 10) {
+        psum = xor32_sum(psum);
+        mx = xor32_max(mx);
+      } else if (j == 11) {
+        l_run += psum;
+        if (mx > m_run + kRefLimit) {       // too far above the reference: restart with a new one
+          m_run = mx + kRefMargin;
+          lds_epoch = epoch + 1;
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };

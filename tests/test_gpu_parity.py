@@ -116,9 +116,10 @@ def test_select_crowded_threshold_exact(values, lens, expect):
     assert np.array_equal(idx, ref)
 
 
-# Rows longer than one select segment (16384 keys) are split over several workgroups whose lists
-# meet in global memory; rows longer than 65536 keys are emitted in several bitmap chunks.
-@pytest.mark.parametrize("T,lens", [(1, (16384, 16385, 40000, 70000)), (4, (33000, 20000))])
+# Rows longer than one select segment (two scan steps of 16384 keys for rows up to 32768 keys, one
+# step beyond) are split over several workgroups whose lists meet in global memory; rows longer
+# than 65536 keys are emitted in several bitmap chunks.
+@pytest.mark.parametrize("T,lens", [(1, (16385, 32768, 32769, 70000)), (4, (33000, 20000))])
 def test_multi_segment_rows_exact(T, lens):
     spec = W.custom("grid8_long", len(lens), T, lens, 64, 128, 2048, 16, values="grid8")
     _run(spec, exact=True, check_sfa=False)
