@@ -172,6 +172,16 @@ const char *dsa_last_error(void);
 /* DSA_VERSION of the library. */
 int dsa_version(void);
 
+/* Synchronises `stream`, then reports the device-side precondition checks of every call made on
+ * the current device since the last dsa_debug_status (the kernels clamp or skip what fails them,
+ * see the conventions above, and record which kind failed).  Returns DSA_OK when none failed;
+ * DSA_ERR_SHAPE when some did, with dsa_last_error() naming them (a block_table entry outside
+ * [0, num_pages) for a visible position, a seq_lens entry outside [T, max_seq_len], an attention
+ * index that is neither -1 nor a visible position); DSA_ERR_HIP if the synchronisation fails.
+ * Reading clears the record.  The checks cost a compare per page or index in the kernels'
+ * set-up code and run in every build. */
+dsa_status dsa_debug_status(hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,7 +56,7 @@ _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
            "dsa_sparse_attn", "dsa_profile_start", "dsa_profile_stop", "dsa_last_error",
-           "dsa_version"]
+           "dsa_version", "dsa_debug_status"]
 
 
 def lib() -> ctypes.CDLL:
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_attn.restype = ctypes.c_int
     L.dsa_last_error.argtypes = []
     L.dsa_last_error.restype = ctypes.c_char_p
+    L.dsa_debug_status.argtypes = [vp]
+    L.dsa_debug_status.restype = ctypes.c_int
     L.dsa_version.argtypes = []
     L.dsa_version.restype = ctypes.c_int
     L.dsa_profile_start.argtypes = []
@@ -184,3 +186,10 @@ def dsa_profile_stop() -> dict:
     if n < 0:
         raise DsaError(6, "dsa_profile_stop: HIP error")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}
+
+
+def dsa_debug_status(stream=None) -> None:
+    """Synchronises the stream and raises DsaError if a kernel met a violated device-side
+    precondition since the last call (bad block-table entry, sequence length or attention
+    index); the record is cleared by reading it."""
+    _check(lib().dsa_debug_status(_stream(stream)))

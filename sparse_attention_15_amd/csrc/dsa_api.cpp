@@ -76,6 +76,21 @@ int dsa_version(void) { return DSA_VERSION; }
 
 const char* dsa_last_error(void) { return g_last_error.c_str(); }
 
+dsa_status dsa_debug_status(hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "stream synchronize: %s", hipGetErrorString(e));
+  uint32_t fi = 0, fa = 0;
+  e = dsa::indexer_take_input_flags(&fi);
+  if (e == hipSuccess) e = dsa::attn_take_input_flags(&fa);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "reading the input-check flags: %s", hipGetErrorString(e));
+  const uint32_t f = fi | fa;
+  if (f == 0) return DSA_OK;
+  return fail(DSA_ERR_SHAPE, "device-side input checks failed:%s%s%s",
+              (f & 1u) ? " block_table entry outside [0, num_pages);" : "",
+              (f & 2u) ? " seq_lens entry outside [T, max_seq_len];" : "",
+              (f & 4u) ? " attention index neither -1 nor a visible position;" : "");
+}
+
 size_t dsa_indexer_workspace_size(const dsa_paged_layout* layout, const dsa_indexer_shape* shape) {
   if (check_indexer_shape(shape) != DSA_OK || check_layout(layout, shape->T) != DSA_OK) return 0;
   return dsa::plan_indexer(*layout, *shape).total;

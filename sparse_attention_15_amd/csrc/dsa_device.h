@@ -126,17 +126,34 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return pre + x - v;
 }
 
+// Device-side input checks.  Each translation unit that includes this header has its own flag
+// word; a kernel that meets a violated precondition ORs a bit into it (vector atomic, only on the
+// violating path) and carries on with the clamped value, so bad inputs give wrong numbers and a
+// flag, never an out-of-bounds access.  dsa_debug_status() reads and clears the words.
+constexpr uint32_t kFlagPage = 1u;         // a block-table entry in use lies outside [0, num_pages)
+constexpr uint32_t kFlagLen = 2u;          // a sequence length lies outside [T, max_seq_len]
+constexpr uint32_t kFlagIndex = 4u;        // an attention index is neither -1 nor a visible position
+static __device__ uint32_t g_input_flags;
+__device__ __forceinline__ void flag_input(uint32_t bit) { atomicOr(&g_input_flags, bit); }
+
 // Length of query row (b, t): keys 0..pos are visible, pos = seq_len - T + t.  seq_len is clamped
 // to the block-table capacity so a bad length can never address past the table.
 __device__ __forceinline__ int row_visible(const int32_t* seq_lens, int b, int T, int t, int cap) {
   int L = seq_lens[b];
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+  if (L < T || L > cap) {
+    flag_input(kFlagLen);
+    L = L < 0 ? 0 : (L > cap ? cap : L);
+  }
   int n = L - T + t + 1;
   return n < 0 ? 0 : n;
 }
 
 __device__ __forceinline__ int clamp_page(int p, int num_pages) {
-  return p < 0 ? 0 : (p >= num_pages ? num_pages - 1 : p);
+  if (p < 0 || p >= num_pages) {
+    flag_input(kFlagPage);
+    p = p < 0 ? 0 : num_pages - 1;
+  }
+  return p;
 }
 
 }  // namespace dsa

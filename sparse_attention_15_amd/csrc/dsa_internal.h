@@ -47,6 +47,10 @@ struct IndexerArgs {
   void* workspace;
 };
 
+// Read and clear the device-side input-check flags of each translation unit (current device).
+hipError_t indexer_take_input_flags(uint32_t* flags);
+hipError_t attn_take_input_flags(uint32_t* flags);
+
 IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S);
 bool indexer_supported(int heads, int dim);
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t stream);

@@ -1072,6 +1072,13 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
 // ------------------------------------------------------------------------------------------------
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+hipError_t indexer_take_input_flags(uint32_t* flags) {
+  uint32_t z = 0;
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_input_flags), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_input_flags), &z, sizeof z, 0, hipMemcpyHostToDevice);
+  return e;
+}
+
 IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S) {
   IndexerPlan p;
   p.rows = L.batch * S.T;

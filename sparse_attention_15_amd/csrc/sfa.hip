@@ -150,6 +150,7 @@ void sfa_main(SfaArgs a) {
   lds_barrier();
   for (int j = tid; j < ntiles * kBK; j += NT) {   // NT is a multiple of 64: whole waves
     const int s = j == tid ? s_first : (j < nkeys ? idx[j] : -1);
+    if (s < -1 || s >= n) flag_input(kFlagIndex);
     const int r = s >= 0 && s < n ? clamp_page(bt[s / kPage], a.num_pages) * kPage + (s % kPage) : -1;
     lds_rows[j] = r;
     const uint64_t bal = __ballot(r >= 0);
@@ -529,6 +530,13 @@ __global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
 
 // ------------------------------------------------------------------------------------------------
 static size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
+
+hipError_t attn_take_input_flags(uint32_t* flags) {
+  uint32_t z = 0;
+  hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_input_flags), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_input_flags), &z, sizeof z, 0, hipMemcpyHostToDevice);
+  return e;
+}
 
 AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   AttnPlan p;
