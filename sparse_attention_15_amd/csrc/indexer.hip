@@ -284,7 +284,9 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   __shared__ float lds_ksc[2][C::KT / kPage > 0 ? C::KT / kPage : 1];
   __shared__ int lds_tstart[kMaxSeqPersist + 1];
   __shared__ int lds_len[kMaxSeqPersist];       // clamped sequence length (= visible keys of the last query row)
-  __shared__ int lds_page[kMaxPagesPersist];    // physical pages of this workgroup's tiles, in order
+  // per tile of this workgroup: sequence | tile index << 9, the physical pages of its (one or two)
+  // pages (-1 past the sequence end), and the sequence's clamped length
+  __shared__ int4 lds_rec[kMaxPagesPersist];
   __shared__ uint32_t sh[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -311,7 +313,9 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   const int total = carry;
   const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
   const int hi = (int)((long long)(blockIdx.x + 1) * total / gridDim.x);
-  const int n_items = hi - lo;
+  // the grid keeps every range within the page table (n_items * PPT <= kMaxPagesPersist)
+  constexpr int PPT = C::KT / kPage > 0 ? C::KT / kPage : 1;   // pages per tile
+  const int n_items = min(hi - lo, kMaxPagesPersist / PPT);
   if (n_items <= 0) return;
 
   auto locate = [&](int f) -> int {   // sequence holding flat tile f
@@ -322,24 +326,24 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
     }
     return l;
   };
-  // physical page ids of this workgroup's tiles (one round of block-table loads, off the
-  // per-tile critical path); a range longer than the LDS table reads the block table directly
-  constexpr int PPT = C::KT / kPage > 0 ? C::KT / kPage : 1;   // pages per tile
-  const bool page_cached = n_items * PPT <= kMaxPagesPersist;
-  if (page_cached) {
-    for (int i = tid; i < n_items * PPT; i += kThreads) {
-      const int f = lo + i / PPT;
-      const int b = locate(f);
-      const int lp = (f - lds_tstart[b]) * PPT + i % PPT;
-      lds_page[i] = lp * kPage < lds_len[b]
-          ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : 0;
+  // Tile records of this workgroup's range: one round of block-table loads, off the per-tile
+  // path.  A tile's loads then depend on one LDS read, and the compiler sees exactly the tile
+  // loads between two tiles, so it can wait for the oldest while the others stay in flight.
+  static_assert(PPT <= 2, "two pages per record");
+  for (int i = tid; i < n_items; i += kThreads) {
+    const int f = lo + i;
+    const int b = locate(f);
+    const int j = f - lds_tstart[b];
+    const int n = lds_len[b];
+    int pg[2] = {-1, -1};
+#pragma unroll
+    for (int h = 0; h < PPT; ++h) {
+      const int lp = j * PPT + h;
+      if (lp * kPage < n) pg[h] = clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages);
     }
+    lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
   }
   __syncthreads();
-  auto page_of = [&](int f, int b, int lp) -> int {
-    if (page_cached) return lds_page[(f - lo) * PPT + (lp % PPT)];
-    return clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages);
-  };
 
   const int qi = wave / C::WPQ, nsub = wave % C::WPQ;
   const bool qvalid = qi < a.T;
@@ -386,31 +390,36 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   // sequence end and tiles past the range read page 0 instead), so the compiler can wait for one
   // tile while the next stays in flight: a load that is skipped on some path would make it wait
   // for all of them.
-  u32x4 pre0[C::LPT], pre1[C::LPT];
-  int pb0 = 0, pj0 = 0, pb1 = 0, pj1 = 0;
-  int b_iss = locate(lo);             // sequence of the last tile issued (tiles go in order)
+  // kPre tiles are in flight while one is computed; the two LDS buffers alternate by step parity.
+  constexpr int kPre = TQ == 1 ? 2 : 3;
+  u32x4 pre[kPre][C::LPT];
+  int pb[kPre], pj[kPre];
+  float psc[kPre];                    // fp8: this thread's page scale of the tile (thread < PPT)
+  int b_iss = lds_rec[0].x & 511;     // sequence of the last tile issued (dummies reuse it)
   // A dummy call (live == false, past the end of the range) reads page 0 only and leaves the
   // sequence cursor alone; its buffer is never committed.
-  auto issue = [&](int f, bool live, u32x4 (&pre)[C::LPT], int& pb, int& pj) {
-    int b = b_iss, j = 0;
+  auto issue = [&](int f, bool live, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc) {
+    int b = b_iss, j = 0, pg0 = -1, pg1 = -1;
     if (live) {
-      while (b + 1 < a.B && lds_tstart[b + 1] <= f) ++b;
+      const int4 r = lds_rec[f - lo];
+      b = r.x & 511; j = r.x >> 9; pg0 = r.y; pg1 = r.z;
       b_iss = b;
-      j = f - lds_tstart[b];            // 0 <= j < tiles of sequence b
     }
     pb = b; pj = j;
-    const int nmax = live ? lds_len[b] : 0;
-    const int ts = j * C::KT;
 #pragma unroll
     for (int q = 0; q < C::LPT; ++q) {
       const int i = tid + kThreads * q;
       const int key = i / C::CPK, c = i % C::CPK;
-      const int lp = ts / kPage + key / kPage;   // >= 0
-      const int phys = lp * kPage < nmax ? page_of(f, b, lp) : 0;
+      const int pg = PPT == 1 || key < kPage ? pg0 : pg1;   // -1 past the end (and for dummies)
+      const int phys = pg < 0 ? 0 : pg;
       pre[q] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
     }
+    if constexpr (FP8) {              // one scale load per thread; pages past the end read page 0
+      const int pg = PPT == 2 && tid == 1 ? pg1 : pg0;
+      psc = a.k_scale[pg < 0 ? 0 : pg];
+    }
   };
-  auto commit = [&](const u32x4 (&pre)[C::LPT], int buf, int b, int j) {
+  auto commit = [&](const u32x4 (&pre)[C::LPT], float psc, int buf, int b, int j) {
 #pragma unroll
     for (int q = 0; q < C::LPT; ++q) {
       const int i = tid + kThreads * q;
@@ -420,7 +429,7 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
     if constexpr (FP8) {
       if (tid < PPT) {
         const int lp = j * C::KT / kPage + tid;
-        lds_ksc[buf][tid] = (lp * kPage < lds_len[b]) ? a.k_scale[page_of(lds_tstart[b] + j, b, lp)] : 0.f;
+        lds_ksc[buf][tid] = (lp * kPage < lds_len[b]) ? psc : 0.f;
       }
     }
   };
@@ -471,14 +480,22 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   };
 
   for (int i = tid; i < TQ * kBins; i += kThreads) lds_hist[i] = 0u;
-  issue(lo, true, pre0, pb0, pj0);
-  issue(n_items > 1 ? lo + 1 : lo, n_items > 1, pre1, pb1, pj1);
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) issue(u < n_items ? lo + u : lo, u < n_items, pre[u], pb[u], pj[u], psc[u]);
   int b_cur = -1;
-  auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, int buf) {
-    commit(pre, buf, pb, pj);
+  // Every step commits, meets the barrier and issues its loads, including the up to kPre - 1
+  // dead steps past the range (dummy loads, no compute): the same kPre - 1 tiles of loads then
+  // follow each buffer's on every path, so the compiler waits for that buffer alone.
+  auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc) {
+    const int buf = i & 1;
+    const bool alive = i < n_items;
+    commit(pre, psc, buf, pb, pj);
     const int b = pb, j = pj;
-    lds_barrier();                    // keeps the next tile's loads in flight
-    if (b != b_cur) {                 // new sequence: publish the old histogram, load new q
+    // the buffer is free: the next loads go out before the barrier, their set-up overlapping it
+    const bool live = i + kPre < n_items;
+    issue(live ? lo + i + kPre : lo, live, pre, pb, pj, psc);
+    lds_barrier();                    // keeps the next tiles' loads in flight
+    if (alive && b != b_cur) {        // new sequence: publish the old histogram, load new q
       if (b_cur >= 0) flush(b_cur);
       load_q(b);
       b_cur = b;
@@ -487,13 +504,11 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
       lds_barrier();
     }
-    const bool live = i + 2 < n_items;
-    issue(live ? lo + i + 2 : lo, live, pre, pb, pj);
-    compute(buf, b, j);
+    if (alive) compute(buf, b, j);
   };
-  for (int i = 0; i < n_items; i += 2) {
-    step(i, pre0, pb0, pj0, 0);
-    if (i + 1 < n_items) step(i + 1, pre1, pb1, pj1, 1);
+  for (int i = 0; i < n_items; i += kPre) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) step(i + u, pre[u], pb[u], pj[u], psc[u]);
   }
   __syncthreads();
   flush(b_cur);
@@ -1165,8 +1180,10 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
     const int kt = p.tq == 1 ? 128 : 64;
     const long long max_tiles = (long long)a.B * ((a.max_seq_len + kt - 1) / kt);
     grid = (int)std::max<long long>(1, std::min<long long>(2LL * device_cus(), (max_tiles + 1) / 2));
-    // the decode kernel's per-workgroup tile table holds kDecodeMaxItems tiles
+    // a workgroup's range (at most ceil(max_tiles / grid) tiles) must fit its tile table:
+    // kDecodeMaxItems tiles in the decode kernel, kMaxPagesPersist pages in the others
     if (p.tq == 1) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
+    else grid = (int)std::max<long long>(grid, (max_tiles * (kt / kPage) + kMaxPagesPersist - 1) / kMaxPagesPersist);
   }
   if (grid > 0) {
     LaunchScope ls("li_score", st);
