@@ -517,7 +517,8 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 // ------------------------------------------------------------------------------------------------
 // Decode, one query row per sequence.  The persistent grid walks the same flattened
 // (sequence, 128-key tile) list as li_score_persist, but each wave streams only its own 32-key
-// block of every tile, through a private two-slot LDS ring filled with direct-to-LDS loads (the
+// block of every tile, through a private LDS ring (two 8 KiB slots for bf16 keys, four 4 KiB
+// slots for fp8) filled with direct-to-LDS loads (the
 // block lies in one page, so its address is a scalar base plus a per-lane offset).  Nothing in
 // the main loop waits for another wave: the waves meet only when the sequence changes, to publish
 // the shared row histogram and load the next query.
@@ -531,11 +532,14 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   constexpr int NLD = BLK / 1024;                  // wave-wide loads per block
   constexpr int KPL = 1024 / C::ROWB;              // keys per load
   static_assert(NLD >= 1 && KPL * C::CPK == 64 && C::KT / kPage == 2, "block shape");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][2][BLK];
+  // ring slots per wave: 64 KiB of ring per workgroup either way (two workgroups per CU)
+  constexpr int NSLOT = FP8 ? 4 : 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][NSLOT][BLK];
   __shared__ uint32_t lds_hist[kBins];
   // per tile of this workgroup: sequence | tile index << 9, the physical pages of its two halves
   // (-1 past the sequence end), and the sequence's visible length
   __shared__ int4 lds_rec[kDecodeMaxItems];
+  __shared__ float2 lds_rsc[FP8 ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
   __shared__ uint32_t sh[8];
   // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
   static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
@@ -617,6 +621,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   };
 
   // the first sequence's query loads while the tile records are built
+  float2 my_sc = make_float2(0.f, 0.f);   // fp8: scales of this thread's record (n_items <= threads)
   int b_cur = locate(lo);
   load_q(b_cur);
   for (int i = tid; i < n_items; i += kThreads) {
@@ -631,19 +636,21 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       pg[h] = lp * kPage < n ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : -1;
     }
     lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
+    // fp8 page scales: loaded now, stored to LDS once the first gathers are in flight
+    if constexpr (FP8) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
 
   // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i (page half wave / 2), into
-  // ring slot i & 1.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key % CPK),
-  // so the slot holds key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block past
-  // the sequence end reads page 0; its keys are never stored.
-  float pks[2] = {1.f, 1.f};
+  // ring slot i % NSLOT.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key %
+  // CPK), so the slot holds key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block
+  // past the sequence end reads page 0; its keys are never stored.  The loop issues no other
+  // global load (the fp8 page scales come from the tile records), so the counter waits below see
+  // only these.
   auto issue = [&](int i, int slot) {
     const int4 r = lds_rec[i];
     const int pg = __builtin_amdgcn_readfirstlane(wave < 2 ? r.y : r.z);
     const int phys = pg < 0 ? 0 : pg;
-    if constexpr (FP8) pks[slot] = pg < 0 ? 0.f : a.k_scale[phys];
     const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (wave & 1)) * C::ROWB;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
@@ -652,15 +659,26 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), lds_k[wave][slot] + 1024 * u);
     }
   };
-  issue(0, 0);
-  if (n_items > 1) issue(1, 1);
-  // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table loads, so no wait
-  // for them lands in the main loop (it also covers the first two blocks)
+#pragma unroll
+  for (int u = 0; u < NSLOT; ++u)
+    if (u < n_items) issue(u, u);
+  // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
+  // so no wait for them lands in the main loop (it also covers the first blocks)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (FP8) {
+    static_assert(kDecodeMaxItems <= kThreads, "one record per thread");
+    if (tid < n_items) lds_rsc[tid] = my_sc;
+    lds_barrier();
+  }
 
   for (int i = 0; i < n_items; ++i) {
-    const int slot = i & 1;
-    if (i + 1 < n_items) wait_vmcnt<NLD>(); else wait_vmcnt<0>();
+    const int slot = i % NSLOT;
+    // this wave's block i has landed; up to NSLOT - 1 later blocks stay in flight
+    const int later = min(NSLOT - 1, n_items - 1 - i);
+    if (later >= 3) wait_vmcnt<3 * NLD>();
+    else if (later == 2) wait_vmcnt<2 * NLD>();
+    else if (later == 1) wait_vmcnt<NLD>();
+    else wait_vmcnt<0>();
     const int4 rec = lds_rec[i];
     const int b = __builtin_amdgcn_readfirstlane(rec.x & 511);
     const int j = __builtin_amdgcn_readfirstlane(rec.x >> 9);
@@ -673,7 +691,11 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       __syncthreads();
       b_cur = b;
     }
-    const float kscale = pks[slot];   // read before issue() below refills this slot's record
+    float kscale = 1.f;
+    if constexpr (FP8) {
+      const float2 sc = lds_rsc[i];
+      kscale = wave < 2 ? sc.x : sc.y;
+    }
     const unsigned char* blk = lds_k[wave][slot];
     frag_t bfr[C::KS];
 #pragma unroll
@@ -696,7 +718,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
         else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
       }
     // the slot's reads are complete (the MFMAs consumed them): refill it
-    if (i + 2 < n_items) issue(i + 2, slot);
+    if (i + NSLOT < n_items) issue(i + NSLOT, slot);
     float part = 0.f;
 #pragma unroll
     for (int m = 0; m < C::MB; ++m)
