@@ -545,10 +545,15 @@ AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   p.head_chunks = (p.waves + p.groups_per_wg - 1) / p.groups_per_wg;
   const int rows = L.batch * S.T;
   // splits: enough workgroups (rows x head chunks x splits) to cover the GPU's 256 compute units,
-  // at most 64 splits, each holding a whole number of 32-row tiles
+  // at most 64 splits, each holding a whole number of 32-row tiles.  A split of fewer than 4 tiles
+  // pays more for its partial output (written, then read back by the combine) and its prologue
+  // than its extra parallelism returns, so splits keep 4 tiles as long as the grid still has 128
+  // workgroups (8 rows at K = 2048: 16 splits of 4 tiles measured faster than 32 of 2).
   const int tiles = (S.top_k + kBK - 1) / kBK;
   const int per_split = std::max(rows * p.head_chunks, 1);
   int splits = (256 + per_split - 1) / per_split;
+  const int min_splits = (128 + per_split - 1) / per_split;
+  splits = std::max(min_splits, std::min(splits, tiles / 4));
   splits = std::max(1, std::min(splits, std::min(64, tiles)));
   const int tiles_per = (tiles + splits - 1) / splits;
   p.keys_per_split = tiles_per * kBK;
