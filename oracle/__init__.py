@@ -25,11 +25,13 @@ What the oracle computes (readings of the pages where they are silent are marked
     [P2] "Inheritance and Extension of Core Operators" (blockwise attention whose cross-block
     reduction equals the global softmax).  Reading: exact softmax over the selected set, MLA latent
     rows of width 576 of which the first 512 columns are V, explicit softmax scale.
-  * codecs            -- bf16 and OCP E4M3FN decoding from the format definitions.
+  * codecs            -- bf16, OCP E4M3FN and E8M0 (MX shared scale) decoding from the format
+    definitions.  The MXFP8 indexer inputs ([P1] §4) are E4M3FN codes with one E8M0 scale per 32
+    consecutive elements of each q row and each cached key row.
 
 Pins: every function is pinned in tests/test_oracle_*.py against closed forms, invariants,
 brute force on tiny inputs and library routines (torch casts, torch SDPA); see the test headers.
 """
-from .codecs import bf16_bits_to_f64, e4m3_codes_to_f64, e4m3_table  # noqa: F401
+from .codecs import bf16_bits_to_f64, e4m3_codes_to_f64, e4m3_table, e8m0_to_f64  # noqa: F401
 from .indexer import indexer_scores_ref, indexer_topk_ref, visible_positions  # noqa: F401
 from .sfa import sparse_attn_ref  # noqa: F401

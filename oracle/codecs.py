@@ -5,6 +5,9 @@ E4M3FN (OCP 8-bit floating point, "FN" variant): 1 sign bit, 4 exponent bits wit
 bits; exponent field 0 encodes subnormals m * 2^-9; no infinities; codes 0x7F and 0xFF are NaN;
 largest finite magnitude 448.  The pages name FP8 storage for the indexer path ([P1] §4, [P3] §3.3)
 without fixing the flavour; E4M3FN is this library's reading.
+E8M0 (the shared scale of the OCP Microscaling formats, which [P1] §4 and [P3] §3.3 name as MXFP8
+for the indexer): an unsigned 8-bit biased exponent with no sign and no mantissa, value
+2^(e - 127) for e in 0..254; e = 255 is NaN.
 """
 import numpy as np
 
@@ -36,3 +39,11 @@ _E4M3 = e4m3_table()
 
 def e4m3_codes_to_f64(u8: np.ndarray) -> np.ndarray:
     return _E4M3[np.asarray(u8, dtype=np.uint8)]
+
+
+def e8m0_to_f64(u8: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scale bytes: 2^(e - 127), NaN for 255."""
+    e = np.asarray(u8, dtype=np.uint8).astype(np.int64)
+    out = np.ldexp(1.0, e - 127).astype(np.float64)
+    out[e == 255] = np.nan
+    return out

@@ -6,6 +6,9 @@ and Top-K; the paged K cache is read in place).  Readings where the pages are si
   * score I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]); one key vector per position, shared by
     the indexer heads; no softmax or extra scale (any scale is folded into w);
   * fp8 path: q = q_scale[t,h] * e4m3(q_code), k = k_scale[page] * e4m3(k_code);
+  * mxfp8 path (MXFP8, [P1] §4, [P3] §3.3): every run of 32 consecutive elements of a q row or
+    of a cached key row shares one E8M0 scale: q[t,h,d] = e8m0(q_scale[t,h,d // 32]) *
+    e4m3(q_code[t,h,d]) and k[s,d] = e8m0(k_scale[page, slot, d // 32]) * e4m3(k_code[s,d]);
   * queries are the last T positions of their sequence: query t of sequence b sits at
     pos = seq_len[b] - T + t and sees keys 0..pos (its own key included);
   * K' = min(K, pos + 1) positions are kept: the K' largest scores, ties to the lower position;
@@ -14,7 +17,7 @@ Arithmetic is float64 on the decoded inputs; a score of -0 compares equal to +0.
 """
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_codes_to_f64
+from .codecs import bf16_bits_to_f64, e4m3_codes_to_f64, e8m0_to_f64
 
 PAGE = 64
 
@@ -24,8 +27,16 @@ def visible_positions(seq_len: int, T: int, t: int) -> int:
     return int(seq_len) - int(T) + int(t) + 1
 
 
+MX_GROUP = 32   # elements per shared scale in the MX formats
+
+
 def _decode(x, dtype):
     return bf16_bits_to_f64(x) if dtype == "bf16" else e4m3_codes_to_f64(x)
+
+
+def _mx_scales(scale_bytes, dim):
+    """Per-element scale of MX rows: each E8M0 byte covers MX_GROUP consecutive elements."""
+    return np.repeat(e8m0_to_f64(scale_bytes), MX_GROUP, axis=-1)[..., :dim]
 
 
 def _keys_of_sequence(k_cache, k_scale, block_table, b, n, dtype):
@@ -36,6 +47,8 @@ def _keys_of_sequence(k_cache, k_scale, block_table, b, n, dtype):
     k = _decode(k_cache[pages, s % PAGE], dtype)
     if dtype == "fp8":
         k = k * k_scale[pages].astype(np.float64)[:, None]
+    elif dtype == "mxfp8":
+        k = k * _mx_scales(k_scale[pages, s % PAGE], k.shape[-1])
     return k
 
 
@@ -51,6 +64,8 @@ def indexer_scores_ref(q_idx, q_scale, w, k_cache, k_scale, block_table, seq_len
         q = _decode(q_idx[b, t], dtype)                                          # [HI, DI]
         if dtype == "fp8":
             q = q * q_scale[b, t].astype(np.float64)[:, None]
+        elif dtype == "mxfp8":
+            q = q * _mx_scales(q_scale[b, t], q.shape[-1])
         dots = q @ k[:n].T                                                       # [HI, n]
         relu = np.maximum(dots, 0.0)
         wt = w[b, t].astype(np.float64)                                          # [HI]

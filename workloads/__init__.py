@@ -31,6 +31,8 @@ DQK = 576          # MLA latent row: 512 "nope" + 64 rope
 DV = 512           # V = first 512 columns of the latent row
 BF16_NAN = np.uint16(0x7FC0)
 E4M3_NAN = np.uint8(0x7F)
+E8M0_NAN = np.uint8(0xFF)   # NaN scale byte
+MX_GROUP = 32               # elements per MX shared scale
 E4M3_MAX = 448.0
 _SEED_ROOT = 15
 _CHUNK = 1 << 22   # elements per independently seeded generation chunk
@@ -48,8 +50,8 @@ class CaseSpec:
     DI: int                # indexer head dim
     K: int                 # top-k
     H: int                 # attention heads
-    idx_dtype: str = "bf16"   # "bf16" | "fp8"
-    values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "ties2" | "narrow" | "fp8grid" | "sharp"
+    idx_dtype: str = "bf16"   # "bf16" | "fp8" | "mxfp8"
+    values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "ties2" | "narrow" | "fp8grid" | "mxgrid" | "sharp"
     sharp_c: float = 1.0
     variant: int = 0
     spare_pages: int = 1
@@ -75,10 +77,10 @@ class Case:
     block_table: np.ndarray   # [B, max_pages] int32
     num_pages: int
     q_idx: np.ndarray         # [B,T,HI,DI] uint16 (bf16) | uint8 (e4m3)
-    q_scale: np.ndarray | None  # [B,T,HI] f32 (fp8 only)
+    q_scale: np.ndarray | None  # [B,T,HI] f32 (fp8) | [B,T,HI,DI/32] uint8 E8M0 (mxfp8)
     w: np.ndarray             # [B,T,HI] f32
     k_cache: np.ndarray       # [P,PAGE,DI] uint16 | uint8
-    k_scale: np.ndarray | None  # [P] f32 (fp8 only)
+    k_scale: np.ndarray | None  # [P] f32 (fp8) | [P,PAGE,DI/32] uint8 E8M0 (mxfp8)
     q_attn: np.ndarray        # [B,T,H,DQK] uint16
     kv_cache: np.ndarray      # [P,PAGE,DQK] uint16
 
@@ -113,6 +115,12 @@ def config(cfg_id: int, size: str = "full", variant: int = 0) -> CaseSpec:
                             idx_dtype="fp8", variant=variant)
         return CaseSpec("cfg4s_decode_B2_fp8", 4, 2, 1, (3000, 4545), 64, 128, 2048, 128,
                         idx_dtype="fp8", variant=variant)
+    if cfg_id == 6:   # long-context decode, MXFP8 indexer (the fp8 workload's shape)
+        if full:
+            return CaseSpec("mx_decode_B8_L131072_mxfp8", 6, 8, 1, (131072,) * 8, 64, 128, 2048, 128,
+                            idx_dtype="mxfp8", variant=variant)
+        return CaseSpec("mxs_decode_B2_mxfp8", 6, 2, 1, (3000, 4545), 64, 128, 2048, 128,
+                        idx_dtype="mxfp8", variant=variant)
     if cfg_id == 5:   # speculative verify: 4 causal drafts per sequence
         if full:
             return CaseSpec("cfg5_verify_B16_T4_L65536", 5, 16, 4, (65536,) * 16, 64, 128, 2048, 128,
@@ -128,6 +136,21 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+def f32_to_mxfp8(x: np.ndarray) -> tuple:
+    """Quantise the last axis (a multiple of 32) to MXFP8 as the OCP Microscaling format defines it:
+    each run of 32 elements shares the E8M0 exponent floor(log2(amax)) - 8 (8 = the largest E4M3
+    exponent), clamped to the E8M0 range; elements are x / scale rounded to E4M3 (RNE, saturated).
+    Returns (codes uint8, scale bytes uint8 with the last axis divided by 32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // MX_GROUP, MX_GROUP)
+    amax = np.abs(g).max(axis=-1)
+    e = np.where(amax > 0, np.floor(np.log2(np.maximum(amax, 1e-38))) - 8, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    scaled = (g.astype(np.float64) / np.ldexp(1.0, e)[..., None]).astype(np.float32)
+    codes = f32_to_e4m3_codes(scaled).reshape(x.shape)
+    return codes, (e + 127).astype(np.uint8)
 
 
 def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
@@ -263,11 +286,35 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
         if poison:
             k_cache = k_cache.copy()
             k_cache[~valid] = E4M3_NAN
+    elif spec.idx_dtype == "mxfp8":
+        if DI % MX_GROUP:
+            raise ValueError("MXFP8 rows need a multiple of 32 elements")
+        G = DI // MX_GROUP
+        if v == "mxgrid":
+            # integer codes in [-2, 2] (exact in e4m3), q scales 2^-2..2^0, k scales 2^-1..2^1,
+            # w multiples of 1/16 in [0, 1]: every fp32 partial sum of a 64 x 128 score is a
+            # multiple of 2^-7 below 2^16, so exact in any order
+            q_idx = f32_to_e4m3_codes(rngq.integers(-2, 2, size=(B, T, HI, DI), endpoint=True))
+            k_cache = f32_to_e4m3_codes(rngk.integers(-2, 2, size=(P, PAGE, DI), endpoint=True))
+            q_scale = (127 + rngq.integers(-2, 0, size=(B, T, HI, G), endpoint=True)).astype(np.uint8)
+            k_scale = (127 + rngk.integers(-1, 1, size=(P, PAGE, G), endpoint=True)).astype(np.uint8)
+            w = (rngw.integers(0, 16, size=(B, T, HI), endpoint=True) / 16.0).astype(np.float32)
+        else:
+            qf = _normal_f32(key0 + [2], B * T * HI * DI, 1.0 / np.sqrt(DI)).reshape(B, T, HI, DI)
+            q_idx, q_scale = f32_to_mxfp8(qf)
+            kf = _normal_f32(key0 + [3], P * PAGE * DI, 1.0 / np.sqrt(DI)).reshape(P, PAGE, DI)
+            k_cache, k_scale = f32_to_mxfp8(kf)
+            w = _normal_f32(key0 + [4], B * T * HI, 1.0 / np.sqrt(64.0)).reshape(B, T, HI)
+        if poison:
+            k_cache = k_cache.copy()
+            k_cache[~valid] = E4M3_NAN
+            k_scale = k_scale.copy()
+            k_scale[~valid] = E8M0_NAN
     else:
         raise ValueError(spec.idx_dtype)
 
     # ---- attention q / kv
-    if v in ("grid", "grid8", "ties", "ties2", "narrow", "fp8grid"):
+    if v in ("grid", "grid8", "ties", "ties2", "narrow", "fp8grid", "mxgrid"):
         q_attn = _grid_bf16(rngs, (B, T, H, DQK))
         kv_cache = _grid_bf16(rngv, (P, PAGE, DQK))
     elif v == "sharp":
