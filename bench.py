@@ -46,14 +46,16 @@ def visible(spec, seq_lens):
 
 def algorithmic_bytes(spec, seq_lens):
     """Bytes the method must move per step (no over-fetch, no scratch): see the design doc."""
-    elt = 1 if spec.idx_dtype == "fp8" else 2
+    fp8, mx = spec.idx_dtype == "fp8", spec.idx_dtype == "mxfp8"
+    elt = 1 if (fp8 or mx) else 2
+    mxs = spec.DI // 32 if mx else 0      # MXFP8: one E8M0 byte per 32 elements
     rows = visible(spec, seq_lens)
     k_bytes = 0
     for b in range(spec.B):
         n = int(seq_lens[b])              # keys read once per sequence, shared by its T queries
         pages = (n + 63) // 64
-        k_bytes += n * spec.DI * elt + pages * 4 + (pages * 4 if elt == 1 else 0)
-    q_idx = spec.B * spec.T * spec.HI * (spec.DI * elt + 4 + (4 if elt == 1 else 0))
+        k_bytes += n * (spec.DI * elt + mxs) + pages * 4 + (pages * 4 if fp8 else 0)
+    q_idx = spec.B * spec.T * spec.HI * (spec.DI * elt + mxs + 4 + (4 if fp8 else 0))
     li_score = k_bytes + q_idx
     idx_rw = 2 * spec.B * spec.T * spec.K * 4
     kp = sum(min(spec.K, n) for _, _, n in rows)
@@ -84,7 +86,7 @@ def recorded_traffic(kernel, workload):
 def describe(spec):
     lens = np.asarray(spec.lens)
     kind = {1: "decode", 2: "decode", 3: "causal prefill", 4: "decode, fp8 indexer",
-            5: "speculative verify"}.get(spec.cfg_id, "custom")
+            5: "speculative verify", 6: "decode, MXFP8 indexer"}.get(spec.cfg_id, "custom")
     return (f"{kind}: B={spec.B} T={spec.T} ctx " +
             (f"{lens.min()}..{lens.max()} (mean {lens.mean():.0f})" if lens.min() != lens.max() else f"{lens[0]}")
             + f", K={spec.K}, indexer {spec.HI}x{spec.DI} {spec.idx_dtype}, attention {spec.H} heads 576/512 bf16, page 64")
@@ -100,7 +102,7 @@ def cpu_baseline(case, max_rows: int, budget_s: float, min_s: float = 10.0):
         cores = 1
     spec = case.spec
     rows = [(b, t) for b in range(spec.B) for t in range(spec.T)]
-    dt = "fp8" if spec.idx_dtype == "fp8" else "bf16"
+    dt = spec.idx_dtype
     # passes over the first rows of the batch until about min_s of CPU time (at most budget_s)
     sample = rows[:max_rows]
     done, passes, t0 = 0, 0, time.perf_counter()
@@ -128,7 +130,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, help="named workload 1..5 (default 2)")
+    ap.add_argument("--workload", type=int, default=2,
+                    help="named workload 1..5 (default 2); 6 = workload 4 with an MXFP8 indexer")
     ap.add_argument("--rotate-gib", type=float, default=2.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32)
@@ -173,6 +176,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     fp8 = spec.idx_dtype == "fp8"
+    mx = spec.idx_dtype == "mxfp8"
     base = dict(q=up(case.q_idx), w=up(case.w), k=up(case.k_cache),
                 qs=None if case.q_scale is None else up(case.q_scale),
                 ks=None if case.k_scale is None else up(case.k_scale),
@@ -182,7 +186,8 @@ def main():
     log(f"uploaded {R} rotation copies ({ab['step'] * R / 2 ** 30:.2f} GiB of touched bytes)")
 
     layout = dsa.make_layout(bt, sl, case.num_pages, spec.max_len)
-    ishape = dsa.IndexerShape(spec.T, spec.HI, spec.DI, spec.K, dsa.DSA_FP8_E4M3 if fp8 else dsa.DSA_BF16)
+    ishape = dsa.IndexerShape(spec.T, spec.HI, spec.DI, spec.K,
+                              dsa.DSA_MXFP8_E4M3 if mx else (dsa.DSA_FP8_E4M3 if fp8 else dsa.DSA_BF16))
     ashape = dsa.AttnShape(spec.T, spec.H, 576, 512, spec.K, spec.sm_scale)
     iws = torch.empty(max(256, dsa.dsa_indexer_workspace_size(layout, ishape)), dtype=torch.uint8, device=dev)
     aws_n = dsa.dsa_sparse_attn_workspace_size(layout, ashape)
@@ -266,7 +271,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8+bf16" if fp8 else "bf16",
+        "dtype": "mxfp8+bf16" if mx else ("fp8+bf16" if fp8 else "bf16"),
         "data": "synthetic",
         "config": {"workload": describe(spec), "batch": spec.B, "query_tokens": spec.T,
                    "ctx_min": int(lens.min()), "ctx_max": int(lens.max()), "ctx_mean": float(lens.mean()),

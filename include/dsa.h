@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DSA_VERSION 1
+#define DSA_VERSION 2
 #define DSA_PAGE_SIZE 64          /* tokens per cache page */
 #define DSA_DIM_QK 576            /* MLA latent row: 512 "nope" + 64 rope columns */
 #define DSA_DIM_V 512             /* V = the first 512 columns of the latent row */
@@ -56,7 +56,11 @@ typedef enum {
 
 typedef enum {
   DSA_BF16 = 0,              /* bfloat16 */
-  DSA_FP8_E4M3 = 1           /* OCP E4M3FN (max 448, no infinities) */
+  DSA_FP8_E4M3 = 1,          /* OCP E4M3FN (max 448, no infinities), fp32 scale per q head and
+                                per K page */
+  DSA_MXFP8_E4M3 = 2         /* MXFP8 (OCP Microscaling): E4M3FN codes, one E8M0 scale byte
+                                2^(e - 127) per 32 consecutive elements of each q head row and
+                                each cached key row ([P1] §4, [P3] §3.3); indexer decode only */
 } dsa_dtype;
 
 /* Geometry of the paged caches ([P1] §2 "on-demand in-page addressing"; [P3] §3.1, the paged K
@@ -82,7 +86,8 @@ typedef struct {
   int32_t heads;                /* indexer heads H_I: 8, 16, 32 or 64 */
   int32_t dim;                  /* indexer head dim d_I: 64 or 128 */
   int32_t top_k;                /* K, 1..DSA_MAX_TOP_K */
-  dsa_dtype dtype;              /* storage of q and the indexer-K cache */
+  dsa_dtype dtype;              /* storage of q and the indexer-K cache (DSA_MXFP8_E4M3: T = 1
+                                   and batch <= 512 only, else DSA_ERR_UNSUPPORTED) */
 } dsa_indexer_shape;
 
 typedef struct {
@@ -103,21 +108,27 @@ size_t dsa_indexer_workspace_size(const dsa_paged_layout *layout, const dsa_inde
  *
  * For every query row (b, t) it computes, for each visible key s (0 <= s <= pos),
  *     I[s] = sum_h w[b,t,h] * max(0, q[b,t,h,:] . k[s,:])
- * (fp8: q = q_scale[b,t,h] * e4m3(q code), k = k_scale[page of s] * e4m3(k code)), keeps the
+ * (fp8: q = q_scale[b,t,h] * e4m3(q code), k = k_scale[page of s] * e4m3(k code); MXFP8:
+ * q[d] = 2^(q_scale[b,t,h,d/32] - 127) * e4m3(q code[d]) and k[d] likewise with the key's own
+ * scale bytes k_scale[page of s, slot of s, d/32]), keeps the
  * K' = min(top_k, pos + 1) largest scores with ties going to the lower position, and writes
  * those positions in ascending order followed by -1 up to top_k.  Scores are accumulated in fp32.
  *
  *   q        [batch, T, heads, dim]  bf16 or e4m3, 16-byte aligned
- *   q_scale  [batch, T, heads] fp32 > 0 for DSA_FP8_E4M3, else must be NULL; 4-byte aligned
+ *   q_scale  DSA_FP8_E4M3: [batch, T, heads] fp32 > 0, 4-byte aligned;
+ *            DSA_MXFP8_E4M3: [batch, T, heads, dim / 32] uint8 E8M0 exponents (255 = NaN);
+ *            bf16: must be NULL
  *   w        [batch, T, heads] fp32 head weights, 4-byte aligned
  *   k_cache  [num_pages, page_size, dim] bf16 or e4m3 (same dtype as q), 16-byte aligned
- *   k_scale  [num_pages] fp32 > 0, one per page, for DSA_FP8_E4M3, else must be NULL
+ *   k_scale  DSA_FP8_E4M3: [num_pages] fp32 > 0, one per page, 4-byte aligned;
+ *            DSA_MXFP8_E4M3: [num_pages, page_size, dim / 32] uint8 E8M0 exponents, 16-byte
+ *            aligned; bf16: must be NULL
  *   idx_out  [batch, T, top_k] int32 logical positions, ascending, -1 padded; 4-byte aligned
  *   workspace / workspace_bytes: device scratch, 256-byte aligned, at least
  *            dsa_indexer_workspace_size() bytes; contents on entry are ignored.
  */
-dsa_status dsa_indexer_topk(const void *q, const float *q_scale, const float *w,
-                            const void *k_cache, const float *k_scale,
+dsa_status dsa_indexer_topk(const void *q, const void *q_scale, const float *w,
+                            const void *k_cache, const void *k_scale,
                             const dsa_paged_layout *layout, const dsa_indexer_shape *shape,
                             int32_t *idx_out, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);

@@ -4,7 +4,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of include/ds
 built in-tree by sparse_attention_15_amd.build).  This package only marshals torch tensors into
 that ABI; it has no fallback path.
 """
-from ._lib import (DSA_BF16, DSA_FP8_E4M3, AttnShape, DsaError, IndexerShape, Layout,  # noqa: F401
+from ._lib import (DSA_BF16, DSA_FP8_E4M3, DSA_MXFP8_E4M3, AttnShape, DsaError, IndexerShape, Layout,  # noqa: F401
                    dsa_debug_status, dsa_indexer_topk, dsa_indexer_workspace_size, dsa_profile_start,
                    dsa_profile_stop, dsa_sparse_attn, dsa_sparse_attn_workspace_size, lib,
                    make_layout)

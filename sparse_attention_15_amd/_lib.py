@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libdsa.so")
 DSA_OK = 0
 DSA_BF16 = 0
 DSA_FP8_E4M3 = 1
+DSA_MXFP8_E4M3 = 2
 PAGE_SIZE = 64
 DIM_QK = 576
 DIM_V = 512
@@ -130,15 +131,16 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def dsa_indexer_topk(q, q_scale, w, k_cache, k_scale, block_table, seq_lens, *, T: int, top_k: int,
                      num_pages: int | None = None, max_seq_len: int, fp8: bool = False,
-                     idx_out=None, workspace=None, stream=None) -> torch.Tensor:
+                     mx: bool = False, idx_out=None, workspace=None, stream=None) -> torch.Tensor:
     """Lightning Indexer + Top-K.  q [B,T,HI,DI] (bf16 or uint8 e4m3 codes), w [B,T,HI] fp32,
     k_cache [P,64,DI], block_table [B,max_pages] int32, seq_lens [B] int32 (device tensors).
-    Returns idx_out [B,T,top_k] int32."""
+    fp8: fp32 scales q_scale [B,T,HI] and k_scale [P]; mx (MXFP8): uint8 E8M0 scales
+    q_scale [B,T,HI,DI/32] and k_scale [P,64,DI/32].  Returns idx_out [B,T,top_k] int32."""
     B, Tq, HI, DI = q.shape
     assert Tq == T
     P = k_cache.shape[0] if num_pages is None else num_pages
     layout = make_layout(block_table, seq_lens, P, max_seq_len)
-    shape = IndexerShape(T, HI, DI, top_k, DSA_FP8_E4M3 if fp8 else DSA_BF16)
+    shape = IndexerShape(T, HI, DI, top_k, DSA_MXFP8_E4M3 if mx else (DSA_FP8_E4M3 if fp8 else DSA_BF16))
     if idx_out is None:
         idx_out = torch.empty((B, T, top_k), dtype=torch.int32, device=q.device)
     need = dsa_indexer_workspace_size(layout, shape)

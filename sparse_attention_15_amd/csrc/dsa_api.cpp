@@ -48,7 +48,8 @@ dsa_status check_indexer_shape(const dsa_indexer_shape* S) {
   if (S->T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", S->T);
   if (S->top_k < 1 || S->top_k > DSA_MAX_TOP_K)
     return fail(DSA_ERR_UNSUPPORTED, "top_k %d outside 1..%d", S->top_k, DSA_MAX_TOP_K);
-  if (S->dtype != DSA_BF16 && S->dtype != DSA_FP8_E4M3) return fail(DSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)S->dtype);
+  if (S->dtype != DSA_BF16 && S->dtype != DSA_FP8_E4M3 && S->dtype != DSA_MXFP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "unknown dtype %d", (int)S->dtype);
   if (!dsa::indexer_supported(S->heads, S->dim))
     return fail(DSA_ERR_UNSUPPORTED, "indexer heads %d x dim %d unsupported (heads 8/16/32/64, dim 64/128)", S->heads, S->dim);
   return DSA_OK;
@@ -96,23 +97,28 @@ size_t dsa_indexer_workspace_size(const dsa_paged_layout* layout, const dsa_inde
   return dsa::plan_indexer(*layout, *shape).total;
 }
 
-dsa_status dsa_indexer_topk(const void* q, const float* q_scale, const float* w, const void* k_cache,
-                            const float* k_scale, const dsa_paged_layout* layout,
+dsa_status dsa_indexer_topk(const void* q, const void* q_scale, const float* w, const void* k_cache,
+                            const void* k_scale, const dsa_paged_layout* layout,
                             const dsa_indexer_shape* shape, int32_t* idx_out, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   dsa_status st = check_indexer_shape(shape);
   if (st != DSA_OK) return st;
   if ((st = check_layout(layout, shape->T)) != DSA_OK) return st;
   const bool fp8 = shape->dtype == DSA_FP8_E4M3;
+  const bool mx = shape->dtype == DSA_MXFP8_E4M3;
   if (q == nullptr || w == nullptr || k_cache == nullptr || idx_out == nullptr)
     return fail(DSA_ERR_NULL, "q / w / k_cache / idx_out is NULL");
-  if (fp8 && (q_scale == nullptr || k_scale == nullptr))
-    return fail(DSA_ERR_NULL, "fp8 indexer needs q_scale and k_scale");
-  if (!fp8 && (q_scale != nullptr || k_scale != nullptr))
+  if ((fp8 || mx) && (q_scale == nullptr || k_scale == nullptr))
+    return fail(DSA_ERR_NULL, "fp8 and MXFP8 indexers need q_scale and k_scale");
+  if (!fp8 && !mx && (q_scale != nullptr || k_scale != nullptr))
     return fail(DSA_ERR_SHAPE, "q_scale / k_scale must be NULL for the bf16 indexer");
+  if (mx && !dsa::indexer_mx_supported(layout->batch, shape->T))
+    return fail(DSA_ERR_UNSUPPORTED, "the MXFP8 indexer runs decode only (T = 1, batch <= 512); got T %d, batch %d",
+                shape->T, layout->batch);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(w, 4) || !aligned(idx_out, 4) ||
-      (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4))))
-    return fail(DSA_ERR_ALIGN, "q / k_cache need 16-byte alignment, w / scales / idx_out 4-byte");
+      (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4))) || (mx && !aligned(k_scale, 16)))
+    return fail(DSA_ERR_ALIGN, "q / k_cache need 16-byte alignment, w / idx_out 4-byte, fp8 scales 4-byte, "
+                "MXFP8 k_scale 16-byte");
   const dsa::IndexerPlan plan = dsa::plan_indexer(*layout, *shape);
   if (workspace == nullptr || workspace_bytes < plan.total)
     return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total);
@@ -123,7 +129,7 @@ dsa_status dsa_indexer_topk(const void* q, const float* q_scale, const float* w,
   a.block_table = layout->block_table; a.seq_lens = layout->seq_lens;
   a.B = layout->batch; a.T = shape->T; a.max_pages = layout->max_pages; a.num_pages = layout->num_pages;
   a.max_seq_len = layout->max_seq_len;
-  a.heads = shape->heads; a.dim = shape->dim; a.top_k = shape->top_k; a.fp8 = fp8;
+  a.heads = shape->heads; a.dim = shape->dim; a.top_k = shape->top_k; a.fp8 = fp8; a.mx = mx;
   a.idx_out = idx_out; a.workspace = workspace;
   const hipError_t e = dsa::launch_indexer(a, plan, stream);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "indexer launch: %s", hipGetErrorString(e));

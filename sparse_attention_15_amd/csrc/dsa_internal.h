@@ -35,14 +35,15 @@ struct IndexerPlan {
 
 struct IndexerArgs {
   const void* q;
-  const float* q_scale;
+  const void* q_scale;    // fp32 per head (fp8) or E8M0 bytes per 32 elements (MXFP8)
   const float* w;
   const void* k_cache;
-  const float* k_scale;
+  const void* k_scale;    // fp32 per page (fp8) or E8M0 bytes per 32 elements (MXFP8)
   const int32_t* block_table;
   const int32_t* seq_lens;
   int B, T, max_pages, num_pages, max_seq_len, heads, dim, top_k;
-  bool fp8;
+  bool fp8;              // E4M3 with fp32 per-head / per-page scales
+  bool mx;               // MXFP8: E4M3 with E8M0 scales per 32 elements
   int32_t* idx_out;
   void* workspace;
 };
@@ -53,6 +54,7 @@ hipError_t attn_take_input_flags(uint32_t* flags);
 
 IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S);
 bool indexer_supported(int heads, int dim);
+bool indexer_mx_supported(int batch, int T);   // the MXFP8 indexer runs the decode path only
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t stream);
 
 struct AttnPlan {

@@ -23,6 +23,7 @@
 //                   lowest-position ties up to the quota, and merges both lists into idx_out.
 // A row with n <= K selects every visible position and skips the score scratch.
 #include <algorithm>
+#include <type_traits>
 
 #include "dsa_device.h"
 #include "dsa_internal.h"
@@ -46,6 +47,30 @@ __global__ __launch_bounds__(256) void li_zero_hist(uint32_t* __restrict__ hist,
 // integer, a negative one as a negative integer (avoids the NaN-quieting fmaxf expansion).
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// MXFP8 operands (OCP Microscaling: E4M3 elements, one E8M0 scale 2^(e - 127) per 32 consecutive
+// elements) are dequantised to bf16 in registers and multiplied on the bf16 MFMA: an E4M3 value
+// times a power of two has at most 4 significant bits, so its bf16 form is exact while it stays
+// within the fp32 exponent range.
+typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  if (e == 0xFFu) return __uint_as_float(0x7FC00000u);   // NaN
+  return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
+}
+__device__ __forceinline__ uint32_t mx_pack(mx_f32x2 v, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mx_f32x2){v.x * s, v.y * s}, mx_bf16x2));
+}
+// Eight E4M3 codes (byte i = element i) times scale s, as eight bf16.
+__device__ __forceinline__ bf16x8 mx_to_bf16x8(long codes, float s) {
+  const int lo = (int)(uint32_t)codes, hi = (int)(uint32_t)((unsigned long)codes >> 32);
+  u32x4 v;
+  v[0] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(lo, false), s);
+  v[1] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(lo, true), s);
+  v[2] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(hi, false), s);
+  v[3] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(hi, true), s);
+  return as_bf16x8(v);
+}
+
 // ------------------------------------------------------------------------------------------------
 struct ScoreArgs {
   const unsigned char* q;       // [B,T,HI,DI] bf16 | e4m3
@@ -57,6 +82,8 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   uint32_t* keys;               // [rows, row_stride]
   uint32_t* hist;               // [rows, kBins]
+  const unsigned char* q_e8;    // MXFP8: [B,T,HI,DI/32] E8M0 scale bytes of q
+  const unsigned char* k_e8;    // MXFP8: [P,64,DI/32] E8M0 scale bytes of the K cache
   int B, T, max_pages, num_pages, K, n_chunks, n_qtiles, row_stride, max_seq_len;
 };
 
@@ -524,14 +551,20 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 // the shared row histogram and load the next query.
 constexpr int kDecodeMaxItems = 256;   // tiles per decode workgroup (the grid is sized for it)
 
-template <int HI, int DI, bool FP8>
+// MX: MXFP8 operands (FP8 storage, one E8M0 scale per 32 elements, bf16 MFMA after dequantising).
+template <int HI, int DI, bool FP8, bool MX = false>
 __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
+  static_assert(!MX || (FP8 && DI % 32 == 0), "MXFP8 keeps E4M3 codes, 32 elements per scale");
   using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles, 4 waves x 32 keys
-  typedef typename AFrag<FP8>::T frag_t;
+  typedef std::conditional_t<MX, bf16x8, typename AFrag<FP8>::T> frag_t;
   constexpr int BLK = 32 * C::ROWB;                // one wave's block (bytes)
-  constexpr int NLD = BLK / 1024;                  // wave-wide loads per block
+  constexpr int NG = DI / 32;                      // MX: scale bytes per key row
+  constexpr int SB = 32 * NG;                      // MX: scale bytes per block
+  // wave-wide loads per block: the code rows, plus (MX) one for the block's scale bytes
+  constexpr int NLD = BLK / 1024 + (MX ? 1 : 0);
   constexpr int KPL = 1024 / C::ROWB;              // keys per load
   static_assert(NLD >= 1 && KPL * C::CPK == 64 && C::KT / kPage == 2, "block shape");
+  static_assert(SB % 16 == 0 && SB / 16 <= 64, "scale bytes of a block: one 16-byte load per lane");
   // ring slots per wave: 64 KiB of ring per workgroup either way (two workgroups per CU)
   constexpr int NSLOT = FP8 ? 4 : 2;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][NSLOT][BLK];
@@ -539,7 +572,8 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   // per tile of this workgroup: sequence | tile index << 9, the physical pages of its two halves
   // (-1 past the sequence end), and the sequence's visible length
   __shared__ int4 lds_rec[kDecodeMaxItems];
-  __shared__ float2 lds_rsc[FP8 ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
+  __shared__ float2 lds_rsc[FP8 && !MX ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? 4 : 1][MX ? NSLOT : 1][MX ? SB : 16];
   __shared__ uint32_t sh[8];
   // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
   static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
@@ -593,10 +627,13 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       for (int kk = 0; kk < C::KS; ++kk) {
         if (head < HI) {
           const unsigned char* src = a.q + (((size_t)b * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
-          if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
+          if constexpr (MX)
+            afrag[m][kk] = mx_to_bf16x8(*reinterpret_cast<const long*>(src),
+                                        e8m0_value(a.q_e8[((size_t)b * HI + head) * NG + kk / 2]));
+          else if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
           else afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
         } else {
-          if constexpr (FP8) afrag[m][kk] = 0;
+          if constexpr (FP8 && !MX) afrag[m][kk] = 0;
           else afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
         }
       }
@@ -606,7 +643,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
         float wv = 0.f;
         if (hd < HI) {
           wv = a.w[(size_t)b * HI + hd];
-          if constexpr (FP8) wv *= a.q_scale[(size_t)b * HI + hd];
+          if constexpr (FP8 && !MX) wv *= a.q_scale[(size_t)b * HI + hd];
         }
         wreg[m][r] = wv;
       }
@@ -637,7 +674,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     }
     lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
     // fp8 page scales: loaded now, stored to LDS once the first gathers are in flight
-    if constexpr (FP8) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
+    if constexpr (FP8 && !MX) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
 
@@ -653,10 +690,15 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     const int phys = pg < 0 ? 0 : pg;
     const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (wave & 1)) * C::ROWB;
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) {
+    for (int u = 0; u < BLK / 1024; ++u) {
       const int key = KPL * u + lane / C::CPK;
       const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
       lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), lds_k[wave][slot] + 1024 * u);
+    }
+    if constexpr (MX) {
+      // the block's scale bytes (key-major, NG per key) are contiguous in the scale pool
+      if (lane < SB / 16)
+        lds_dma16(a.k_e8 + ((size_t)phys * kPage + 32 * (wave & 1)) * NG + 16 * lane, lds_kx[wave][slot]);
     }
   };
 #pragma unroll
@@ -665,7 +707,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
   // so no wait for them lands in the main loop (it also covers the first blocks)
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  if constexpr (FP8) {
+  if constexpr (FP8 && !MX) {
     static_assert(kDecodeMaxItems <= kThreads, "one record per thread");
     if (tid < n_items) lds_rsc[tid] = my_sc;
     lds_barrier();
@@ -692,7 +734,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       b_cur = b;
     }
     float kscale = 1.f;
-    if constexpr (FP8) {
+    if constexpr (FP8 && !MX) {
       const float2 sc = lds_rsc[i];
       kscale = wave < 2 ? sc.x : sc.y;
     }
@@ -700,7 +742,11 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     frag_t bfr[C::KS];
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
-      if constexpr (FP8)
+      if constexpr (MX)
+        bfr[kk] = mx_to_bf16x8(
+            *reinterpret_cast<const long*>(blk + nl * C::ROWB + 16 * (kk ^ (nl & (C::CPK - 1))) + 8 * hh),
+            e8m0_value(lds_kx[wave][slot][nl * NG + kk / 2]));
+      else if constexpr (FP8)
         bfr[kk] = *reinterpret_cast<const long*>(blk + nl * C::ROWB + 16 * (kk ^ (nl & (C::CPK - 1))) + 8 * hh);
       else
         bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blk + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
@@ -714,7 +760,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
       for (int m = 0; m < C::MB; ++m) {
-        if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+        if constexpr (FP8 && !MX) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
         else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
       }
     // the slot's reads are complete (the MFMAs consumed them): refill it
@@ -725,7 +771,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
     part = xor32_sum(part);
-    if constexpr (FP8) part *= kscale;
+    if constexpr (FP8 && !MX) part *= kscale;
     const int s = j * C::KT + 32 * wave + nl;
     if (hh == 0 && s < n_me) {
       const uint32_t key = float_key(part);
@@ -1142,7 +1188,13 @@ bool indexer_supported(int heads, int dim) {
 }
 
 template <int HI, int DI, bool FP8>
-static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, hipStream_t st) {
+static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, bool mx, hipStream_t st) {
+  if constexpr (FP8) {
+    if (mx) {   // MXFP8: decode only (the host checks persist && tq == 1)
+      hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      return;
+    }
+  }
   if (persist) {
     if (tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, FP8>), dim3(grid), dim3(kThreads), 0, st, s);
     else if (tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
@@ -1155,10 +1207,12 @@ static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, hip
 }
 
 template <int HI, int DI>
-static void launch_score_dt(const ScoreArgs& s, bool fp8, int tq, int grid, bool persist, hipStream_t st) {
-  if (fp8) launch_score<HI, DI, true>(s, tq, grid, persist, st);
-  else launch_score<HI, DI, false>(s, tq, grid, persist, st);
+static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int grid, bool persist, hipStream_t st) {
+  if (fp8 || mx) launch_score<HI, DI, true>(s, tq, grid, persist, mx, st);
+  else launch_score<HI, DI, false>(s, tq, grid, persist, false, st);
 }
+
+bool indexer_mx_supported(int batch, int T) { return T == 1 && batch <= kMaxSeqPersist; }
 
 // Compute units of the current device (cached per device).
 static int device_cus() {
@@ -1185,10 +1239,12 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
 
   ScoreArgs s;
   s.q = static_cast<const unsigned char*>(a.q);
-  s.q_scale = a.q_scale;
+  s.q_scale = a.fp8 ? static_cast<const float*>(a.q_scale) : nullptr;
   s.w = a.w;
   s.kc = static_cast<const unsigned char*>(a.k_cache);
-  s.k_scale = a.k_scale;
+  s.k_scale = a.fp8 ? static_cast<const float*>(a.k_scale) : nullptr;
+  s.q_e8 = a.mx ? static_cast<const unsigned char*>(a.q_scale) : nullptr;
+  s.k_e8 = a.mx ? static_cast<const unsigned char*>(a.k_scale) : nullptr;
   s.block_table = a.block_table;
   s.seq_lens = a.seq_lens;
   s.keys = reinterpret_cast<uint32_t*>(ws + p.off_keys);
@@ -1210,14 +1266,14 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   if (grid > 0) {
     LaunchScope ls("li_score", st);
     switch (a.heads * 1000 + a.dim) {
-      case 8064: launch_score_dt<8, 64>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 8128: launch_score_dt<8, 128>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 16064: launch_score_dt<16, 64>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 16128: launch_score_dt<16, 128>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 32064: launch_score_dt<32, 64>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 32128: launch_score_dt<32, 128>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 64064: launch_score_dt<64, 64>(s, a.fp8, p.tq, grid, persist, st); break;
-      case 64128: launch_score_dt<64, 128>(s, a.fp8, p.tq, grid, persist, st); break;
+      case 8064: launch_score_dt<8, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 8128: launch_score_dt<8, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 16064: launch_score_dt<16, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 16128: launch_score_dt<16, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 32064: launch_score_dt<32, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 32128: launch_score_dt<32, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 64064: launch_score_dt<64, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 64128: launch_score_dt<64, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
       default: return hipErrorInvalidValue;
     }
   }

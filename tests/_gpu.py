@@ -45,12 +45,13 @@ class Dev:
         self.q_attn = up(c.q_attn)
         self.kv = up(c.kv_cache)
         self.fp8 = s.idx_dtype == "fp8"
+        self.mx = s.idx_dtype == "mxfp8"
 
     def indexer(self, **kw) -> torch.Tensor:
         s = self.c.spec
         return dsa.dsa_indexer_topk(self.q_idx, self.q_scale, self.w, self.k, self.k_scale, self.bt,
                                     self.sl, T=s.T, top_k=s.K, max_seq_len=s.max_len, fp8=self.fp8,
-                                    num_pages=self.c.num_pages, **kw)
+                                    mx=self.mx, num_pages=self.c.num_pages, **kw)
 
     def attn(self, idx, **kw):
         s = self.c.spec

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert dsa.lib().dsa_version() == 1
+    assert dsa.lib().dsa_version() == 2
 
 
 def _layout(B=2, max_pages=4, max_len=256, num_pages=9, page=64):
@@ -82,6 +82,10 @@ def _attn_call(q=FAKE, kv=FAKE, idx=FAKE, layout=None, shape=None, out=FAKE, lse
     (dict(shape=_ishape(H=12)), 4), (dict(shape=_ishape(D=96)), 4), (dict(shape=_ishape(K=0)), 4),
     (dict(shape=_ishape(K=4096)), 4), (dict(shape=_ishape(T=0)), 2),
     (dict(shape=_ishape(dt=1)), 1),                       # fp8 without scales
+    (dict(shape=_ishape(dt=2)), 1),                       # MXFP8 without scales
+    (dict(shape=_ishape(dt=2, T=2), qs=FAKE, ks=FAKE), 4),   # MXFP8 runs decode only
+    (dict(shape=_ishape(dt=2), qs=FAKE, ks=FAKE + 4), 3),    # MXFP8 k scales need 16 bytes
+    (dict(shape=_ishape(dt=3)), 4),                       # unknown dtype
     (dict(qs=FAKE, ks=FAKE), 2),                          # scales given for bf16
     (dict(layout=_layout(page=128)), 4), (dict(layout=_layout(B=0)), 2),
     (dict(layout=_layout(max_pages=2, max_len=256)), 2),  # table too short for max_len

@@ -1,0 +1,70 @@
+"""GPU parity of the MXFP8 indexer ("Inference Optimization for Kimi K3.1 Pro", §4: the Lightning
+Indexer's Q and K in MXFP8) through the C ABI, against the CPU oracle.
+
+The exact integer-grid variant (codes in [-2, 2], power-of-two group scales, weights in sixteenths)
+makes every fp32 partial sum exact, so its indices must match the oracle bit for bit; it runs at
+both indexer head dims, which place 4 and 2 scale bytes per key.  The Gaussian cases (rows
+quantised to MXFP8 as the OCP Microscaling format defines it) use the near-tie band.  Sizes span
+several 128-key tiles, score workgroups and select scan steps, with ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests._gpu import Dev, check_attn, check_indices_band, oracle_args, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(spec, exact, check_sfa=False, case=None):
+    print(f"[case] {spec.name} B={spec.B} lens={spec.lens[:4]} HI={spec.HI} DI={spec.DI} K={spec.K} "
+          f"{spec.idx_dtype}/{spec.values}", flush=True)
+    c = case if case is not None else W.make_case(spec)
+    d = Dev(c)
+    idx_t = d.indexer()
+    torch.cuda.synchronize()
+    idx = to_np(idx_t)
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=spec.K, dtype="mxfp8",
+                                         return_scores=True)
+    if exact:
+        bad = np.nonzero((idx != ref).any(axis=-1))
+        assert np.array_equal(idx, ref), f"index mismatch in rows {list(zip(*bad))[:5]}"
+    else:
+        check_indices_band(idx, ref, extra, spec.K, c.seq_lens, 1)
+    if check_sfa:
+        out, lse = d.attn(idx_t)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
+                                              spec.sm_scale)
+        check_attn(to_np(out), to_np(lse), o_ref, l_ref)
+    return c, idx
+
+
+@pytest.mark.parametrize("HI,DI,K,lens", [(64, 128, 2048, (3000, 5000, 4545)),
+                                          (8, 64, 256, (4096, 1000)),
+                                          (32, 64, 300, (2100, 777))])
+def test_mx_grid_exact(HI, DI, K, lens):
+    spec = W.custom("mxgrid", len(lens), 1, lens, HI, DI, K, 16, idx_dtype="mxfp8", values="mxgrid")
+    _run(spec, exact=True)
+
+
+def test_mx_small_gaussian_decode():
+    _run(W.config(6, "small"), exact=False, check_sfa=True)
+
+
+def test_mx_ragged_rows_and_short_rows():
+    # one row shorter than K (all positions), others with partial last pages
+    spec = W.custom("mx_ragged", 4, 1, (1500, 2049, 2113, 6001), 64, 128, 2048, 16, idx_dtype="mxfp8")
+    _run(spec, exact=False)
+
+
+def test_mx_page_permutation_bit_identical():
+    spec = W.custom("mx_perm", 2, 1, (2600, 4100), 64, 128, 2048, 16, idx_dtype="mxfp8")
+    c = W.make_case(spec)
+    c2 = W.permute_pages(c)
+    i1 = to_np(Dev(c).indexer())
+    i2 = to_np(Dev(c2).indexer())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(i1, i2)

@@ -24,8 +24,7 @@ def _run(spec, exact, sfa_rows=None, check_sfa=True):
     idx_t = d.indexer()
     torch.cuda.synchronize()
     idx = to_np(idx_t)
-    dt = "fp8" if spec.idx_dtype == "fp8" else "bf16"
-    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype=dt,
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype=spec.idx_dtype,
                                          return_scores=True)
     if exact:
         bad = np.nonzero((idx != ref).any(axis=-1))
