@@ -48,27 +48,18 @@ __global__ __launch_bounds__(256) void li_zero_hist(uint32_t* __restrict__ hist,
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // MXFP8 operands (OCP Microscaling: E4M3 elements, one E8M0 scale 2^(e - 127) per 32 consecutive
-// elements) are dequantised to bf16 in registers and multiplied on the bf16 MFMA: an E4M3 value
-// times a power of two has at most 4 significant bits, so its bf16 form is exact while it stays
-// within the fp32 exponent range.
-typedef float mx_f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 mx_bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float e8m0_value(uint32_t e) {
-  if (e == 0xFFu) return __uint_as_float(0x7FC00000u);   // NaN
-  return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);   // 2^-127 is subnormal
+// elements) go straight to gfx950's block-scaled MFMA, 32x32x64 with E4M3 A and B.  Its operand
+// lanes (checked on the device): for a 64-element chunk of the dot product, lane r + 32h of A
+// (row r) or B (column r) holds 32 codes, bytes 0-15 in the chunk's first 32-element block and
+// bytes 16-31 in its second; the block's scale comes from byte 0 of the scale operand of lane
+// r + 32 * block.  So lane (r, h) takes elements 16h..16h+15 of each 32-element group of the
+// chunk and the scale of group h: one E8M0 scale per MX group, no dequantisation.
+typedef int mx_i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_mx(mx_i32x8 a, mx_i32x8 b, f32x16 c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
-__device__ __forceinline__ uint32_t mx_pack(mx_f32x2 v, float s) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mx_f32x2){v.x * s, v.y * s}, mx_bf16x2));
-}
-// Eight E4M3 codes (byte i = element i) times scale s, as eight bf16.
-__device__ __forceinline__ bf16x8 mx_to_bf16x8(long codes, float s) {
-  const int lo = (int)(uint32_t)codes, hi = (int)(uint32_t)((unsigned long)codes >> 32);
-  u32x4 v;
-  v[0] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(lo, false), s);
-  v[1] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(lo, true), s);
-  v[2] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(hi, false), s);
-  v[3] = mx_pack(__builtin_amdgcn_cvt_pk_f32_fp8(hi, true), s);
-  return as_bf16x8(v);
+__device__ __forceinline__ mx_i32x8 mx_join(u32x4 lo, u32x4 hi) {
+  return mx_i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -551,12 +542,16 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 // the shared row histogram and load the next query.
 constexpr int kDecodeMaxItems = 256;   // tiles per decode workgroup (the grid is sized for it)
 
-// MX: MXFP8 operands (FP8 storage, one E8M0 scale per 32 elements, bf16 MFMA after dequantising).
+// MX: MXFP8 operands (FP8 storage, one E8M0 scale per 32 elements, block-scaled MFMA).
 template <int HI, int DI, bool FP8, bool MX = false>
 __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
-  static_assert(!MX || (FP8 && DI % 32 == 0), "MXFP8 keeps E4M3 codes, 32 elements per scale");
+  static_assert(!MX || FP8, "MXFP8 keeps E4M3 codes");
+  static_assert(!FP8 || DI % 64 == 0, "E4M3 products run in 64-element MFMA chunks");
   using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles, 4 waves x 32 keys
-  typedef std::conditional_t<MX, bf16x8, typename AFrag<FP8>::T> frag_t;
+  typedef typename AFrag<FP8>::T frag_t;
+  // E4M3 operands (fp8 and MXFP8) run on the 32x32x64 block-scaled MFMA, fp8 with unit scales
+  // (its per-head and per-page scales apply outside the product)
+  constexpr int NC = FP8 ? DI / 64 : 1;            // 64-element chunks of the dot product
   constexpr int BLK = 32 * C::ROWB;                // one wave's block (bytes)
   constexpr int NG = DI / 32;                      // MX: scale bytes per key row
   constexpr int SB = 32 * NG;                      // MX: scale bytes per block
@@ -617,24 +612,35 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     return l;
   };
 
-  frag_t afrag[C::MB][C::KS];
+  frag_t afrag[FP8 ? 1 : C::MB][FP8 ? 1 : C::KS];
+  mx_i32x8 amx[FP8 ? C::MB : 1][NC];             // E4M3: q codes of lane (head, h) per chunk
+  int asc[FP8 ? C::MB : 1][NC];                  // their group scales (127 = 1 for fp8)
   float wreg[C::MB][16];
   auto load_q = [&](int b) {
 #pragma unroll
     for (int m = 0; m < C::MB; ++m) {
       const int head = 32 * m + nl;
+      if constexpr (FP8) {
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        if (head < HI) {
-          const unsigned char* src = a.q + (((size_t)b * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
-          if constexpr (MX)
-            afrag[m][kk] = mx_to_bf16x8(*reinterpret_cast<const long*>(src),
-                                        e8m0_value(a.q_e8[((size_t)b * HI + head) * NG + kk / 2]));
-          else if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
-          else afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
-        } else {
-          if constexpr (FP8 && !MX) afrag[m][kk] = 0;
-          else afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        for (int c = 0; c < NC; ++c) {
+          if (head < HI) {
+            const unsigned char* src = a.q + ((size_t)b * HI + head) * DI + 64 * c + 16 * hh;
+            amx[m][c] = mx_join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 32));
+            asc[m][c] = MX ? (int)a.q_e8[((size_t)b * HI + head) * NG + 2 * c + hh] : 127;
+          } else {
+            amx[m][c] = mx_i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            asc[m][c] = 127;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+          if (head < HI) {
+            const unsigned char* src = a.q + (((size_t)b * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
+            afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
+          } else {
+            afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+          }
         }
       }
 #pragma unroll
@@ -739,30 +745,36 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       kscale = wave < 2 ? sc.x : sc.y;
     }
     const unsigned char* blk = lds_k[wave][slot];
-    frag_t bfr[C::KS];
-#pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk) {
-      if constexpr (MX)
-        bfr[kk] = mx_to_bf16x8(
-            *reinterpret_cast<const long*>(blk + nl * C::ROWB + 16 * (kk ^ (nl & (C::CPK - 1))) + 8 * hh),
-            e8m0_value(lds_kx[wave][slot][nl * NG + kk / 2]));
-      else if constexpr (FP8)
-        bfr[kk] = *reinterpret_cast<const long*>(blk + nl * C::ROWB + 16 * (kk ^ (nl & (C::CPK - 1))) + 8 * hh);
-      else
-        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blk + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
-    }
     f32x16 acc[C::MB];
 #pragma unroll
     for (int m = 0; m < C::MB; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+    if constexpr (FP8) {
+      // key nl: chunks 4c + h and 4c + 2 + h of its row (16 bytes each, XOR-swizzled by the key)
+      mx_i32x8 bmx[NC];
+      int bsc[NC];
 #pragma unroll
-    for (int kk = 0; kk < C::KS; ++kk)
-#pragma unroll
-      for (int m = 0; m < C::MB; ++m) {
-        if constexpr (FP8 && !MX) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
-        else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+      for (int c = 0; c < NC; ++c) {
+        const unsigned char* row = blk + nl * C::ROWB;
+        bmx[c] = mx_join(*reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + hh) ^ (nl & (C::CPK - 1)))),
+                         *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 + hh) ^ (nl & (C::CPK - 1)))));
+        bsc[c] = MX ? (int)lds_kx[wave][slot][nl * NG + 2 * c + hh] : 127;
       }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int m = 0; m < C::MB; ++m) acc[m] = mfma_mx(amx[m][c], bmx[c], acc[m], asc[m][c], bsc[c]);
+    } else {
+      bf16x8 bfr[C::KS];
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk)
+        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blk + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
+#pragma unroll
+      for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+        for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+    }
     // the slot's reads are complete (the MFMAs consumed them): refill it
     if (i + NSLOT < n_items) issue(i + NSLOT, slot);
     float part = 0.f;
