@@ -1,0 +1,61 @@
+"""MXFP8 quantisation of key and query rows, by definition (test infrastructure only).
+
+Follows the indexer's quantised storage ([P1] §4: the Lightning Indexer's Q and K in MXFP8; [P1] §3
+and [P3] §3.3: the indexer prolog writes the new keys into the cache), with MXFP8 as the OCP
+Microscaling format defines it.  Each run of 32 consecutive elements V_0..V_31 of a row:
+  * shared exponent s = floor(log2(max_i |V_i|)) - 8 (8 = the largest E4M3 exponent), clamped to
+    [-127, 127]; a run of zeros takes s = -127;
+  * scale byte e = s + 127 (E8M0: value 2^(e - 127));
+  * element codes: V_i / 2^s rounded to the nearest E4M3 value, ties to even, magnitudes above 448
+    clamped to 448; the sign of a result that rounds to zero is the sign of V_i.
+Finite inputs only.  Arithmetic in float64 (every step is exact there: the inputs are bf16).
+"""
+import numpy as np
+
+from .codecs import e4m3_table
+
+MX_GROUP = 32
+E4M3_MAX = 448.0
+
+
+def _e4m3_rne(x: np.ndarray) -> np.ndarray:
+    """E4M3FN codes of float64 values: round to nearest (ties to even), clamp to +-448."""
+    a = np.abs(x)
+    # spacing of the representable values around |x|: 2^(E - 3) for normal E >= -6, 2^-9 below
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.ldexp(1.0, (np.maximum(e, -6) - 3).astype(np.int64))
+    q = np.round(a / step) * step            # numpy rounds halves to even
+    q = np.minimum(q, E4M3_MAX)
+    # code of each magnitude from the format's own value table (positive codes 0x00..0x7E)
+    tab = e4m3_table()[:0x7F]
+    idx = np.searchsorted(tab, q)
+    assert np.array_equal(tab[idx], q), "rounded value not representable"
+    neg = np.signbit(x)
+    return (idx + np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def mxfp8_quantize_rows(v: np.ndarray):
+    """v [..., D] (D a multiple of 32), finite -> (codes uint8 [..., D], scale bytes uint8 [..., D/32])."""
+    v = np.asarray(v, dtype=np.float64)
+    g = v.reshape(*v.shape[:-1], v.shape[-1] // MX_GROUP, MX_GROUP)
+    amax = np.abs(g).max(axis=-1)
+    s = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    s = np.clip(s, -127, 127).astype(np.int64)
+    codes = _e4m3_rne(g / np.ldexp(1.0, s)[..., None]).reshape(v.shape)
+    return codes, (s + 127).astype(np.uint8)
+
+
+def cache_append_ref(k_new, k_cache, k_scale, block_table, seq_lens, T):
+    """The paged MXFP8 K cache after appending k_new [B, T, D] (already decoded to float):
+    token t of sequence b is logical position seq_lens[b] - T + t, stored at page
+    block_table[b, pos // 64], slot pos % 64.  Returns new (k_cache, k_scale) copies."""
+    kc, ks = k_cache.copy(), k_scale.copy()
+    codes, sc = mxfp8_quantize_rows(k_new)
+    B = k_new.shape[0]
+    for b in range(B):
+        for t in range(T):
+            pos = int(seq_lens[b]) - T + t
+            p, slot = int(block_table[b, pos // 64]), pos % 64
+            kc[p, slot] = codes[b, t]
+            ks[p, slot] = sc[b, t]
+    return kc, ks

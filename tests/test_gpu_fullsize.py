@@ -1,4 +1,5 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration bench.py times.
+"""GPU parity at the five workloads' full sizes (and the MXFP8 variant of the fp8 one), in the launch
+configuration bench.py times.
 
 The oracle cannot score every row at these sizes in seconds, so it checks sampled rows completely
 (near-tie index gate, attention gates on the GPU's own indices) and every row is checked for the
@@ -33,6 +34,7 @@ def _row_properties(idx, spec, seq_lens):
     (4, [(0, 0), (5, 0)]),
     (5, [(0, 0), (0, 3), (9, 1), (15, 2)]),
     (3, [(0, 0), (0, 2047), (0, 2048), (0, 5000), (0, 8191)]),
+    (6, [(0, 0), (3, 0), (7, 0)]),
 ])
 def test_full_size_sampled(cfg, rows):
     spec = W.config(cfg)
@@ -44,9 +46,8 @@ def test_full_size_sampled(cfg, rows):
     torch.cuda.synchronize()
     idx = to_np(idx_t)
     _row_properties(idx, spec, c.seq_lens)
-    dt = "fp8" if spec.idx_dtype == "fp8" else "bf16"
-    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype=dt, rows=rows,
-                                         return_scores=True)
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype=spec.idx_dtype,
+                                         rows=rows, return_scores=True)
     swaps = check_indices_band(idx, ref, extra, spec.K, c.seq_lens, spec.T, rows=rows)
     print(f"[case] band swaps on sampled rows: {swaps}", flush=True)
     o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
@@ -54,3 +55,19 @@ def test_full_size_sampled(cfg, rows):
     bi = [r[0] for r in rows]
     ti = [r[1] for r in rows]
     check_attn(to_np(out_t[bi, ti]), to_np(lse_t[bi, ti]), o_ref[bi, ti], l_ref[bi, ti])
+
+
+def test_full_size_mxfp8_grid_exact_rows():
+    """The exact MXFP8 grid at the MXFP8 workload's full shape (8 x 131072 keys): sampled rows must
+    match the oracle bit for bit (every fp32 partial sum is exact), all rows keep the properties."""
+    spec = W.custom("mxgrid_full", 8, 1, (131072,) * 8, 64, 128, 2048, 128, idx_dtype="mxfp8",
+                    values="mxgrid", cfg_id=6)
+    rows = [(1, 0), (6, 0)]
+    print(f"[case] full {spec.name} rows {rows}", flush=True)
+    c = W.make_case(spec)
+    idx = to_np(Dev(c).indexer())
+    torch.cuda.synchronize()
+    _row_properties(idx, spec, c.seq_lens)
+    ref = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=spec.K, dtype="mxfp8", rows=rows)
+    for b, t in rows:
+        np.testing.assert_array_equal(idx[b, t], ref[b, t])
