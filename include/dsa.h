@@ -133,6 +133,35 @@ dsa_status dsa_indexer_topk(const void *q, const void *q_scale, const float *w,
                             int32_t *idx_out, void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* MXFP8 quantisation of bf16 rows ([P1] §4: the Lightning Indexer's Q and K in MXFP8; [P1] §3,
+ * [P3] §3.3: the indexer prolog quantises the indexer q and k).  Each run of 32 consecutive
+ * elements of a row shares the E8M0 exponent s = floor(log2(max |v|)) - 8 (OCP Microscaling;
+ * clamped to [-127, 127], -127 for a run of zeros); its elements are v * 2^-s rounded to E4M3
+ * (nearest, ties to even) and clamped to +-448.  Finite inputs only.
+ *
+ *   x       [rows, dim] bf16, 16-byte aligned; dim a multiple of 32 (32..4096)
+ *   codes   [rows, dim] E4M3 codes, 16-byte aligned
+ *   scales  [rows, dim / 32] E8M0 bytes (value 2^(e - 127))
+ * For the indexer queries: rows = batch * T * heads, the layout dsa_indexer_topk reads with
+ * DSA_MXFP8_E4M3. */
+dsa_status dsa_mxfp8_quantize(const void *x, int64_t rows, int32_t dim, void *codes, void *scales,
+                              hipStream_t stream);
+
+/* Appends the T newest keys of every sequence to the paged MXFP8 indexer-K cache ([P1] §3: the
+ * prolog writes the new keys into the cache; §4: MXFP8 storage), quantising each key row exactly as
+ * dsa_mxfp8_quantize does.  Key t of sequence b is logical position seq_lens[b] - T + t (the
+ * lengths already count the new tokens, as in dsa_indexer_topk) and is written to page
+ * block_table[b, pos / page_size], slot pos % page_size; nothing else in the cache changes.
+ *
+ *   k_new    [batch, T, dim] bf16, 16-byte aligned; dim a multiple of 32 (32..4096)
+ *   k_cache  [num_pages, page_size, dim] E4M3 codes, 16-byte aligned
+ *   k_scale  [num_pages, page_size, dim / 32] E8M0 bytes
+ * Positions of one call must be distinct (true whenever the block tables of different sequences
+ * do not share pages); seq_lens and block_table entries are device-side preconditions as for
+ * dsa_indexer_topk. */
+dsa_status dsa_indexer_cache_append(const void *k_new, const dsa_paged_layout *layout, int32_t T,
+                                    int32_t dim, void *k_cache, void *k_scale, hipStream_t stream);
+
 /* Bytes of workspace dsa_sparse_attn needs for this layout and shape (0 on invalid input). */
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_attn_shape *shape);
 

@@ -56,8 +56,8 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_profile_start", "dsa_profile_stop", "dsa_last_error",
-           "dsa_version", "dsa_debug_status"]
+           "dsa_sparse_attn", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_profile_start",
+           "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
 def lib() -> ctypes.CDLL:
@@ -80,6 +80,11 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_attn.argtypes = [vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
                                   vp, vp, vp, sz, vp]
     L.dsa_sparse_attn.restype = ctypes.c_int
+    L.dsa_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    L.dsa_mxfp8_quantize.restype = ctypes.c_int
+    L.dsa_indexer_cache_append.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
+                                           vp, vp, vp]
+    L.dsa_indexer_cache_append.restype = ctypes.c_int
     L.dsa_last_error.argtypes = []
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_debug_status.argtypes = [vp]
@@ -151,6 +156,33 @@ def dsa_indexer_topk(q, q_scale, w, k_cache, k_scale, block_table, seq_lens, *, 
                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)))
     return idx_out
+
+
+def dsa_mxfp8_quantize(x, codes=None, scales=None, stream=None):
+    """MXFP8 quantisation of bf16 rows x [..., dim] (dim a multiple of 32).  Returns (codes uint8
+    [..., dim], scales uint8 E8M0 [..., dim / 32])."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((*x.shape[:-1], dim // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().dsa_mxfp8_quantize(_ptr(x), rows, dim, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def dsa_indexer_cache_append(k_new, k_cache, k_scale, block_table, seq_lens, *, max_seq_len: int,
+                             num_pages: int | None = None, stream=None):
+    """Appends k_new [B, T, dim] bf16 (the T newest keys of each sequence) to the paged MXFP8 cache
+    k_cache [P, 64, dim] uint8 / k_scale [P, 64, dim / 32] uint8, in place."""
+    assert k_new.dtype == torch.bfloat16 and k_new.is_contiguous()
+    B, T, dim = k_new.shape
+    P = k_cache.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    _check(lib().dsa_indexer_cache_append(_ptr(k_new), ctypes.byref(layout), T, dim, _ptr(k_cache),
+                                          _ptr(k_scale), _stream(stream)))
+    return k_cache, k_scale
 
 
 def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float, max_seq_len: int,

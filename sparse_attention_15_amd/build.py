@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["indexer.hip", "sfa.hip", "dsa_api.cpp", "dsa_profile.cpp"]
+SOURCES = ["indexer.hip", "sfa.hip", "quant.hip", "dsa_api.cpp", "dsa_profile.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU ops stay disabled: the compiler would otherwise form v_pk_*_f32 from plain
 # float code.

@@ -80,11 +80,12 @@ const char* dsa_last_error(void) { return g_last_error.c_str(); }
 dsa_status dsa_debug_status(hipStream_t stream) {
   hipError_t e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "stream synchronize: %s", hipGetErrorString(e));
-  uint32_t fi = 0, fa = 0;
+  uint32_t fi = 0, fa = 0, fq = 0;
   e = dsa::indexer_take_input_flags(&fi);
   if (e == hipSuccess) e = dsa::attn_take_input_flags(&fa);
+  if (e == hipSuccess) e = dsa::quant_take_input_flags(&fq);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "reading the input-check flags: %s", hipGetErrorString(e));
-  const uint32_t f = fi | fa;
+  const uint32_t f = fi | fa | fq;
   if (f == 0) return DSA_OK;
   return fail(DSA_ERR_SHAPE, "device-side input checks failed:%s%s%s",
               (f & 1u) ? " block_table entry outside [0, num_pages);" : "",
@@ -133,6 +134,42 @@ dsa_status dsa_indexer_topk(const void* q, const void* q_scale, const float* w, 
   a.idx_out = idx_out; a.workspace = workspace;
   const hipError_t e = dsa::launch_indexer(a, plan, stream);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "indexer launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+dsa_status dsa_mxfp8_quantize(const void* x, int64_t rows, int32_t dim, void* codes, void* scales,
+                              hipStream_t stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr)
+    return fail(DSA_ERR_NULL, "x / codes / scales is NULL");
+  if (rows < 0) return fail(DSA_ERR_SHAPE, "rows %lld < 0", (long long)rows);
+  if (dim < 32 || dim > 4096 || dim % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (a multiple of 32, 32..4096)", dim);
+  if (!aligned(x, 16) || !aligned(codes, 16)) return fail(DSA_ERR_ALIGN, "x / codes need 16-byte alignment");
+  dsa::QuantLaunch q;
+  q.src = x; q.codes = codes; q.scales = scales; q.rows = rows; q.dim = dim;
+  const hipError_t e = dsa::launch_mx_quant(q, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "quantise launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
+dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* layout, int32_t T,
+                                    int32_t dim, void* k_cache, void* k_scale, hipStream_t stream) {
+  if (T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", T);
+  dsa_status st = check_layout(layout, T);
+  if (st != DSA_OK) return st;
+  if (k_new == nullptr || k_cache == nullptr || k_scale == nullptr)
+    return fail(DSA_ERR_NULL, "k_new / k_cache / k_scale is NULL");
+  if (dim < 32 || dim > 4096 || dim % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (a multiple of 32, 32..4096)", dim);
+  if (!aligned(k_new, 16) || !aligned(k_cache, 16)) return fail(DSA_ERR_ALIGN, "k_new / k_cache need 16-byte alignment");
+  dsa::QuantLaunch q;
+  q.src = k_new; q.codes = k_cache; q.scales = k_scale;
+  q.block_table = layout->block_table; q.seq_lens = layout->seq_lens;
+  q.rows = (long long)layout->batch * T; q.dim = dim; q.T = T;
+  q.max_pages = layout->max_pages; q.num_pages = layout->num_pages; q.max_seq_len = layout->max_seq_len;
+  q.paged = true;
+  const hipError_t e = dsa::launch_mx_quant(q, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "cache append launch: %s", hipGetErrorString(e));
   return DSA_OK;
 }
 

@@ -51,6 +51,20 @@ struct IndexerArgs {
 // Read and clear the device-side input-check flags of each translation unit (current device).
 hipError_t indexer_take_input_flags(uint32_t* flags);
 hipError_t attn_take_input_flags(uint32_t* flags);
+hipError_t quant_take_input_flags(uint32_t* flags);
+
+// MXFP8 quantisation of bf16 rows (quant.hip): to contiguous rows, or appended to the paged cache.
+struct QuantLaunch {
+  const void* src;            // bf16 [rows, dim]
+  void* codes;                // E4M3 destination
+  void* scales;               // E8M0 destination
+  const int32_t* block_table = nullptr;
+  const int32_t* seq_lens = nullptr;
+  long long rows = 0;
+  int dim = 0, T = 1, max_pages = 0, num_pages = 0, max_seq_len = 0;
+  bool paged = false;
+};
+hipError_t launch_mx_quant(const QuantLaunch& q, hipStream_t stream);
 
 IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S);
 bool indexer_supported(int heads, int dim);

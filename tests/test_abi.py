@@ -116,3 +116,26 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         L.lib()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scales=None), 1),
+    (dict(dim=48), 4), (dict(dim=0), 4), (dict(rows=-1), 2),
+    (dict(x=FAKE + 8), 3), (dict(codes=FAKE + 4), 3),
+])
+def test_mxfp8_quantize_rejects(kw, status):
+    a = dict(x=FAKE, rows=4, dim=128, codes=FAKE, scales=FAKE)
+    a.update(kw)
+    assert dsa.lib().dsa_mxfp8_quantize(a["x"], a["rows"], a["dim"], a["codes"], a["scales"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), 1), (dict(k_cache=None), 1), (dict(k_scale=None), 1),
+    (dict(T=0), 2), (dict(dim=100), 4), (dict(k_new=FAKE + 2), 3),
+    (dict(layout=_layout(page=32)), 4), (dict(layout=_layout(max_len=0)), 2),
+])
+def test_cache_append_rejects(kw, status):
+    a = dict(k_new=FAKE, layout=_layout(), T=1, dim=128, k_cache=FAKE, k_scale=FAKE)
+    a.update(kw)
+    assert dsa.lib().dsa_indexer_cache_append(a["k_new"], ctypes.byref(a["layout"]), a["T"], a["dim"],
+                                              a["k_cache"], a["k_scale"], None) == status

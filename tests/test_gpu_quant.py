@@ -1,0 +1,97 @@
+"""GPU parity of the MXFP8 quantiser and the paged cache append ("Inference Optimization for Kimi
+K3.1 Pro", §3: the indexer prolog writes the new keys into the cache; §4: MXFP8 indexer storage)
+through the C ABI, against the CPU oracle.  Codes and scale bytes are byte outputs: bit-exact.
+
+Inputs mix group magnitudes over many octaves, all-zero groups, groups whose small elements land
+on E4M3 subnormals or round to (signed) zero, elements near 448 * scale, and exact ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_15_amd as dsa
+import workloads as W
+from oracle.quant import cache_append_ref, mxfp8_quantize_rows
+from tests._gpu import DEV, oracle_args, to_np, up
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_rows(shape, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape) * 10.0 ** rng.integers(-6, 5, shape[:-1] + (shape[-1] // 32, 1)).repeat(32, -1).reshape(shape)
+    x = x.astype(np.float32)
+    flat = x.reshape(-1, 32)
+    flat[::7] = 0.0                                        # all-zero groups
+    flat[1::11, 1:] *= 1e-4                                # one large element: the rest near/below the subnormals
+    flat[2::13, 3] = -0.0
+    flat[3::17, :] = np.float32(448.0) * np.float32(2.0 ** -5)   # exact powers: amax on a binade edge
+    return W.f32_to_bf16_bits(x)
+
+
+def _decode_bf16(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("rows,dim", [(1, 32), (333, 128), (4096, 64), (20, 4096)])
+def test_quantize_rows_bit_exact(rows, dim):
+    print(f"[case] quantize rows={rows} dim={dim}", flush=True)
+    bits = _bf16_rows((rows, dim), seed=rows + dim)
+    codes, scales = dsa.dsa_mxfp8_quantize(up(bits))
+    torch.cuda.synchronize()
+    ref_c, ref_s = mxfp8_quantize_rows(_decode_bf16(bits))
+    np.testing.assert_array_equal(to_np(scales), ref_s)
+    np.testing.assert_array_equal(to_np(codes), ref_c)
+
+
+@pytest.mark.parametrize("T,lens", [(1, (130, 64, 4097)), (4, (4, 200, 1000)), (64, (64, 128))])
+def test_cache_append_bit_exact(T, lens):
+    print(f"[case] append T={T} lens={lens}", flush=True)
+    spec = W.custom("append", len(lens), T, lens, 8, 128, 64, 16, idx_dtype="mxfp8")
+    c = W.make_case(spec)
+    rng = np.random.default_rng(7)
+    # the cache holds other contents (noise) everywhere; only the appended slots may change
+    kc = rng.integers(0, 256, c.k_cache.shape).astype(np.uint8)
+    ks = rng.integers(0, 256, c.k_scale.shape).astype(np.uint8)
+    new = _bf16_rows((len(lens), T, 128), seed=T)
+    kc_d, ks_d = up(kc), up(ks)
+    dsa.dsa_indexer_cache_append(up(new), kc_d, ks_d, up(c.block_table), up(c.seq_lens),
+                                 max_seq_len=spec.max_len, num_pages=c.num_pages)
+    torch.cuda.synchronize()
+    ref_c, ref_s = cache_append_ref(_decode_bf16(new), kc, ks, c.block_table, c.seq_lens, T)
+    np.testing.assert_array_equal(to_np(ks_d), ref_s)
+    np.testing.assert_array_equal(to_np(kc_d), ref_c)
+
+
+def test_prolog_then_indexer_end_to_end():
+    """Quantise the queries and append every key through the library, then run the MXFP8 indexer:
+    its indices equal the oracle's on the library-written codes (which the tests above show equal
+    the oracle's own quantisation)."""
+    spec = W.custom("prolog", 2, 1, (3000, 4500), 64, 128, 2048, 16, idx_dtype="mxfp8")
+    c = W.make_case(spec)
+    B, L = 2, 4500     # keys drawn for the longer context
+    q_bits = _bf16_rows((B, 1, 64, 128), seed=11)
+    k_bits = _bf16_rows((B, L, 128), seed=12)
+    q_codes, q_sc = dsa.dsa_mxfp8_quantize(up(q_bits))
+    kc = torch.zeros(c.k_cache.shape, dtype=torch.uint8, device=DEV)
+    ks = torch.zeros(c.k_scale.shape, dtype=torch.uint8, device=DEV)
+    bt, sl = up(c.block_table), up(c.seq_lens)
+    # two appends write every key of both contexts (3000 and 4500): sequence 1's last 3000 with
+    # sequence 0's whole context, then sequence 1's first 1500 with sequence 0's last 1500 again
+    n0, n1 = 3000, 4500
+    new1 = np.stack([k_bits[0, :n0], k_bits[1, n1 - n0:n1]])
+    dsa.dsa_indexer_cache_append(up(new1), kc, ks, bt, up(np.array([n0, n1], np.int32)),
+                                 max_seq_len=L, num_pages=c.num_pages)
+    new2 = np.stack([k_bits[0, n0 - 1500:n0], k_bits[1, :1500]])
+    dsa.dsa_indexer_cache_append(up(new2), kc, ks, bt, up(np.array([n0, 1500], np.int32)),
+                                 max_seq_len=L, num_pages=c.num_pages)
+    idx = dsa.dsa_indexer_topk(q_codes, q_sc, up(c.w), kc, ks, bt, sl, T=1, top_k=spec.K,
+                               max_seq_len=spec.max_len, mx=True, num_pages=c.num_pages)
+    torch.cuda.synchronize()
+    got = to_np(idx)
+    args = dict(oracle_args(c), q_idx=to_np(q_codes), q_scale=to_np(q_sc), k_cache=to_np(kc),
+                k_scale=to_np(ks))
+    ref, extra = oracle.indexer_topk_ref(**args, T=1, K=spec.K, dtype="mxfp8", return_scores=True)
+    from tests._gpu import check_indices_band
+    check_indices_band(got, ref, extra, spec.K, c.seq_lens, 1)
