@@ -87,10 +87,11 @@ dsa_status dsa_debug_status(hipStream_t stream) {
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "reading the input-check flags: %s", hipGetErrorString(e));
   const uint32_t f = fi | fa | fq;
   if (f == 0) return DSA_OK;
-  return fail(DSA_ERR_SHAPE, "device-side input checks failed:%s%s%s",
+  return fail(DSA_ERR_SHAPE, "device-side input checks failed:%s%s%s%s",
               (f & 1u) ? " block_table entry outside [0, num_pages);" : "",
               (f & 2u) ? " seq_lens entry outside [T, max_seq_len];" : "",
-              (f & 4u) ? " attention index neither -1 nor a visible position;" : "");
+              (f & 4u) ? " attention index neither -1 nor a visible position;" : "",
+              (f & 8u) ? " histogram-clear handshake timed out (workspace shared by overlapping calls?);" : "");
 }
 
 size_t dsa_indexer_workspace_size(const dsa_paged_layout* layout, const dsa_indexer_shape* shape) {

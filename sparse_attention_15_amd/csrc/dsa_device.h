@@ -133,6 +133,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 constexpr uint32_t kFlagPage = 1u;         // a block-table entry in use lies outside [0, num_pages)
 constexpr uint32_t kFlagLen = 2u;          // a sequence length lies outside [T, max_seq_len]
 constexpr uint32_t kFlagIndex = 4u;        // an attention index is neither -1 nor a visible position
+constexpr uint32_t kFlagSync = 8u;         // a wait for another workgroup's histogram clear timed out
 static __device__ uint32_t g_input_flags;
 __device__ __forceinline__ void flag_input(uint32_t bit) { atomicOr(&g_input_flags, bit); }
 

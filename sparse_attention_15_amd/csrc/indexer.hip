@@ -11,7 +11,8 @@
 // in ascending order, -1 padded.
 //
 // Kernels, in launch order:
-//   li_zero_hist    clears the per-row 2048-bin histograms of the score keys' top 11 bits.
+//   li_zero_hist    clears the per-row 2048-bin histograms of the score keys' top 11 bits (prefill
+//                   and verify; the decode score kernel clears its rows itself, see there).
 //   li_score        one workgroup per (sequence, tile of query rows, chunk of 1024 keys): streams
 //                   the chunk's pages (page-table resolved) through LDS, MFMA score GEMM
 //                   [heads x dim] x [dim x keys], ReLU and head-weight reduction in registers,
@@ -23,6 +24,8 @@
 //                   lowest-position ties up to the quota, and merges both lists into idx_out.
 // A row with n <= K selects every visible position and skips the score scratch.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -33,6 +36,11 @@ namespace dsa {
 constexpr int kTileKeys = 128;    // keys staged in LDS per step (two pages)
 constexpr int kChunkKeys = 1024;  // keys per score workgroup
 constexpr int kBins = 2048;       // first radix digit: key bits 31..21
+// Control words per row, after the histograms: [0..2] the select's counters (segments done, list
+// cursors), [4..5] the 64-bit tag that marks the row's histogram cleared for this call (decode).
+constexpr int kCtl = 8;
+constexpr int kTagWord = 4;
+constexpr unsigned kSyncSpinCap = 1u << 20;   // waits for a tag end after ~50 ms at most
 constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------------------------------------
@@ -73,6 +81,8 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   uint32_t* keys;               // [rows, row_stride]
   uint32_t* hist;               // [rows, kBins]
+  uint32_t* ctl;                // [rows, kCtl] control words
+  unsigned long long tag;       // decode: this call's histogram-cleared tag (never 0)
   const unsigned char* q_e8;    // MXFP8: [B,T,HI,DI/32] E8M0 scale bytes of q
   const unsigned char* k_e8;    // MXFP8: [P,64,DI/32] E8M0 scale bytes of the K cache
   int B, T, max_pages, num_pages, K, n_chunks, n_qtiles, row_stride, max_seq_len;
@@ -569,6 +579,8 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   __shared__ int4 lds_rec[kDecodeMaxItems];
   __shared__ float2 lds_rsc[FP8 && !MX ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
   __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? 4 : 1][MX ? NSLOT : 1][MX ? SB : 16];
+  __shared__ int lds_starts[kDecodeMaxItems];      // sequences whose first tile is in this range
+  __shared__ int lds_nstarts;
   __shared__ uint32_t sh[8];
   // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
   static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
@@ -594,7 +606,10 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     if (b < a.B) lds_tstart[b] = carry + (int)ex;
     carry += (int)tot;
   }
-  if (tid == 0) lds_tstart[a.B] = carry;
+  if (tid == 0) {
+    lds_tstart[a.B] = carry;
+    lds_nstarts = 0;
+  }
   for (int i = tid; i < kBins; i += kThreads) lds_hist[i] = 0u;
   __syncthreads();
   const int total = carry;
@@ -655,7 +670,20 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       }
     }
   };
+  // Adds the LDS histogram into sequence b's row once the workgroup that clears that row (the one
+  // holding its first tile) has published this call's tag.  The wait is bounded: past the cap the
+  // counts go in anyway and the debug flag records it.
   auto flush = [&](int b) {
+    if (tid == 0) {
+      const unsigned long long* tagp =
+          reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)b * kCtl + kTagWord);
+      unsigned spins = 0;
+      while (__hip_atomic_load(tagp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
+        if (++spins > kSyncSpinCap) { flag_input(kFlagSync); break; }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
     for (int i = tid; i < kBins; i += kThreads) {
       const uint32_t v = lds_hist[i];
       if (v != 0u) atomicAdd(&a.hist[(size_t)b * kBins + i], v);
@@ -679,10 +707,32 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       pg[h] = lp * kPage < n ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : -1;
     }
     lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
+    if (j == 0) lds_starts[atomicAdd(&lds_nstarts, 1)] = b;
     // fp8 page scales: loaded now, stored to LDS once the first gathers are in flight
     if constexpr (FP8 && !MX) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
+  // This workgroup clears the histogram and control words of every sequence it starts (no other
+  // workgroup has flushed into them: they all wait for the tag), then publishes this call's tag
+  // for each.  The zeros and the tag travel through device-coherent (agent-scope) stores, which go
+  // past the per-XCD L2s, and the histogram adds are device-coherent atomics, so finishing the
+  // stores (vmcnt) before the tag is written is enough; a release/acquire fence pair would write
+  // back and invalidate whole L2s in every workgroup.
+  const int n_starts = lds_nstarts;
+  for (int k = 0; k < n_starts; ++k) {
+    const int b = lds_starts[k];
+    for (int i = tid; i < kBins; i += kThreads)
+      __hip_atomic_store(&a.hist[(size_t)b * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < kTagWord)
+      __hip_atomic_store(&a.ctl[(size_t)b * kCtl + tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (n_starts > 0) {
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int k = tid; k < n_starts; k += kThreads)
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * kCtl + kTagWord),
+                         a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i (page half wave / 2), into
   // ring slot i % NSLOT.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key %
@@ -801,7 +851,8 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
 struct SelectArgs {
   const uint32_t* keys;     // [rows, row_stride] order-preserving score keys
   const uint32_t* hist;     // [rows, kBins] histogram of key bits 31..21
-  uint32_t* ctl;            // [rows, 4] zeroed per call: segments done, gt cursor, candidate cursor
+  uint32_t* ctl;            // [rows, kCtl]: segments done, gt cursor, candidate cursor (zeroed per
+                            // call), then the histogram-cleared tag, which the select resets
   int32_t* g_gt;            // [rows, DSA_MAX_TOP_K] positions above the threshold range
   uint2* g_cand;            // [rows, kCandCap] (key, position) inside the threshold range
   const int32_t* seq_lens;
@@ -942,6 +993,10 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.x, seg = blockIdx.y;
   const int b = row / a.T, t = row % a.T;
+  // the score kernel of this call is done with the row's histogram-cleared tag: reset it, so a
+  // replay of the same launches (same tag) waits for its own clear again
+  if (seg == 0 && tid == 0)
+    *reinterpret_cast<unsigned long long*>(a.ctl + (size_t)row * kCtl + kTagWord) = 0ull;
   const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
   int32_t* out = a.idx_out + (size_t)row * a.K;
   if (n <= a.K) {
@@ -1058,7 +1113,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       // publish this segment's lists; the last segment to finish carries on with the row
       const uint32_t cnt = S.cursor;
       const uint32_t ng = min(cnt & 0xFFFFu, (uint32_t)DSA_MAX_TOP_K), nc = min(cnt >> 16, (uint32_t)kCandCap);
-      uint32_t* ctl = a.ctl + (size_t)row * 4;
+      uint32_t* ctl = a.ctl + (size_t)row * kCtl;
       if (tid == 0) {
         S.pub[0] = atomicAdd(&ctl[1], ng);
         S.pub[1] = atomicAdd(&ctl[2], nc);
@@ -1183,7 +1238,7 @@ IndexerPlan plan_indexer(const dsa_paged_layout& L, const dsa_indexer_shape& S) 
   p.n_qtiles = (S.T + p.tq - 1) / p.tq;
   size_t off = 0;
   // the select's per-row control words follow the histograms so one clear covers both
-  p.off_hist = off; off = align_up(off + (size_t)p.rows * (kBins + 4) * 4, 256);
+  p.off_hist = off; off = align_up(off + (size_t)p.rows * (kBins + kCtl) * 4, 256);
   p.off_keys = off; off = align_up(off + (size_t)p.rows * p.row_stride * 4, 256);
   p.n_seg = (L.max_seq_len + seg_len_of(L.max_seq_len) - 1) / seg_len_of(L.max_seq_len);
   p.off_gt = p.off_cand = 0;
@@ -1226,6 +1281,19 @@ static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int g
 
 bool indexer_mx_supported(int batch, int T) { return T == 1 && batch <= kMaxSeqPersist; }
 
+// A fresh 64-bit tag per decode call (never 0): a random start mixed with a call counter
+// (splitmix64), so a tag left in a workspace by any earlier call cannot match by accident.
+static unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+      (unsigned long long)(uintptr_t)&counter};
+  unsigned long long z = counter.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z | 1ull;
+}
+
 // Compute units of the current device (cached per device).
 static int device_cus() {
   static int cached[64] = {0};
@@ -1242,9 +1310,12 @@ static int device_cus() {
 hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_t st) {
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
-  const size_t hist_words = (size_t)p.rows * (kBins + 4);   // histograms + select control words
-  const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
-  {
+  const size_t hist_words = (size_t)p.rows * (kBins + kCtl);   // histograms + control words
+  const bool persist = a.T <= 4 && a.B <= kMaxSeqPersist;
+  // the decode kernel clears each row's histogram itself (tag handshake); the others need it clear
+  const bool self_clear = persist && p.tq == 1;
+  if (!self_clear) {
+    const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
     LaunchScope ls("li_zero_hist", st);
     hipLaunchKernelGGL(li_zero_hist, dim3(zgrid), dim3(256), 0, st, hist, hist_words);
   }
@@ -1261,10 +1332,11 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.seq_lens = a.seq_lens;
   s.keys = reinterpret_cast<uint32_t*>(ws + p.off_keys);
   s.hist = hist;
+  s.ctl = hist + (size_t)p.rows * kBins;
+  s.tag = self_clear ? next_call_tag() : 0ull;
   s.B = a.B; s.T = a.T; s.max_pages = a.max_pages; s.num_pages = a.num_pages; s.K = a.top_k;
   s.n_chunks = p.n_chunks; s.n_qtiles = p.n_qtiles; s.row_stride = p.row_stride;
   s.max_seq_len = a.max_seq_len;
-  const bool persist = a.T <= 4 && a.B <= kMaxSeqPersist;
   int grid = a.B * p.n_qtiles * p.n_chunks;
   if (persist) {
     const int kt = p.tq == 1 ? 128 : 64;
