@@ -60,7 +60,9 @@ typedef enum {
                                 per K page */
   DSA_MXFP8_E4M3 = 2         /* MXFP8 (OCP Microscaling): E4M3FN codes, one E8M0 scale byte
                                 2^(e - 127) per 32 consecutive elements of each q head row and
-                                each cached key row ([P1] §4, [P3] §3.3); indexer decode only */
+                                each cached key row ([P1] §4, [P3] §3.3); indexer decode and
+                                causal prefill (T = 2..4 with batch <= 512, the verify kernel,
+                                returns DSA_ERR_UNSUPPORTED) */
 } dsa_dtype;
 
 /* Geometry of the paged caches ([P1] §2 "on-demand in-page addressing"; [P3] §3.1, the paged K
@@ -86,8 +88,8 @@ typedef struct {
   int32_t heads;                /* indexer heads H_I: 8, 16, 32 or 64 */
   int32_t dim;                  /* indexer head dim d_I: 64 or 128 */
   int32_t top_k;                /* K, 1..DSA_MAX_TOP_K */
-  dsa_dtype dtype;              /* storage of q and the indexer-K cache (DSA_MXFP8_E4M3: T = 1
-                                   and batch <= 512 only, else DSA_ERR_UNSUPPORTED) */
+  dsa_dtype dtype;              /* storage of q and the indexer-K cache (DSA_MXFP8_E4M3: not
+                                   for T = 2..4 with batch <= 512) */
 } dsa_indexer_shape;
 
 typedef struct {

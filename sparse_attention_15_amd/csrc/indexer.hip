@@ -109,13 +109,20 @@ struct AFrag<false> { typedef bf16x8 T; };
 template <>
 struct AFrag<true> { typedef long T; };
 
-template <int HI, int DI, bool FP8, int TQ>
+// MX: MXFP8 operands (E4M3 codes, one E8M0 scale per 32 elements) on the 32x32x64 block-scaled MFMA.
+template <int HI, int DI, bool FP8, int TQ, bool MX = false>
 __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
+  static_assert(!MX || (FP8 && DI % 64 == 0), "MXFP8 keeps E4M3 codes, 64-element MFMA chunks");
   using C = ScoreCfg<HI, DI, FP8, TQ>;
   typedef typename AFrag<FP8>::T frag_t;
+  constexpr int NG = DI / 32;                     // MX: scale bytes per key row
+  constexpr int NC = DI / 64;                     // MX: 64-element chunks of the dot product
+  constexpr int SBT = kTileKeys * NG;             // MX: scale bytes per tile (two pages)
+  static_assert(!MX || (SBT % 32 == 0 && SBT / 16 <= kThreads), "tile scale bytes");
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[C::TILEB];
   __shared__ uint32_t lds_hist[TQ * kBins];
   __shared__ float lds_ksc[kTileKeys / kPage];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? SBT : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 31, hh = lane >> 5;
@@ -154,10 +161,26 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
   const size_t row = (size_t)b * a.T + tq;
 
   // A operand: q rows of this query, held for the whole chunk
-  frag_t afrag[C::MB][C::KS];
+  frag_t afrag[MX ? 1 : C::MB][MX ? 1 : C::KS];
+  mx_i32x8 amx[MX ? C::MB : 1][MX ? NC : 1];      // MX: q codes of lane (head, h) per chunk
+  int asc[MX ? C::MB : 1][MX ? NC : 1];           // MX: their group scales
 #pragma unroll
   for (int m = 0; m < C::MB; ++m) {
     const int head = 32 * m + nl;
+    if constexpr (MX) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        if (head < HI) {
+          const unsigned char* src = a.q + (row * HI + head) * DI + 64 * c + 16 * hh;
+          amx[m][c] = mx_join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 32));
+          asc[m][c] = a.q_e8[(row * HI + head) * NG + 2 * c + hh];
+        } else {
+          amx[m][c] = mx_i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          asc[m][c] = 127;
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int kk = 0; kk < C::KS; ++kk) {
       if (head < HI) {
@@ -180,7 +203,7 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
       float wv = 0.f;
       if (head < HI) {
         wv = a.w[row * HI + head];
-        if constexpr (FP8) wv *= a.q_scale[row * HI + head];
+        if constexpr (FP8 && !MX) wv *= a.q_scale[row * HI + head];
       }
       wreg[m][r] = wv;
     }
@@ -188,6 +211,7 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
   const int ntiles = (s_end - s_begin + kTileKeys - 1) / kTileKeys;
   const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
   u32x4 pre[C::LPT];
+  u32x4 pre_sc;   // MX: 16 of the tile's scale bytes (threads < SBT / 16)
 
   auto issue = [&](int tile) {
     const int ts = s_begin + tile * kTileKeys;
@@ -201,6 +225,15 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
         pre[j] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
       }
     }
+    if constexpr (MX) {
+      // a page's 64 keys hold kPage * NG contiguous scale bytes
+      if (tid < SBT / 16) {
+        const int half = tid / (SBT / 32), off = 16 * (tid % (SBT / 32));
+        const int lp = ts / kPage + half;
+        if (lp * kPage < s_end)
+          pre_sc = *reinterpret_cast<const u32x4*>(a.k_e8 + (size_t)clamp_page(bt[lp], a.num_pages) * kPage * NG + off);
+      }
+    }
   };
   auto commit = [&](int tile) {
     const int ts = s_begin + tile * kTileKeys;
@@ -210,7 +243,9 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
       const int key = i / C::CPK, c = i % C::CPK;
       *reinterpret_cast<u32x4*>(lds_k + key * C::ROWB + 16 * (c ^ (key & (C::CPK - 1)))) = pre[j];
     }
-    if constexpr (FP8) {
+    if constexpr (MX) {
+      if (tid < SBT / 16) *reinterpret_cast<u32x4*>(lds_kx + 16 * tid) = pre_sc;
+    } else if constexpr (FP8) {
       if (tid < kTileKeys / kPage) {
         const int lp = ts / kPage + tid;
         lds_ksc[tid] = (lp * kPage < s_end) ? a.k_scale[clamp_page(bt[lp], a.num_pages)] : 0.f;
@@ -234,30 +269,47 @@ __global__ __launch_bounds__(256) void li_score(ScoreArgs a) {
         for (int m = 0; m < C::MB; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-        // all B fragments of the key column are read before the first MFMA
-        frag_t bfr[C::KS];
+        if constexpr (MX) {
+          // key kt: chunks 4c + h and 4c + 2 + h of its row, and its group scales
+          const unsigned char* krow = lds_k + kt * C::ROWB;
+          mx_i32x8 bmx[NC];
+          int bsc[NC];
 #pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk) {
-          if constexpr (FP8)
-            bfr[kk] = *reinterpret_cast<const long*>(lds_k + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
-          else
-            bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                lds_k + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
-        }
-#pragma unroll
-        for (int kk = 0; kk < C::KS; ++kk)
-#pragma unroll
-          for (int m = 0; m < C::MB; ++m) {
-            if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
-            else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+          for (int c = 0; c < NC; ++c) {
+            bmx[c] = mx_join(*reinterpret_cast<const u32x4*>(krow + 16 * ((4 * c + hh) ^ (kt & (C::CPK - 1)))),
+                             *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * c + 2 + hh) ^ (kt & (C::CPK - 1)))));
+            bsc[c] = lds_kx[kt * NG + 2 * c + hh];
           }
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int m = 0; m < C::MB; ++m) acc[m] = mfma_mx(amx[m][c], bmx[c], acc[m], asc[m][c], bsc[c]);
+        } else {
+          // all B fragments of the key column are read before the first MFMA
+          frag_t bfr[C::KS];
+#pragma unroll
+          for (int kk = 0; kk < C::KS; ++kk) {
+            if constexpr (FP8)
+              bfr[kk] = *reinterpret_cast<const long*>(lds_k + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
+            else
+              bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                  lds_k + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
+          }
+#pragma unroll
+          for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+            for (int m = 0; m < C::MB; ++m) {
+              if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+              else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+            }
+        }
         float part = 0.f;
 #pragma unroll
         for (int m = 0; m < C::MB; ++m)
 #pragma unroll
           for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
         part = xor32_sum(part);
-        if constexpr (FP8) part *= lds_ksc[kt / kPage];
+        if constexpr (FP8 && !MX) part *= lds_ksc[kt / kPage];
         const int s = ts + kt;
         if (emit && hh == 0 && s < n_me) {
           const uint32_t key = float_key(part);
@@ -1257,8 +1309,11 @@ bool indexer_supported(int heads, int dim) {
 template <int HI, int DI, bool FP8>
 static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, bool mx, hipStream_t st) {
   if constexpr (FP8) {
-    if (mx) {   // MXFP8: decode only (the host checks persist && tq == 1)
-      hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+    if (mx) {   // MXFP8: decode or the chunked (prefill) grid; the host rejects verify
+      if (persist) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, true, 1, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else hipLaunchKernelGGL((li_score<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
       return;
     }
   }
@@ -1279,7 +1334,9 @@ static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int g
   else launch_score<HI, DI, false>(s, tq, grid, persist, false, st);
 }
 
-bool indexer_mx_supported(int batch, int T) { return T == 1 && batch <= kMaxSeqPersist; }
+// MXFP8 runs the decode kernel and the chunked (prefill) grid; the verify kernel (2-4 query rows
+// per sequence on the persistent grid) has no MXFP8 path.
+bool indexer_mx_supported(int batch, int T) { return !(T >= 2 && T <= 4 && batch <= kMaxSeqPersist); }
 
 // A fresh 64-bit tag per decode call (never 0): a random start mixed with a call counter
 // (splitmix64), so a tag left in a workspace by any earlier call cannot match by accident.

@@ -5,7 +5,8 @@ The exact integer-grid variant (codes in [-2, 2], power-of-two group scales, wei
 makes every fp32 partial sum exact, so its indices must match the oracle bit for bit; it runs at
 both indexer head dims, which place 4 and 2 scale bytes per key.  The Gaussian cases (rows
 quantised to MXFP8 as the OCP Microscaling format defines it) use the near-tie band.  Sizes span
-several 128-key tiles, score workgroups and select scan steps, with ragged tails.
+several 128-key tiles, score workgroups and select scan steps, with ragged tails.  Decode runs the
+decode score kernel; causal prefill and more than 4 query rows per sequence run the chunked grid.
 """
 import numpy as np
 import pytest
@@ -68,3 +69,39 @@ def test_mx_page_permutation_bit_identical():
     i2 = to_np(Dev(c2).indexer())
     torch.cuda.synchronize()
     np.testing.assert_array_equal(i1, i2)
+
+
+# ---------------------------------------------------------------- chunked grid: prefill and T > 4
+def _run_rows(spec, rows, exact):
+    print(f"[case] {spec.name} T={spec.T} lens={spec.lens} rows={rows[:6]} {spec.values}", flush=True)
+    c = W.make_case(spec)
+    idx = to_np(Dev(c).indexer())
+    torch.cuda.synchronize()
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=spec.T, K=spec.K, dtype="mxfp8",
+                                         rows=rows, return_scores=True)
+    if exact:
+        for b, t in rows:
+            np.testing.assert_array_equal(idx[b, t], ref[b, t], err_msg=f"row {(b, t)}")
+    else:
+        check_indices_band(idx, ref, extra, spec.K, c.seq_lens, spec.T, rows=rows)
+
+
+def test_mx_prefill_grid_exact_rows():
+    L = 2304
+    spec = W.custom("mxgrid_prefill", 1, L, (L,), 64, 128, 2048, 16, idx_dtype="mxfp8",
+                    values="mxgrid")
+    rows = [(0, t) for t in (0, 1, 63, 64, 1000, 2046, 2047, 2048, 2049, 2200, 2303)]
+    _run_rows(spec, rows, exact=True)
+
+
+def test_mx_multi_query_grid_exact():
+    # T = 6 rows per sequence is past the verify kernel: the chunked grid runs it
+    spec = W.custom("mxgrid_T6", 2, 6, (3000, 4100), 64, 128, 2048, 16, idx_dtype="mxfp8",
+                    values="mxgrid")
+    _run_rows(spec, [(b, t) for b in range(2) for t in range(6)], exact=True)
+
+
+def test_mx_small_prefill_gaussian():
+    spec = W.config(7, "small")
+    rows = [(0, t) for t in (0, 5, 511, 512, 800, 1099)]
+    _run_rows(spec, rows, exact=False)

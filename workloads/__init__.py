@@ -121,6 +121,10 @@ def config(cfg_id: int, size: str = "full", variant: int = 0) -> CaseSpec:
                             idx_dtype="mxfp8", variant=variant)
         return CaseSpec("mxs_decode_B2_mxfp8", 6, 2, 1, (3000, 4545), 64, 128, 2048, 128,
                         idx_dtype="mxfp8", variant=variant)
+    if cfg_id == 7:   # causal prefill chunk, MXFP8 indexer (workload 3's shape)
+        L = 8192 if full else 1100
+        return CaseSpec(f"mx_prefill{'' if full else 's'}_T{L}_mxfp8", 7, 1, L, (L,), 64, 128, 2048, 128,
+                        idx_dtype="mxfp8", variant=variant)
     if cfg_id == 5:   # speculative verify: 4 causal drafts per sequence
         if full:
             return CaseSpec("cfg5_verify_B16_T4_L65536", 5, 16, 4, (65536,) * 16, 64, 128, 2048, 128,
