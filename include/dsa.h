@@ -60,9 +60,8 @@ typedef enum {
                                 per K page */
   DSA_MXFP8_E4M3 = 2         /* MXFP8 (OCP Microscaling): E4M3FN codes, one E8M0 scale byte
                                 2^(e - 127) per 32 consecutive elements of each q head row and
-                                each cached key row ([P1] §4, [P3] §3.3); indexer decode and
-                                causal prefill (T = 2..4 with batch <= 512, the verify kernel,
-                                returns DSA_ERR_UNSUPPORTED) */
+                                each cached key row ([P1] §4, [P3] §3.3); indexer only, on
+                                every query-row count (decode, verify, causal prefill) */
 } dsa_dtype;
 
 /* Geometry of the paged caches ([P1] §2 "on-demand in-page addressing"; [P3] §3.1, the paged K

@@ -115,8 +115,7 @@ dsa_status dsa_indexer_topk(const void* q, const void* q_scale, const float* w, 
   if (!fp8 && !mx && (q_scale != nullptr || k_scale != nullptr))
     return fail(DSA_ERR_SHAPE, "q_scale / k_scale must be NULL for the bf16 indexer");
   if (mx && !dsa::indexer_mx_supported(layout->batch, shape->T))
-    return fail(DSA_ERR_UNSUPPORTED, "the MXFP8 indexer has no verify path (T = 2..4 with batch <= 512); "
-                "got T %d, batch %d", shape->T, layout->batch);
+    return fail(DSA_ERR_UNSUPPORTED, "no MXFP8 indexer path for T %d, batch %d", shape->T, layout->batch);
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(w, 4) || !aligned(idx_out, 4) ||
       (fp8 && (!aligned(q_scale, 4) || !aligned(k_scale, 4))) || (mx && !aligned(k_scale, 16)))
     return fail(DSA_ERR_ALIGN, "q / k_cache need 16-byte alignment, w / idx_out 4-byte, fp8 scales 4-byte, "

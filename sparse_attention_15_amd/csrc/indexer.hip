@@ -355,10 +355,17 @@ struct PCfg {
   static_assert(LPT >= 1 && NBW >= 1, "tile shape");
 };
 
-template <int HI, int DI, bool FP8, int TQ>
+// MX: MXFP8 operands (E4M3 codes, one E8M0 scale per 32 elements) on the 32x32x64 block-scaled MFMA.
+template <int HI, int DI, bool FP8, int TQ, bool MX = false>
 __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
+  static_assert(!MX || (FP8 && DI % 64 == 0), "MXFP8 keeps E4M3 codes, 64-element MFMA chunks");
   using C = PCfg<HI, DI, FP8, TQ>;
   typedef typename AFrag<FP8>::T frag_t;
+  constexpr int NG = DI / 32;                     // MX: scale bytes per key row
+  constexpr int NC = DI / 64;                     // MX: 64-element chunks of the dot product
+  constexpr int SBT = C::KT * NG;                 // MX: scale bytes per tile
+  static_assert(!MX || (SBT % 16 == 0 && SBT / 16 <= kThreads && C::KT == kPage), "tile scale bytes");
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kx[2][MX ? SBT : 16];
   __shared__ __attribute__((aligned(16))) unsigned char lds_k[2][C::TILEB];
   __shared__ uint32_t lds_hist[TQ * kBins];
   __shared__ float lds_ksc[2][C::KT / kPage > 0 ? C::KT / kPage : 1];
@@ -427,15 +434,30 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 
   const int qi = wave / C::WPQ, nsub = wave % C::WPQ;
   const bool qvalid = qi < a.T;
-  frag_t afrag[C::MB][C::KS];
+  frag_t afrag[MX ? 1 : C::MB][MX ? 1 : C::KS];
+  mx_i32x8 amx[MX ? C::MB : 1][MX ? NC : 1];      // MX: q codes of lane (head, h) per chunk
+  int asc[MX ? C::MB : 1][MX ? NC : 1];           // MX: their group scales
   float wreg[C::MB][16];
   auto load_q = [&](int b) {
     const size_t row = (size_t)b * a.T + (qvalid ? qi : 0);
 #pragma unroll
     for (int m = 0; m < C::MB; ++m) {
       const int head = 32 * m + nl;
+      if constexpr (MX) {
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
+        for (int c = 0; c < NC; ++c) {
+          if (head < HI) {
+            const unsigned char* src = a.q + (row * HI + head) * DI + 64 * c + 16 * hh;
+            amx[m][c] = mx_join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 32));
+            asc[m][c] = a.q_e8[(row * HI + head) * NG + 2 * c + hh];
+          } else {
+            amx[m][c] = mx_i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+            asc[m][c] = 127;
+          }
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < (MX ? 0 : C::KS); ++kk) {
         if (head < HI) {
           const unsigned char* src = a.q + ((row * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
           if constexpr (FP8) afrag[m][kk] = *reinterpret_cast<const long*>(src);
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
         float wv = 0.f;
         if (hd < HI) {
           wv = a.w[row * HI + hd];
-          if constexpr (FP8) wv *= a.q_scale[row * HI + hd];
+          if constexpr (FP8 && !MX) wv *= a.q_scale[row * HI + hd];
         }
         wreg[m][r] = wv;
       }
@@ -475,10 +497,11 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   u32x4 pre[kPre][C::LPT];
   int pb[kPre], pj[kPre];
   float psc[kPre];                    // fp8: this thread's page scale of the tile (thread < PPT)
+  u32x4 psx[kPre];                    // MX: 16 of the tile's scale bytes (threads < SBT / 16 keep theirs)
   int b_iss = lds_rec[0].x & 511;     // sequence of the last tile issued (dummies reuse it)
   // A dummy call (live == false, past the end of the range) reads page 0 only and leaves the
   // sequence cursor alone; its buffer is never committed.
-  auto issue = [&](int f, bool live, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc) {
+  auto issue = [&](int f, bool live, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc, u32x4& psx) {
     int b = b_iss, j = 0, pg0 = -1, pg1 = -1;
     if (live) {
       const int4 r = lds_rec[f - lo];
@@ -494,19 +517,24 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       const int phys = pg < 0 ? 0 : pg;
       pre[q] = *reinterpret_cast<const u32x4*>(a.kc + ((size_t)phys * kPage + (key % kPage)) * C::ROWB + 16 * c);
     }
-    if constexpr (FP8) {              // one scale load per thread; pages past the end read page 0
+    if constexpr (MX) {               // every thread loads 16 scale bytes of the tile's page
+      const int phys = pg0 < 0 ? 0 : pg0;
+      psx = *reinterpret_cast<const u32x4*>(a.k_e8 + (size_t)phys * kPage * NG + 16 * (tid % (SBT / 16)));
+    } else if constexpr (FP8) {       // one scale load per thread; pages past the end read page 0
       const int pg = PPT == 2 && tid == 1 ? pg1 : pg0;
       psc = a.k_scale[pg < 0 ? 0 : pg];
     }
   };
-  auto commit = [&](const u32x4 (&pre)[C::LPT], float psc, int buf, int b, int j) {
+  auto commit = [&](const u32x4 (&pre)[C::LPT], float psc, const u32x4& psx, int buf, int b, int j) {
 #pragma unroll
     for (int q = 0; q < C::LPT; ++q) {
       const int i = tid + kThreads * q;
       const int key = i / C::CPK, c = i % C::CPK;
       *reinterpret_cast<u32x4*>(lds_k[buf] + key * C::ROWB + 16 * (c ^ (key & (C::CPK - 1)))) = pre[q];
     }
-    if constexpr (FP8) {
+    if constexpr (MX) {
+      if (tid < SBT / 16) *reinterpret_cast<u32x4*>(lds_kx[buf] + 16 * tid) = psx;
+    } else if constexpr (FP8) {
       if (tid < PPT) {
         const int lp = j * C::KT / kPage + tid;
         lds_ksc[buf][tid] = (lp * kPage < lds_len[b]) ? psc : 0.f;
@@ -526,30 +554,47 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
       for (int m = 0; m < C::MB; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
-      // all B fragments of the key column are read before the first MFMA
-      frag_t bfr[C::KS];
+      if constexpr (MX) {
+        // key kt: chunks 4c + h and 4c + 2 + h of its row, and its group scales
+        const unsigned char* krow = lds_k[buf] + kt * C::ROWB;
+        mx_i32x8 bmx[NC];
+        int bsc[NC];
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk) {
-        if constexpr (FP8)
-          bfr[kk] = *reinterpret_cast<const long*>(lds_k[buf] + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
-        else
-          bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-              lds_k[buf] + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
-      }
-#pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk)
-#pragma unroll
-        for (int m = 0; m < C::MB; ++m) {
-          if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
-          else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+        for (int c = 0; c < NC; ++c) {
+          bmx[c] = mx_join(*reinterpret_cast<const u32x4*>(krow + 16 * ((4 * c + hh) ^ (kt & (C::CPK - 1)))),
+                           *reinterpret_cast<const u32x4*>(krow + 16 * ((4 * c + 2 + hh) ^ (kt & (C::CPK - 1)))));
+          bsc[c] = lds_kx[buf][kt * NG + 2 * c + hh];
         }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) acc[m] = mfma_mx(amx[m][c], bmx[c], acc[m], asc[m][c], bsc[c]);
+      } else {
+        // all B fragments of the key column are read before the first MFMA
+        frag_t bfr[C::KS];
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk) {
+          if constexpr (FP8)
+            bfr[kk] = *reinterpret_cast<const long*>(lds_k[buf] + kt * C::ROWB + 16 * (kk ^ (kt & (C::CPK - 1))) + 8 * hh);
+          else
+            bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                lds_k[buf] + kt * C::ROWB + 16 * ((2 * kk + hh) ^ (kt & (C::CPK - 1)))));
+        }
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk)
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) {
+            if constexpr (FP8) acc[m] = mfma_fp8(afrag[m][kk], bfr[kk], acc[m]);
+            else acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+          }
+      }
       float part = 0.f;
 #pragma unroll
       for (int m = 0; m < C::MB; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
       part = xor32_sum(part);
-      if constexpr (FP8) part *= lds_ksc[buf][kt / kPage];
+      if constexpr (FP8 && !MX) part *= lds_ksc[buf][kt / kPage];
       const int s = j * C::KT + kt;
       if (hh == 0 && s < n_me) {
         const uint32_t key = float_key(part);
@@ -561,19 +606,19 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 
   for (int i = tid; i < TQ * kBins; i += kThreads) lds_hist[i] = 0u;
 #pragma unroll
-  for (int u = 0; u < kPre; ++u) issue(u < n_items ? lo + u : lo, u < n_items, pre[u], pb[u], pj[u], psc[u]);
+  for (int u = 0; u < kPre; ++u) issue(u < n_items ? lo + u : lo, u < n_items, pre[u], pb[u], pj[u], psc[u], psx[u]);
   int b_cur = -1;
   // Every step commits, meets the barrier and issues its loads, including the up to kPre - 1
   // dead steps past the range (dummy loads, no compute): the same kPre - 1 tiles of loads then
   // follow each buffer's on every path, so the compiler waits for that buffer alone.
-  auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc) {
+  auto step = [&](int i, u32x4 (&pre)[C::LPT], int& pb, int& pj, float& psc, u32x4& psx) {
     const int buf = i & 1;
     const bool alive = i < n_items;
-    commit(pre, psc, buf, pb, pj);
+    commit(pre, psc, psx, buf, pb, pj);
     const int b = pb, j = pj;
     // the buffer is free: the next loads go out before the barrier, their set-up overlapping it
     const bool live = i + kPre < n_items;
-    issue(live ? lo + i + kPre : lo, live, pre, pb, pj, psc);
+    issue(live ? lo + i + kPre : lo, live, pre, pb, pj, psc, psx);
     lds_barrier();                    // keeps the next tiles' loads in flight
     if (alive && b != b_cur) {        // new sequence: publish the old histogram, load new q
       if (b_cur >= 0) flush(b_cur);
@@ -588,7 +633,7 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
   };
   for (int i = 0; i < n_items; i += kPre) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) step(i + u, pre[u], pb[u], pj[u], psc[u]);
+    for (int u = 0; u < kPre; ++u) step(i + u, pre[u], pb[u], pj[u], psc[u], psx[u]);
   }
   __syncthreads();
   flush(b_cur);
@@ -1309,8 +1354,10 @@ bool indexer_supported(int heads, int dim) {
 template <int HI, int DI, bool FP8>
 static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, bool mx, hipStream_t st) {
   if constexpr (FP8) {
-    if (mx) {   // MXFP8: decode or the chunked (prefill) grid; the host rejects verify
-      if (persist) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+    if (mx) {   // MXFP8: decode, verify or the chunked (prefill) grid
+      if (persist && tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (persist && tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (persist) hipLaunchKernelGGL((li_score_persist<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
       else if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, true, 1, true>), dim3(grid), dim3(kThreads), 0, st, s);
       else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
       else hipLaunchKernelGGL((li_score<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
@@ -1334,9 +1381,8 @@ static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int g
   else launch_score<HI, DI, false>(s, tq, grid, persist, false, st);
 }
 
-// MXFP8 runs the decode kernel and the chunked (prefill) grid; the verify kernel (2-4 query rows
-// per sequence on the persistent grid) has no MXFP8 path.
-bool indexer_mx_supported(int batch, int T) { return !(T >= 2 && T <= 4 && batch <= kMaxSeqPersist); }
+// MXFP8 runs on every score path (decode, verify, chunked prefill).
+bool indexer_mx_supported(int batch, int T) { return batch >= 1 && T >= 1; }
 
 // A fresh 64-bit tag per decode call (never 0): a random start mixed with a call counter
 // (splitmix64), so a tag left in a workspace by any earlier call cannot match by accident.

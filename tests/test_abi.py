@@ -83,7 +83,6 @@ def _attn_call(q=FAKE, kv=FAKE, idx=FAKE, layout=None, shape=None, out=FAKE, lse
     (dict(shape=_ishape(K=4096)), 4), (dict(shape=_ishape(T=0)), 2),
     (dict(shape=_ishape(dt=1)), 1),                       # fp8 without scales
     (dict(shape=_ishape(dt=2)), 1),                       # MXFP8 without scales
-    (dict(shape=_ishape(dt=2, T=2), qs=FAKE, ks=FAKE), 4),   # MXFP8 runs decode only
     (dict(shape=_ishape(dt=2), qs=FAKE, ks=FAKE + 4), 3),    # MXFP8 k scales need 16 bytes
     (dict(shape=_ishape(dt=3)), 4),                       # unknown dtype
     (dict(qs=FAKE, ks=FAKE), 2),                          # scales given for bf16

@@ -6,7 +6,8 @@ makes every fp32 partial sum exact, so its indices must match the oracle bit for
 both indexer head dims, which place 4 and 2 scale bytes per key.  The Gaussian cases (rows
 quantised to MXFP8 as the OCP Microscaling format defines it) use the near-tie band.  Sizes span
 several 128-key tiles, score workgroups and select scan steps, with ragged tails.  Decode runs the
-decode score kernel; causal prefill and more than 4 query rows per sequence run the chunked grid.
+decode score kernel, 2-4 query rows per sequence the verify kernel; causal prefill and more than 4
+query rows per sequence run the chunked grid.
 """
 import numpy as np
 import pytest
@@ -105,3 +106,22 @@ def test_mx_small_prefill_gaussian():
     spec = W.config(7, "small")
     rows = [(0, t) for t in (0, 5, 511, 512, 800, 1099)]
     _run_rows(spec, rows, exact=False)
+
+
+# ---------------------------------------------------------------- verify kernel: 2-4 rows per sequence
+@pytest.mark.parametrize("T,lens", [(4, (3000, 4100, 2051)), (2, (2600, 70, 4545))])
+def test_mx_verify_grid_exact(T, lens):
+    spec = W.custom(f"mxgrid_verify_T{T}", len(lens), T, lens, 64, 128, 2048, 16, idx_dtype="mxfp8",
+                    values="mxgrid")
+    _run_rows(spec, [(b, t) for b in range(len(lens)) for t in range(T)], exact=True)
+
+
+def test_mx_verify_grid_exact_dim64():
+    spec = W.custom("mxgrid_verify_d64", 2, 4, (2100, 777), 32, 64, 300, 16, idx_dtype="mxfp8",
+                    values="mxgrid")
+    _run_rows(spec, [(b, t) for b in range(2) for t in range(4)], exact=True)
+
+
+def test_mx_verify_gaussian():
+    spec = W.custom("mx_verify", 3, 4, (5000, 2049, 6001), 64, 128, 2048, 16, idx_dtype="mxfp8")
+    _run_rows(spec, [(b, t) for b in range(3) for t in range(4)], exact=False)
