@@ -104,7 +104,7 @@ def describe(spec):
     lens = np.asarray(spec.lens)
     kind = {1: "decode", 2: "decode", 3: "causal prefill", 4: "decode, fp8 indexer",
             5: "speculative verify", 6: "decode, MXFP8 indexer",
-            7: "causal prefill, MXFP8 indexer"}.get(spec.cfg_id, "custom")
+            7: "causal prefill, MXFP8 indexer", 8: "speculative verify, MXFP8 indexer"}.get(spec.cfg_id, "custom")
     return (f"{kind}: B={spec.B} T={spec.T} ctx " +
             (f"{lens.min()}..{lens.max()} (mean {lens.mean():.0f})" if lens.min() != lens.max() else f"{lens[0]}")
             + f", K={spec.K}, indexer {spec.HI}x{spec.DI} {spec.idx_dtype}, attention {spec.H} heads 576/512 bf16, page 64")
@@ -149,7 +149,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2,
-                    help="named workload 1..5 (default 2); 6 / 7 = workload 4 / 3 with an MXFP8 indexer")
+                    help="named workload 1..5 (default 2); 6 / 7 / 8 = workload 4 / 3 / 5 with an MXFP8 indexer")
     ap.add_argument("--rotate-gib", type=float, default=2.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32)

@@ -35,6 +35,7 @@ def _row_properties(idx, spec, seq_lens):
     (5, [(0, 0), (0, 3), (9, 1), (15, 2)]),
     (3, [(0, 0), (0, 2047), (0, 2048), (0, 5000), (0, 8191)]),
     (6, [(0, 0), (3, 0), (7, 0)]),
+    (8, [(0, 0), (0, 3), (11, 2)]),
 ])
 def test_full_size_sampled(cfg, rows):
     spec = W.config(cfg)

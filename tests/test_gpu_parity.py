@@ -63,6 +63,10 @@ def test_cfg5_small_verify():
     _run(W.config(5, "small"), exact=False)
 
 
+def test_mx_small_verify():
+    _run(W.config(8, "small"), exact=False)
+
+
 # ---------------------------------------------------------------- exact-arithmetic variants
 @pytest.mark.parametrize("T,lens", [(1, (3000, 5000)), (4, (2600, 4500))])
 def test_wide_grid_exact(T, lens):

@@ -125,6 +125,12 @@ def config(cfg_id: int, size: str = "full", variant: int = 0) -> CaseSpec:
         L = 8192 if full else 1100
         return CaseSpec(f"mx_prefill{'' if full else 's'}_T{L}_mxfp8", 7, 1, L, (L,), 64, 128, 2048, 128,
                         idx_dtype="mxfp8", variant=variant)
+    if cfg_id == 8:   # speculative verify, MXFP8 indexer (workload 5's shape)
+        if full:
+            return CaseSpec("mx_verify_B16_T4_L65536_mxfp8", 8, 16, 4, (65536,) * 16, 64, 128, 2048, 128,
+                            idx_dtype="mxfp8", variant=variant)
+        return CaseSpec("mxs_verify_B2_T4_mxfp8", 8, 2, 4, (2500, 4100), 64, 128, 2048, 128,
+                        idx_dtype="mxfp8", variant=variant)
     if cfg_id == 5:   # speculative verify: 4 causal drafts per sequence
         if full:
             return CaseSpec("cfg5_verify_B16_T4_L65536", 5, 16, 4, (65536,) * 16, 64, 128, 2048, 128,
