@@ -25,6 +25,9 @@ What the oracle computes (readings of the pages where they are silent are marked
     [P2] "Inheritance and Extension of Core Operators" (blockwise attention whose cross-block
     reduction equals the global softmax).  Reading: exact softmax over the selected set, MLA latent
     rows of width 576 of which the first 512 columns are V, explicit softmax scale.
+  * sparse_attn_fp8kv_ref / dequant_kv_fp8 -- [P1] §4 (FP8 SFA cache, per-token scales over
+    128-wide tiles, BF16 products).  Reading: 5 fp32 scales per token (columns 0-127, ..., 384-511,
+    512-575), element = bf16(float32(e4m3(code) * scale)), then sparse_attn_ref on those rows.
   * codecs            -- bf16, OCP E4M3FN and E8M0 (MX shared scale) decoding from the format
     definitions.  The MXFP8 indexer inputs ([P1] §4) are E4M3FN codes with one E8M0 scale per 32
     consecutive elements of each q row and each cached key row.
@@ -34,4 +37,4 @@ brute force on tiny inputs and library routines (torch casts, torch SDPA); see t
 """
 from .codecs import bf16_bits_to_f64, e4m3_codes_to_f64, e4m3_table, e8m0_to_f64  # noqa: F401
 from .indexer import indexer_scores_ref, indexer_topk_ref, visible_positions  # noqa: F401
-from .sfa import sparse_attn_ref  # noqa: F401
+from .sfa import dequant_kv_fp8, sparse_attn_fp8kv_ref, sparse_attn_ref  # noqa: F401

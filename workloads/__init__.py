@@ -17,6 +17,9 @@ Storage conventions (every array is a numpy array in host memory):
   * Slots past a sequence's length and the spare pages are poisoned with NaN codes
     (bf16 0x7FC0, e4m3 0x7F) so a kernel that reads outside the valid range shows NaN.
   * Unused block-table entries point at a poisoned spare page (never at an invalid page id).
+  * An FP8 latent cache (kv_dtype "fp8") quantises the bf16 latent rows per token and 128-column
+    tile: scale amax / 448 (fp32), codes through torch's E4M3 cast; poisoned slots get NaN codes
+    and NaN scales.
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ class CaseSpec:
     K: int                 # top-k
     H: int                 # attention heads
     idx_dtype: str = "bf16"   # "bf16" | "fp8" | "mxfp8"
+    kv_dtype: str = "bf16"    # latent cache: "bf16" | "fp8" (E4M3 + fp32 scale per token and 128-column tile)
     values: str = "gauss"     # "gauss" | "grid" | "grid8" | "ties" | "ties2" | "narrow" | "fp8grid" | "mxgrid" | "sharp"
     sharp_c: float = 1.0
     variant: int = 0
@@ -83,6 +87,8 @@ class Case:
     k_scale: np.ndarray | None  # [P] f32 (fp8) | [P,PAGE,DI/32] uint8 E8M0 (mxfp8)
     q_attn: np.ndarray        # [B,T,H,DQK] uint16
     kv_cache: np.ndarray      # [P,PAGE,DQK] uint16
+    kv_codes: np.ndarray | None = None   # fp8 latent cache: [P,PAGE,DQK] uint8 E4M3
+    kv_scale: np.ndarray | None = None   # fp8 latent cache: [P,PAGE,8] float32 (5 tile scales used)
 
 
 # ----------------------------------------------------------------------------- named workloads
@@ -146,6 +152,30 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+KV_TILE = 128
+
+
+def bf16_rows_to_fp8_tiles(rows_bits: np.ndarray) -> tuple:
+    """Latent rows [..., 576] (bf16 bits) to an FP8 cache: per row and per 128-column tile
+    (columns 0-127, ..., 384-511, 512-575) the fp32 scale amax / 448 (1 for an all-zero tile) and
+    E4M3 codes of x / scale (torch's cast: nearest even).  Returns (codes uint8 [..., 576],
+    scales float32 [..., 8], entries 5-7 = 1)."""
+    import torch
+    x = torch.from_numpy((rows_bits.astype(np.uint32) << 16).view(np.float32))
+    D = x.shape[-1]
+    nt = (D + KV_TILE - 1) // KV_TILE
+    sc = torch.ones(x.shape[:-1] + (8,), dtype=torch.float32)
+    codes = torch.empty(x.shape, dtype=torch.uint8)
+    for i in range(nt):
+        t = x[..., KV_TILE * i:KV_TILE * (i + 1)]
+        amax = t.abs().amax(dim=-1)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        sc[..., i] = s
+        y = (t / s.unsqueeze(-1)).clamp(-448.0, 448.0)
+        codes[..., KV_TILE * i:KV_TILE * (i + 1)] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.numpy(), sc.numpy()
 
 
 def f32_to_mxfp8(x: np.ndarray) -> tuple:
@@ -333,13 +363,22 @@ def make_case(spec: CaseSpec, poison: bool = True) -> Case:
     else:
         q_attn = _gauss_bf16(key0 + [5], (B, T, H, DQK), 1.0 / np.sqrt(DQK))
         kv_cache = _gauss_bf16(key0 + [6], (P, PAGE, DQK), 1.0 / np.sqrt(DQK))
+    kv_codes = kv_scale = None
+    if spec.kv_dtype == "fp8":
+        kv_codes, kv_scale = bf16_rows_to_fp8_tiles(kv_cache)
+    elif spec.kv_dtype != "bf16":
+        raise ValueError(spec.kv_dtype)
     if poison:
         kv_cache[~valid] = BF16_NAN
+        if kv_codes is not None:
+            kv_codes[~valid] = E4M3_NAN
+            kv_scale[~valid] = np.nan
 
     return Case(spec=spec, seq_lens=lens.astype(np.int32), block_table=bt, num_pages=P,
                 q_idx=np.ascontiguousarray(q_idx), q_scale=q_scale, w=np.ascontiguousarray(w, np.float32),
                 k_cache=np.ascontiguousarray(k_cache), k_scale=k_scale,
-                q_attn=np.ascontiguousarray(q_attn), kv_cache=np.ascontiguousarray(kv_cache))
+                q_attn=np.ascontiguousarray(q_attn), kv_cache=np.ascontiguousarray(kv_cache),
+                kv_codes=kv_codes, kv_scale=kv_scale)
 
 
 def custom(name: str, B: int, T: int, lens, HI: int, DI: int, K: int, H: int, **kw) -> CaseSpec:
@@ -359,4 +398,5 @@ def permute_pages(case: Case, seed: int = 99) -> Case:
         out[perm] = a
         return out
     return dataclasses.replace(case, block_table=perm[case.block_table], k_cache=move(case.k_cache),
-                               k_scale=move(case.k_scale), kv_cache=move(case.kv_cache))
+                               k_scale=move(case.k_scale), kv_cache=move(case.kv_cache),
+                               kv_codes=move(case.kv_codes), kv_scale=move(case.kv_scale))
