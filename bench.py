@@ -62,7 +62,8 @@ def algorithmic_bytes(spec, seq_lens):
     # attention: q rows, bf16 output + lse, the index rows, and the selected latent rows; a causal
     # prefill chunk gathers the same cache-resident rows many times, so each is counted once there
     gathered = sum(int(n) for n in seq_lens) if prefill(spec) else kp
-    sfa = spec.B * spec.T * spec.H * (576 * 2 + 512 * 2 + 4) + gathered * 1152
+    row_bytes = 576 + 32 if spec.kv_dtype == "fp8" else 1152   # fp8 cache: codes + 8 fp32 tile scales
+    sfa = spec.B * spec.T * spec.H * (576 * 2 + 512 * 2 + 4) + gathered * row_bytes
     sfa_main = sfa + spec.B * spec.T * spec.K * 4
     # contraction work: the score over every visible key of the rows that select (n > K), and the
     # two attention products over the K' selected rows
@@ -104,10 +105,13 @@ def describe(spec):
     lens = np.asarray(spec.lens)
     kind = {1: "decode", 2: "decode", 3: "causal prefill", 4: "decode, fp8 indexer",
             5: "speculative verify", 6: "decode, MXFP8 indexer",
-            7: "causal prefill, MXFP8 indexer", 8: "speculative verify, MXFP8 indexer"}.get(spec.cfg_id, "custom")
+            7: "causal prefill, MXFP8 indexer", 8: "speculative verify, MXFP8 indexer",
+            9: "decode, FP8 latent cache"}.get(spec.cfg_id, "custom")
     return (f"{kind}: B={spec.B} T={spec.T} ctx " +
             (f"{lens.min()}..{lens.max()} (mean {lens.mean():.0f})" if lens.min() != lens.max() else f"{lens[0]}")
-            + f", K={spec.K}, indexer {spec.HI}x{spec.DI} {spec.idx_dtype}, attention {spec.H} heads 576/512 bf16, page 64")
+            + f", K={spec.K}, indexer {spec.HI}x{spec.DI} {spec.idx_dtype}, attention {spec.H} heads 576/512 "
+            + ("bf16 products over an fp8 E4M3 latent cache (fp32 scale per token and 128 columns)"
+               if spec.kv_dtype == "fp8" else "bf16") + ", page 64")
 
 
 def cpu_baseline(case, max_rows: int, budget_s: float, min_s: float = 10.0):
@@ -128,8 +132,12 @@ def cpu_baseline(case, max_rows: int, budget_s: float, min_s: float = 10.0):
         for sel in sample:
             idx = oracle.indexer_topk_ref(case.q_idx, case.q_scale, case.w, case.k_cache, case.k_scale,
                                           case.block_table, case.seq_lens, spec.T, spec.K, dt, rows=[sel])
-            oracle.sparse_attn_ref(case.q_attn, case.kv_cache, case.block_table, case.seq_lens, idx,
-                                   spec.sm_scale, rows=[sel])
+            if spec.kv_dtype == "fp8":
+                oracle.sparse_attn_fp8kv_ref(case.q_attn, case.kv_codes, case.kv_scale, case.block_table,
+                                             case.seq_lens, idx, spec.sm_scale, rows=[sel])
+            else:
+                oracle.sparse_attn_ref(case.q_attn, case.kv_cache, case.block_table, case.seq_lens, idx,
+                                       spec.sm_scale, rows=[sel])
             done += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -149,7 +157,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2,
-                    help="named workload 1..5 (default 2); 6 / 7 / 8 = workload 4 / 3 / 5 with an MXFP8 indexer")
+                    help="named workload 1..5 (default 2); 6 / 7 / 8 = workload 4 / 3 / 5 with an MXFP8 "
+                         "indexer; 9 = workload 2 with an FP8 latent cache")
     ap.add_argument("--rotate-gib", type=float, default=2.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32)
@@ -201,10 +210,12 @@ def main():
 
     fp8 = spec.idx_dtype == "fp8"
     mx = spec.idx_dtype == "mxfp8"
+    kv8 = spec.kv_dtype == "fp8"
     base = dict(q=up(case.q_idx), w=up(case.w), k=up(case.k_cache),
                 qs=None if case.q_scale is None else up(case.q_scale),
                 ks=None if case.k_scale is None else up(case.k_scale),
-                qa=up(case.q_attn), kv=up(case.kv_cache))
+                qa=up(case.q_attn), kv=up(case.kv_codes if kv8 else case.kv_cache),
+                kvs=up(case.kv_scale) if kv8 else None)
     copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(R - 1)]
     bt, sl = up(case.block_table), up(case.seq_lens)
     log(f"uploaded {R} rotation copies ({ab['step'] * R / 2 ** 30:.2f} GiB of touched bytes)")
@@ -229,13 +240,14 @@ def main():
     for c in copies:   # pre-marshalled arguments: the timed loop only issues the two C calls
         calls.append(((P(c["q"]), P(c["qs"]), P(c["w"]), P(c["k"]), P(c["ks"]), lref, iref, P(idx),
                        P(iws), iws.numel(), stream),
-                      (P(c["qa"]), P(c["kv"]), P(idx), lref, aref, P(out), P(lse), P(aws), aws.numel(),
-                       stream)))
+                      ((P(c["qa"]), P(c["kv"]), P(c["kvs"])) if kv8 else (P(c["qa"]), P(c["kv"])))
+                      + (P(idx), lref, aref, P(out), P(lse), P(aws), aws.numel(), stream)))
+    attn_call = L.dsa_sparse_attn_fp8kv if kv8 else L.dsa_sparse_attn
 
     def step(i):
         a, b = calls[i % R]
         s1 = L.dsa_indexer_topk(*a)
-        s2 = L.dsa_sparse_attn(*b)
+        s2 = attn_call(*b)
         if s1 or s2:
             raise RuntimeError(L.dsa_last_error().decode())
 

@@ -190,6 +190,21 @@ dsa_status dsa_sparse_attn(const void *q, const void *kv_cache, const int32_t *i
                            void *out, float *lse, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Sparse Flash Attention over an FP8 latent cache ([P1] §4: the SFA cache stored in FP8 with
+ * per-token scales over 128-wide tiles; the products stay BF16 and the dequantised BF16 tile feeds
+ * the matrix unit directly).  Same operation, arguments, workspace and errors as dsa_sparse_attn,
+ * with the cache given as
+ *   kv_codes  [num_pages, page_size, 576] E4M3FN codes (uint8), 16-byte aligned
+ *   kv_scale  [num_pages, page_size, 8] fp32, 16-byte aligned: per token the scales of columns
+ *             0-127, 128-255, 256-383, 384-511 and 512-575 (entries 5-7 are not read)
+ * Each selected row is dequantised as bf16(e4m3(code) * scale), the float32 product rounded to
+ * nearest even and then to bf16 (nearest even), before the bf16 products of dsa_sparse_attn.
+ * The workspace size is dsa_sparse_attn_workspace_size() of the same layout and shape. */
+dsa_status dsa_sparse_attn_fp8kv(const void *q, const void *kv_codes, const float *kv_scale,
+                                 const int32_t *idx, const dsa_paged_layout *layout,
+                                 const dsa_attn_shape *shape, void *out, float *lse, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
 /* Opt-in per-kernel timing (off by default).  dsa_profile_start() turns recording on for the
  * calling thread: each kernel the library then launches from this thread is bracketed by two
  * hipEvents on its stream (events come from a reusable host-side pool; no device memory).

@@ -56,7 +56,7 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_profile_start",
+           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_profile_start",
            "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_attn.argtypes = [vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
                                   vp, vp, vp, sz, vp]
     L.dsa_sparse_attn.restype = ctypes.c_int
+    L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
+                                        vp, vp, vp, sz, vp]
+    L.dsa_sparse_attn_fp8kv.restype = ctypes.c_int
     L.dsa_mxfp8_quantize.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
     L.dsa_mxfp8_quantize.restype = ctypes.c_int
     L.dsa_indexer_cache_append.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
@@ -206,6 +209,30 @@ def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float,
     _check(lib().dsa_sparse_attn(_ptr(q), _ptr(kv_cache), _ptr(idx), ctypes.byref(layout),
                                  ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
                                  _stream(stream)))
+    return out, lse
+
+
+def dsa_sparse_attn_fp8kv(q, kv_codes, kv_scale, idx, block_table, seq_lens, *, sm_scale: float,
+                          max_seq_len: int, num_pages: int | None = None, out=None, lse=None,
+                          want_lse: bool = True, workspace=None, stream=None):
+    """Sparse attention over an FP8 latent cache: kv_codes [P,64,576] uint8 (E4M3), kv_scale
+    [P,64,8] fp32 tile scales; otherwise as dsa_sparse_attn."""
+    B, T, H, D = q.shape
+    K = idx.shape[-1]
+    P = kv_codes.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    shape = AttnShape(T, H, D, DIM_V, K, float(sm_scale))
+    if out is None:
+        out = torch.empty((B, T, H, DIM_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    need = dsa_sparse_attn_workspace_size(layout, shape)
+    if workspace is None and need > 0:
+        workspace = _workspace(need, q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_sparse_attn_fp8kv(_ptr(q), _ptr(kv_codes), _ptr(kv_scale), _ptr(idx),
+                                       ctypes.byref(layout), ctypes.byref(shape), _ptr(out), _ptr(lse),
+                                       _ptr(workspace), wsb, _stream(stream)))
     return out, lse
 
 

@@ -178,17 +178,19 @@ size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout* layout, const dsa_
   return dsa::plan_attn(*layout, *shape).total;
 }
 
-dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* idx,
-                           const dsa_paged_layout* layout, const dsa_attn_shape* shape, void* out,
-                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static dsa_status sparse_attn_impl(const void* q, const void* kv_cache, const float* kv_scale, bool kv8,
+                                   const int32_t* idx, const dsa_paged_layout* layout,
+                                   const dsa_attn_shape* shape, void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
   dsa_status st = check_attn_shape(shape);
   if (st != DSA_OK) return st;
   if ((st = check_layout(layout, shape->T)) != DSA_OK) return st;
   if (q == nullptr || kv_cache == nullptr || idx == nullptr || out == nullptr)
     return fail(DSA_ERR_NULL, "q / kv_cache / idx / out is NULL");
+  if (kv8 && kv_scale == nullptr) return fail(DSA_ERR_NULL, "kv_scale is NULL");
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(idx, 4) ||
-      (lse != nullptr && !aligned(lse, 4)))
-    return fail(DSA_ERR_ALIGN, "q / kv_cache / out need 16-byte alignment, idx / lse 4-byte");
+      (lse != nullptr && !aligned(lse, 4)) || (kv8 && !aligned(kv_scale, 16)))
+    return fail(DSA_ERR_ALIGN, "q / kv_cache / out / kv_scale need 16-byte alignment, idx / lse 4-byte");
   const dsa::AttnPlan plan = dsa::plan_attn(*layout, *shape);
   if (plan.total > 0) {
     if (workspace == nullptr || workspace_bytes < plan.total)
@@ -196,7 +198,7 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* i
     if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   dsa::AttnArgs a;
-  a.q = q; a.kv_cache = kv_cache; a.idx = idx;
+  a.q = q; a.kv_cache = kv_cache; a.kv_scale = kv8 ? kv_scale : nullptr; a.idx = idx;
   a.block_table = layout->block_table; a.seq_lens = layout->seq_lens;
   a.B = layout->batch; a.T = shape->T; a.max_pages = layout->max_pages; a.num_pages = layout->num_pages;
   a.max_seq_len = layout->max_seq_len;
@@ -205,6 +207,21 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* i
   const hipError_t e = dsa::launch_attn(a, plan, stream);
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
   return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* idx,
+                           const dsa_paged_layout* layout, const dsa_attn_shape* shape, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sparse_attn_impl(q, kv_cache, nullptr, false, idx, layout, shape, out, lse, workspace,
+                          workspace_bytes, stream);
+}
+
+dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_codes, const float* kv_scale,
+                                 const int32_t* idx, const dsa_paged_layout* layout,
+                                 const dsa_attn_shape* shape, void* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return sparse_attn_impl(q, kv_codes, kv_scale, true, idx, layout, shape, out, lse, workspace,
+                          workspace_bytes, stream);
 }
 
 }  // extern "C"

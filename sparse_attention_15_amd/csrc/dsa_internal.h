@@ -83,6 +83,7 @@ struct AttnPlan {
 struct AttnArgs {
   const void* q;
   const void* kv_cache;
+  const void* kv_scale = nullptr;   // fp8 latent cache: [P, 64, 8] fp32 tile scales; null for bf16
   const int32_t* idx;
   const int32_t* block_table;
   const int32_t* seq_lens;

@@ -18,6 +18,13 @@
 // into the scale).  With one split the workgroup normalises and writes bf16 output and the
 // natural-log LSE; with several, each writes (m, l, O) partials and sfa_combine merges them:
 // M = max m_i, L = sum_i 2^(m_i - M) l_i, O = sum_i 2^(m_i - M) O_i / L.
+//
+// FP8 latent cache ([P1] §4: the SFA cache in FP8 with per-token scales over 128-wide tiles, BF16
+// products, the dequantised BF16 tile filling the matrix unit's input buffer directly): rows are
+// 576 E4M3 codes plus 8 fp32 scales per token (tiles 0-127, 128-255, 256-383, 384-511, 512-575;
+// 3 unused).  The gather ring then holds the raw codes and scales, and each tile is dequantised
+// (float32 product, bf16 rounding) straight into the same swizzled bf16 tile the bf16 cache is
+// gathered into, so the products run unchanged.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -38,7 +45,8 @@ constexpr float kRefLimit = 100.f;         // a logit above reference + this res
 
 struct SfaArgs {
   const unsigned char* q;       // [rows, H, 576] bf16
-  const unsigned char* kv;      // [P, 64, 576] bf16
+  const unsigned char* kv;      // [P, 64, 576] bf16, or E4M3 codes for the fp8 cache
+  const unsigned char* kv_sc;   // fp8 cache: [P, 64, 8] fp32 tile scales (32 bytes per token)
   const int32_t* idx;           // [rows, K]
   const int32_t* block_table;
   const int32_t* seq_lens;
@@ -80,6 +88,18 @@ constexpr int kRingA = 4;                            // score-product A fragment
 constexpr int kRingV = 4;                            // value-product A fragments in flight (deeper spills)
 constexpr int kMaxSplitKeys = DSA_MAX_TOP_K;
 
+// FP8 cache tile in the gather ring: the 32 rows' codes (576 bytes each) then their scale rows
+// (32 bytes each), as 16-byte chunks in order: 1152 code chunks + 64 scale chunks, one spare
+// wave-wide load to make 20 (a multiple of every wave count).  The bf16 tile the products read sits
+// in the first kTileBytes of the ring; the fp8 slots follow it.
+constexpr int kRowBytes8 = kDimQK;                      // 576
+constexpr int kCodeChunks8 = kBK * kRowBytes8 / 16;     // 1152
+constexpr int kChunks8 = kCodeChunks8 + kBK * 2;        // 1216
+constexpr int kDmaPerTile8 = 20;
+constexpr int kSlotBytes8 = kDmaPerTile8 * 1024;        // 20480
+constexpr int kUnits8 = kBK * kDimQK / 8;               // 8-code conversion units per tile (2304)
+static_assert(kDmaPerTile8 * 64 >= kChunks8 && kTileBytes + 4 * kSlotBytes8 <= 4 * kTileBytes, "fp8 ring");
+
 // Waits until this wave's loads of the tile being consumed have landed; `later` of its later
 // tiles (n loads each) may stay in flight.
 template <int n>
@@ -89,12 +109,12 @@ __device__ __forceinline__ void wait_ring(int later) {
   else wait_vmcnt<0>();
 }
 
-template <int NW>
+template <int NW, bool KV8 = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sfa_main(SfaArgs a) {
   constexpr int NT = NW * 64;               // one wave per 32-head group
-  constexpr int kDmaWave = kDmaPerTile / NW;
-  static_assert(kDmaPerTile % NW == 0, "per-wave load count must be uniform");
+  constexpr int kDmaWave = (KV8 ? kDmaPerTile8 : kDmaPerTile) / NW;
+  static_assert(kDmaPerTile % NW == 0 && kDmaPerTile8 % NW == 0, "per-wave load count must be uniform");
   static_assert(kStages - 2 <= 2, "wait_ring handles up to two later tiles");
   __shared__ __attribute__((aligned(1024))) unsigned char lds_kv[kStages][kTileBytes];
   __shared__ int lds_rows[kMaxSplitKeys];   // physical row of each selected index, -1 = skip
@@ -194,7 +214,49 @@ void sfa_main(SfaArgs a) {
     lds_dma16(src, lds_kv[buf] + kRegionB + 1024 * k);
   };
   auto rope_row = [&](int tile, int u) __attribute__((always_inline)) { return lds_rows[tile * kBK + 8 * (wave + u * NW) + (lane >> 3)]; };
+  // fp8 cache: load L = u * NW + wave of the tile covers 16-byte chunks 64L .. 64L + 63 (lane i:
+  // chunk 64L + i): code chunk c of row r for k < 1152 (k = 36r + c), then the two scale chunks of
+  // each row, then a spare load that rereads fill_row's codes into the slot's unused tail.
+  auto issue8 = [&](int tile, int buf) __attribute__((always_inline)) {
+    unsigned char* slot = &lds_kv[0][0] + kTileBytes + kSlotBytes8 * buf;
+#pragma unroll
+    for (int u = 0; u < kDmaWave; ++u) {
+      const int L = u * NW + wave;
+      const int k = 64 * L + lane;
+      const int r = k < kCodeChunks8 ? k / 36 : (k < kChunks8 ? (k - kCodeChunks8) >> 1 : 0);
+      int pr = k < kChunks8 ? lds_rows[tile * kBK + r] : -1;
+      pr = pr < 0 ? fill_row : pr;
+      const unsigned char* src = k < kCodeChunks8
+          ? a.kv + (size_t)(uint32_t)pr * kRowBytes8 + 16 * (k % 36)
+          : (k < kChunks8 ? a.kv_sc + (size_t)(uint32_t)pr * 32 + 16 * ((k - kCodeChunks8) & 1)
+                          : a.kv + (size_t)(uint32_t)pr * kRowBytes8 + 16 * (lane % 36));
+      lds_dma16(src, slot + 1024 * L);
+    }
+  };
+  // fp8 cache: dequantise ring slot `buf` into the bf16 tile (unit v: row v / 72, 8 codes from
+  // column 8 * (v % 72), i.e. bf16 chunk v % 72 of the row, stored at its swizzled slot).
+  auto dequant8 = [&](int buf) __attribute__((always_inline)) {
+    const unsigned char* slot = &lds_kv[0][0] + kTileBytes + kSlotBytes8 * buf;
+    unsigned char* dst = &lds_kv[0][0];
+    for (int v = tid; v < kUnits8; v += NT) {
+      const int r = v / 72, e = v % 72;
+      const uint2 w = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + 8 * e);
+      const float sc = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 4 * min(e >> 4, 4));
+      u32x4 o8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t word = h ? w.y : w.x;
+        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+        o8[2 * h] = pack_bf16(lo[0] * sc, lo[1] * sc);
+        o8[2 * h + 1] = pack_bf16(hi[0] * sc, hi[1] * sc);
+      }
+      const int off = e < 64 ? 1024 * r + 16 * (e ^ swa(r)) : kRegionB + 128 * r + 16 * ((e - 64) ^ swb(r));
+      *reinterpret_cast<u32x4*>(dst + off) = o8;
+    }
+  };
   auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
+    if constexpr (KV8) { issue8(tile, buf); return; }
     int prow[kRows];                        // read together, made scalar one at a time
 #pragma unroll
     for (int u = 0; u < kRows; ++u) prow[u] = lds_rows[tile * kBK + wave + u * NW];
@@ -245,7 +307,11 @@ void sfa_main(SfaArgs a) {
     wait_ring<kDmaWave>(min(kStages - 2, ntiles_run - 1 - it));
     lds_barrier();                          // tile `it` landed for every wave; slot it-1 is free
     if (it + kStages - 1 < ntiles_run) issue(it + kStages - 1, (buf + kStages - 1) % kStages);
-    const unsigned char* tile = lds_kv[buf];
+    if constexpr (KV8) {                    // every wave is past the previous tile's products
+      dequant8(buf);
+      lds_barrier();
+    }
+    const unsigned char* tile = KV8 ? lds_kv[0] : lds_kv[buf];
     const uint32_t valid = lds_valid[it];
 
     // S^T = X q^T: rows = the tile's 32 keys, columns = this wave's 32 heads.  The A fragments
@@ -571,6 +637,7 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   SfaArgs s;
   s.q = static_cast<const unsigned char*>(a.q);
   s.kv = static_cast<const unsigned char*>(a.kv_cache);
+  s.kv_sc = static_cast<const unsigned char*>(a.kv_scale);
   s.idx = a.idx;
   s.block_table = a.block_table;
   s.seq_lens = a.seq_lens;
@@ -586,9 +653,17 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   const dim3 grid(rows, p.n_splits, p.head_chunks);
   {
     LaunchScope ls("sfa_main", st);
-    if (p.groups_per_wg == 4) hipLaunchKernelGGL(sfa_main<4>, grid, dim3(256), 0, st, s);
-    else if (p.groups_per_wg == 2) hipLaunchKernelGGL(sfa_main<2>, grid, dim3(128), 0, st, s);
-    else hipLaunchKernelGGL(sfa_main<1>, grid, dim3(64), 0, st, s);
+    const bool kv8 = a.kv_scale != nullptr;
+    if (p.groups_per_wg == 4) {
+      if (kv8) hipLaunchKernelGGL((sfa_main<4, true>), grid, dim3(256), 0, st, s);
+      else hipLaunchKernelGGL(sfa_main<4>, grid, dim3(256), 0, st, s);
+    } else if (p.groups_per_wg == 2) {
+      if (kv8) hipLaunchKernelGGL((sfa_main<2, true>), grid, dim3(128), 0, st, s);
+      else hipLaunchKernelGGL(sfa_main<2>, grid, dim3(128), 0, st, s);
+    } else {
+      if (kv8) hipLaunchKernelGGL((sfa_main<1, true>), grid, dim3(64), 0, st, s);
+      else hipLaunchKernelGGL(sfa_main<1>, grid, dim3(64), 0, st, s);
+    }
   }
   if (p.n_splits > 1) {
     LaunchScope ls("sfa_combine", st);

@@ -17,6 +17,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import oracle
 import sparse_attention_15_amd as dsa
 
 DEV = torch.device("cuda:0")
@@ -43,7 +44,9 @@ class Dev:
         self.q_scale = None if c.q_scale is None else up(c.q_scale)
         self.k_scale = None if c.k_scale is None else up(c.k_scale)
         self.q_attn = up(c.q_attn)
-        self.kv = up(c.kv_cache)
+        self.kv8 = s.kv_dtype == "fp8"
+        self.kv = up(c.kv_codes if self.kv8 else c.kv_cache)
+        self.kv_scale = up(c.kv_scale) if self.kv8 else None
         self.fp8 = s.idx_dtype == "fp8"
         self.mx = s.idx_dtype == "mxfp8"
 
@@ -57,8 +60,28 @@ class Dev:
         s = self.c.spec
         if isinstance(idx, np.ndarray):
             idx = up(idx.astype(np.int32))
+        if self.kv8:
+            return dsa.dsa_sparse_attn_fp8kv(self.q_attn, self.kv, self.kv_scale, idx, self.bt, self.sl,
+                                             sm_scale=s.sm_scale, max_seq_len=s.max_len,
+                                             num_pages=self.c.num_pages, **kw)
         return dsa.dsa_sparse_attn(self.q_attn, self.kv, idx, self.bt, self.sl, sm_scale=s.sm_scale,
                                    max_seq_len=s.max_len, num_pages=self.c.num_pages, **kw)
+
+    def attn_bf16(self, idx, kv16, **kw):
+        """The bf16-cache call over another cache of the same geometry (kv16 [P,64,576] bf16)."""
+        s = self.c.spec
+        return dsa.dsa_sparse_attn(self.q_attn, kv16, idx, self.bt, self.sl, sm_scale=s.sm_scale,
+                                   max_seq_len=s.max_len, num_pages=self.c.num_pages, **kw)
+
+
+def attn_ref(c, idx, rows=None):
+    """The oracle's attention for case c (bf16 or fp8 latent cache) on indices idx."""
+    s = c.spec
+    if s.kv_dtype == "fp8":
+        return oracle.sparse_attn_fp8kv_ref(c.q_attn, c.kv_codes, c.kv_scale, c.block_table, c.seq_lens,
+                                            idx, s.sm_scale, rows=rows)
+    return oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx, s.sm_scale,
+                                  rows=rows)
 
 
 def oracle_args(c):

@@ -110,6 +110,19 @@ def test_attn_rejects(kw, status):
     assert _attn_call(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(kvs=None), 1), (dict(kv=None), 1), (dict(kvs=FAKE + 4), 3), (dict(kv=FAKE + 8), 3),
+    (dict(shape=_ashape(H=100)), 4), (dict(shape=_ashape(K=2048), ws=None), 5),
+])
+def test_attn_fp8kv_rejects(kw, status):
+    a = dict(q=FAKE, kv=FAKE, kvs=FAKE, idx=FAKE, shape=_ashape(), out=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    lib = dsa.lib()
+    assert lib.dsa_sparse_attn_fp8kv(a["q"], a["kv"], a["kvs"], a["idx"], ctypes.byref(_layout()),
+                                     ctypes.byref(a["shape"]), a["out"], None, a["ws"], a["wsb"], None) == status
+    assert lib.dsa_last_error().decode() != ""
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))

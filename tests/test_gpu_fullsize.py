@@ -1,5 +1,5 @@
-"""GPU parity at the five workloads' full sizes (and the MXFP8 variant of the fp8 one), in the launch
-configuration bench.py times.
+"""GPU parity at the five workloads' full sizes (and their MXFP8-indexer and FP8-latent-cache
+variants), in the launch configuration bench.py times.
 
 The oracle cannot score every row at these sizes in seconds, so it checks sampled rows completely
 (near-tie index gate, attention gates on the GPU's own indices) and every row is checked for the
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests._gpu import Dev, check_attn, check_indices_band, oracle_args, to_np
+from tests._gpu import Dev, attn_ref, check_attn, check_indices_band, oracle_args, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,7 @@ def _row_properties(idx, spec, seq_lens):
     (3, [(0, 0), (0, 2047), (0, 2048), (0, 5000), (0, 8191)]),
     (6, [(0, 0), (3, 0), (7, 0)]),
     (8, [(0, 0), (0, 3), (11, 2)]),
+    (9, [(0, 0), (13, 0), (31, 0)]),
 ])
 def test_full_size_sampled(cfg, rows):
     spec = W.config(cfg)
@@ -51,8 +52,7 @@ def test_full_size_sampled(cfg, rows):
                                          rows=rows, return_scores=True)
     swaps = check_indices_band(idx, ref, extra, spec.K, c.seq_lens, spec.T, rows=rows)
     print(f"[case] band swaps on sampled rows: {swaps}", flush=True)
-    o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
-                                          spec.sm_scale, rows=rows)
+    o_ref, l_ref = attn_ref(c, idx, rows=rows)
     bi = [r[0] for r in rows]
     ti = [r[1] for r in rows]
     check_attn(to_np(out_t[bi, ti]), to_np(lse_t[bi, ti]), o_ref[bi, ti], l_ref[bi, ti])

@@ -137,6 +137,12 @@ def config(cfg_id: int, size: str = "full", variant: int = 0) -> CaseSpec:
                             idx_dtype="mxfp8", variant=variant)
         return CaseSpec("mxs_verify_B2_T4_mxfp8", 8, 2, 4, (2500, 4100), 64, 128, 2048, 128,
                         idx_dtype="mxfp8", variant=variant)
+    if cfg_id == 9:   # workload 2 with an FP8 latent cache
+        if full:
+            return CaseSpec("kv8_decode_B32_L8k-32k", 9, 32, 1, _ragged(2, variant, 32, 8192, 32768),
+                            64, 128, 2048, 128, kv_dtype="fp8", variant=variant)
+        return CaseSpec("kv8s_decode_B3_ragged", 9, 3, 1, _ragged(2, variant + 100, 3, 2100, 5000),
+                        64, 128, 2048, 128, kv_dtype="fp8", variant=variant)
     if cfg_id == 5:   # speculative verify: 4 causal drafts per sequence
         if full:
             return CaseSpec("cfg5_verify_B16_T4_L65536", 5, 16, 4, (65536,) * 16, 64, 128, 2048, 128,
