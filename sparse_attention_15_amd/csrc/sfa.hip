@@ -219,40 +219,67 @@ void sfa_main(SfaArgs a) {
   // each row, then a spare load that rereads fill_row's codes into the slot's unused tail.
   auto issue8 = [&](int tile, int buf) __attribute__((always_inline)) {
     unsigned char* slot = &lds_kv[0][0] + kTileBytes + kSlotBytes8 * buf;
+    int ln = lane;                          // opaque: keeps the per-load offsets out of the tile loop
+    asm volatile("" : "+v"(ln));
+    int prs[kDmaWave];                      // the tile's row-table reads go out together
+#pragma unroll
+    for (int u = 0; u < kDmaWave; ++u) {
+      const int k = 64 * (u * NW + wave) + ln;
+      const int r = k < kCodeChunks8 ? k / 36 : (k < kChunks8 ? (k - kCodeChunks8) >> 1 : 0);
+      prs[u] = k < kChunks8 ? lds_rows[tile * kBK + r] : -1;
+    }
 #pragma unroll
     for (int u = 0; u < kDmaWave; ++u) {
       const int L = u * NW + wave;
-      const int k = 64 * L + lane;
-      const int r = k < kCodeChunks8 ? k / 36 : (k < kChunks8 ? (k - kCodeChunks8) >> 1 : 0);
-      int pr = k < kChunks8 ? lds_rows[tile * kBK + r] : -1;
-      pr = pr < 0 ? fill_row : pr;
+      const int k = 64 * L + ln;
+      const int pr = prs[u] < 0 ? fill_row : prs[u];
       const unsigned char* src = k < kCodeChunks8
           ? a.kv + (size_t)(uint32_t)pr * kRowBytes8 + 16 * (k % 36)
           : (k < kChunks8 ? a.kv_sc + (size_t)(uint32_t)pr * 32 + 16 * ((k - kCodeChunks8) & 1)
-                          : a.kv + (size_t)(uint32_t)pr * kRowBytes8 + 16 * (lane % 36));
+                          : a.kv + (size_t)(uint32_t)pr * kRowBytes8 + 16 * (ln % 36));
       lds_dma16(src, slot + 1024 * L);
     }
   };
   // fp8 cache: dequantise ring slot `buf` into the bf16 tile (unit v: row v / 72, 8 codes from
   // column 8 * (v % 72), i.e. bf16 chunk v % 72 of the row, stored at its swizzled slot).
+  // Units go in batches: a batch's LDS reads are all issued before its first conversion, so each
+  // batch waits for LDS once.
+  constexpr int kUnitsPT = kUnits8 / NT;                 // 9, 18 or 36 units per thread
+  constexpr int kBatch8 = NW == 4 ? 9 : 3;
+  static_assert(kUnits8 % NT == 0 && kUnitsPT % kBatch8 == 0, "dequant units per thread");
   auto dequant8 = [&](int buf) __attribute__((always_inline)) {
     const unsigned char* slot = &lds_kv[0][0] + kTileBytes + kSlotBytes8 * buf;
     unsigned char* dst = &lds_kv[0][0];
-    for (int v = tid; v < kUnits8; v += NT) {
-      const int r = v / 72, e = v % 72;
-      const uint2 w = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + 8 * e);
-      const float sc = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 4 * min(e >> 4, 4));
-      u32x4 o8;
+    // offsets are recomputed per tile from an opaque copy of the thread id: hoisted out of the
+    // tile loop they would hold 3 registers per unit across the products
+    int t0 = tid;
+    asm volatile("" : "+v"(t0));
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t word = h ? w.y : w.x;
-        const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-        const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-        o8[2 * h] = pack_bf16(lo[0] * sc, lo[1] * sc);
-        o8[2 * h + 1] = pack_bf16(hi[0] * sc, hi[1] * sc);
+    for (int j0 = 0; j0 < kUnitsPT; j0 += kBatch8) {
+      uint2 w[kBatch8];
+      float sc[kBatch8];
+      int off[kBatch8];
+#pragma unroll
+      for (int jj = 0; jj < kBatch8; ++jj) {
+        const int v = t0 + NT * (j0 + jj);
+        const int r = v / 72, e = v % 72;
+        w[jj] = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + 8 * e);
+        sc[jj] = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 4 * min(e >> 4, 4));
+        off[jj] = e < 64 ? 1024 * r + 16 * (e ^ swa(r)) : kRegionB + 128 * r + 16 * ((e - 64) ^ swb(r));
       }
-      const int off = e < 64 ? 1024 * r + 16 * (e ^ swa(r)) : kRegionB + 128 * r + 16 * ((e - 64) ^ swb(r));
-      *reinterpret_cast<u32x4*>(dst + off) = o8;
+#pragma unroll
+      for (int jj = 0; jj < kBatch8; ++jj) {
+        u32x4 o8;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t word = h ? w[jj].y : w[jj].x;
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+          o8[2 * h] = pack_bf16(lo[0] * sc[jj], lo[1] * sc[jj]);
+          o8[2 * h + 1] = pack_bf16(hi[0] * sc[jj], hi[1] * sc[jj]);
+        }
+        *reinterpret_cast<u32x4*>(dst + off[jj]) = o8;
+      }
     }
   };
   auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
