@@ -9,6 +9,12 @@ Microscaling format defines it.  Each run of 32 consecutive elements V_0..V_31 o
   * element codes: V_i / 2^s rounded to the nearest E4M3 value, ties to even, magnitudes above 448
     clamped to 448; the sign of a result that rounds to zero is the sign of V_i.
 Finite inputs only.  Arithmetic in float64 (every step is exact there: the inputs are bf16).
+
+FP8 latent rows ([P1] §4: the SFA cache in FP8 with per-token scales over tiles of 128; reading of
+how the prolog fills it): per token and per 128-column tile of the 576-wide row (columns 0-127,
+..., 384-511, 512-575), scale = amax / 448 in float32 (1 for an all-zero tile), element code =
+E4M3 of float32(x / scale) (nearest even, clamped to +-448).  Both divisions are single float32
+operations, rounded to nearest even.
 """
 import numpy as np
 
@@ -53,6 +59,40 @@ def cache_append_ref(k_new, k_cache, k_scale, block_table, seq_lens, T):
     codes, sc = mxfp8_quantize_rows(k_new)
     B = k_new.shape[0]
     for b in range(B):
+        for t in range(T):
+            pos = int(seq_lens[b]) - T + t
+            p, slot = int(block_table[b, pos // 64]), pos % 64
+            kc[p, slot] = codes[b, t]
+            ks[p, slot] = sc[b, t]
+    return kc, ks
+
+
+KV_TILE = 128
+
+
+def latent_fp8_quantize_rows(x):
+    """x [..., 576] finite (bf16 values) -> (codes uint8 [..., 576], scales float32 [..., 8]; entries
+    5-7 = 1)."""
+    x = np.asarray(x, dtype=np.float32)
+    D = x.shape[-1]
+    codes = np.empty(x.shape, np.uint8)
+    scales = np.ones(x.shape[:-1] + (8,), np.float32)
+    for i in range((D + KV_TILE - 1) // KV_TILE):
+        t = x[..., KV_TILE * i:KV_TILE * (i + 1)]
+        amax = np.abs(t).max(axis=-1)
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        scales[..., i] = sc
+        y = (t / sc[..., None]).astype(np.float32)          # float32 division, nearest even
+        codes[..., KV_TILE * i:KV_TILE * (i + 1)] = _e4m3_rne(y.astype(np.float64))
+    return codes, scales
+
+
+def latent_cache_append_fp8_ref(kv_new, kv_codes, kv_scale, block_table, seq_lens, T):
+    """The FP8 latent cache after appending kv_new [B, T, 576] (bf16 values as float): token t of
+    sequence b goes to logical position seq_lens[b] - T + t.  Returns new (codes, scales) copies."""
+    kc, ks = kv_codes.copy(), kv_scale.copy()
+    codes, sc = latent_fp8_quantize_rows(kv_new)
+    for b in range(kv_new.shape[0]):
         for t in range(T):
             pos = int(seq_lens[b]) - T + t
             p, slot = int(block_table[b, pos // 64]), pos % 64

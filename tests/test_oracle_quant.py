@@ -97,3 +97,70 @@ def test_cache_append_positions():
             touched[p, s] = True
     np.testing.assert_array_equal(kc2[~touched], kc[~touched])
     np.testing.assert_array_equal(ks2[~touched], ks[~touched])
+
+
+# ---------------------------------------------------------------- FP8 latent rows ([P1] §4)
+from oracle.quant import latent_cache_append_fp8_ref, latent_fp8_quantize_rows  # noqa: E402
+
+
+def _bf16_rows(rng, shape, scale):
+    return W.f32_to_bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
+
+
+def _bits_to_f32(b):
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_latent_fp8_agrees_with_generator():
+    rng = np.random.default_rng(21)
+    bits = _bf16_rows(rng, (300, 576), 10.0 ** rng.integers(-4, 3, (300, 1)))
+    c1, s1 = latent_fp8_quantize_rows(_bits_to_f32(bits))
+    c2, s2 = W.bf16_rows_to_fp8_tiles(bits)
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+
+
+def test_latent_fp8_closed_forms():
+    x = np.zeros((3, 576), np.float32)
+    x[0, :128] = np.linspace(-448, 448, 128, dtype=np.float32).round()   # amax 448: scale 1
+    x[1, 512] = 3.0                                                       # rope tile only
+    codes, sc = latent_fp8_quantize_rows(x)
+    assert sc[0].tolist() == [1.0] * 8
+    np.testing.assert_array_equal(codes[0, :128], _e4m3_rne(x[0, :128].astype(np.float64)))
+    assert sc[1, 4] == np.float32(3.0) / np.float32(448.0) and sc[1, :4].tolist() == [1.0] * 4
+    assert e4m3_codes_to_f64(codes[1, 512:513])[0] == 448.0 and (codes[2] == 0).all()
+
+
+def test_latent_fp8_tile_max_is_448_and_error_bound():
+    rng = np.random.default_rng(22)
+    x = _bits_to_f32(_bf16_rows(rng, (80, 576), 10.0 ** rng.integers(-5, 2, (80, 1))))
+    codes, sc = latent_fp8_quantize_rows(x)
+    v = e4m3_codes_to_f64(codes)
+    tile = np.minimum(np.arange(576) // 128, 4)
+    for i in range(5):
+        assert (np.abs(v[:, tile == i]).max(axis=1) == 448.0).all()
+    s = sc[:, tile].astype(np.float64)
+    el = np.abs(x / s)
+    step = np.where(el >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(el, 1e-300))) - 3), 2.0 ** -9)
+    assert (np.abs(v * s - x) <= (step / 2) * s * (1 + 1e-6) + 1e-30).all()
+
+
+def test_latent_fp8_append_positions():
+    P = 7
+    rng = np.random.default_rng(23)
+    kc = rng.integers(0, 256, (P, 64, 576)).astype(np.uint8)
+    ks = rng.standard_normal((P, 64, 8)).astype(np.float32)
+    bt = np.array([[3, 5], [6, 0]], np.int32)
+    sl = np.array([66, 2], np.int32)
+    new = _bits_to_f32(_bf16_rows(rng, (2, 2, 576), 0.1))
+    kc2, ks2 = latent_cache_append_fp8_ref(new, kc, ks, bt, sl, 2)
+    codes, sc = latent_fp8_quantize_rows(new)
+    touched = np.zeros((P, 64), bool)
+    for b, positions in ((0, (64, 65)), (1, (0, 1))):
+        for t, pos in enumerate(positions):
+            p, s = bt[b, pos // 64], pos % 64
+            np.testing.assert_array_equal(kc2[p, s], codes[b, t])
+            np.testing.assert_array_equal(ks2[p, s], sc[b, t])
+            touched[p, s] = True
+    np.testing.assert_array_equal(kc2[~touched], kc[~touched])
+    np.testing.assert_array_equal(ks2[~touched], ks[~touched])
