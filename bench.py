@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32)
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--append-kv8", action="store_true",
+                    help="time dsa_latent_cache_append_fp8 instead: 8 sequences x 16384 new latent "
+                         "rows (576 bf16) into the FP8 latent cache")
     ap.add_argument("--append", action="store_true",
                     help="time dsa_indexer_cache_append instead: a prefill chunk of MXFP8 keys "
                          "(8 sequences x 65536 tokens x 128 dims) into the paged cache")
@@ -193,6 +196,8 @@ def main():
 
     if args.append:
         return bench_append(args, dev, dsa)
+    if args.append_kv8:
+        return bench_append_kv8(args, dev, dsa)
 
     spec = W.config(args.workload)
     log("workload", describe(spec))
@@ -329,6 +334,65 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_append_kv8(args, dev, dsa):
+    """dsa_latent_cache_append_fp8 of a prefill chunk: B sequences x T new latent rows (576 bf16),
+    written as E4M3 codes plus 8 fp32 tile scales per token at each token's page and slot.
+    Algorithmic bytes per call: 1152 B read + 576 + 32 B written per row (plus the tables)."""
+    import torch
+    import oracle.quant as oq
+    B, T, D = 8, 16384, 576
+    P = B * T // 64 + 1
+    gen = torch.Generator(device=dev).manual_seed(16)
+    perm = torch.randperm(P, device=dev, generator=gen).to(torch.int32)
+    bt = perm[:B * T // 64].view(B, T // 64).contiguous()
+    sl = torch.full((B,), T, dtype=torch.int32, device=dev)
+    nbytes = B * T * (D * 2 + D + 32) + bt.numel() * 4
+    R = max(1, math.ceil(args.rotate_gib * 2 ** 30 / nbytes))
+    srcs = [(torch.randn(B, T, D, device=dev, generator=gen) / 24).to(torch.bfloat16) for _ in range(R)]
+    kcs = [torch.empty(P, 64, D, dtype=torch.uint8, device=dev) for _ in range(R)]
+    kss = [torch.empty(P, 64, 8, dtype=torch.float32, device=dev) for _ in range(R)]
+    log(f"latent fp8 append: B={B} T={T}, {nbytes / 1e6:.1f} MB per call, {R} rotation copies")
+
+    def step(i):
+        j = i % R
+        dsa.dsa_latent_cache_append_fp8(srcs[j], kcs[j], kss[j], bt, sl, max_seq_len=T, num_pages=P)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"timed {args.steps} calls: {ms * 1e3:.1f} us/call, {gbs:.1f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's quantiser on the first rows of one call (NumPy float32 / float64)
+        x = srcs[0].float().cpu().numpy().reshape(-1, D)
+        rows, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            oq.latent_fp8_quantize_rows(x[rows % (B * T):rows % (B * T) + 1024])
+            rows += 1024
+        el = time.perf_counter() - t0
+        cpu = {"value": round(rows / el * D * 2 / 1e9, 4), "unit": "GB/s (bf16 read)", "cores": 1,
+               "kind": "oracle", "sample": f"{rows} rows of one call in {el:.1f} s"}
+    print(json.dumps({
+        "metric": "FP8 latent-cache append throughput", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"latent cache append B={B} T={T} dim={D}, page 64, permuted pages",
+                   "rotation_copies": R},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kv8_append_rows", "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu}), flush=True)
 
 
 def bench_append(args, dev, dsa):

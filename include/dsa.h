@@ -205,6 +205,18 @@ dsa_status dsa_sparse_attn_fp8kv(const void *q, const void *kv_codes, const floa
                                  const dsa_attn_shape *shape, void *out, float *lse, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* FP8 latent-cache append (the prolog step that writes a step's new latent rows into the cache
+ * that dsa_sparse_attn_fp8kv reads; [P1] §4: FP8 SFA cache with per-token scales over tiles of
+ * 128).  kv_new [batch, T, 576] bf16 (16-byte aligned): token t of sequence b is logical position
+ * seq_lens[b] - T + t, written to page block_table[b, pos / 64], slot pos % 64 of kv_codes
+ * [num_pages, 64, 576] E4M3 and kv_scale [num_pages, 64, 8] fp32 (both 16-byte aligned).  Per
+ * token and per 128-column tile (0-127, ..., 384-511, 512-575): scale = amax / 448 (1 for an
+ * all-zero tile), code = E4M3(x / scale), both divisions fp32 nearest even, codes nearest even and
+ * clamped to +-448; scale entries 5-7 are set to 1.  Finite inputs.  seq_lens must already count
+ * the T new tokens.  Errors as for dsa_indexer_cache_append. */
+dsa_status dsa_latent_cache_append_fp8(const void *kv_new, const dsa_paged_layout *layout, int32_t T,
+                                       void *kv_codes, float *kv_scale, hipStream_t stream);
+
 /* Opt-in per-kernel timing (off by default).  dsa_profile_start() turns recording on for the
  * calling thread: each kernel the library then launches from this thread is bracketed by two
  * hipEvents on its stream (events come from a reusable host-side pool; no device memory).

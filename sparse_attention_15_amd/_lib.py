@@ -56,7 +56,7 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_profile_start",
+           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_profile_start",
            "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_cache_append.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
                                            vp, vp, vp]
     L.dsa_indexer_cache_append.restype = ctypes.c_int
+    L.dsa_latent_cache_append_fp8.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, vp, vp, vp]
+    L.dsa_latent_cache_append_fp8.restype = ctypes.c_int
     L.dsa_last_error.argtypes = []
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_debug_status.argtypes = [vp]
@@ -186,6 +188,19 @@ def dsa_indexer_cache_append(k_new, k_cache, k_scale, block_table, seq_lens, *, 
     _check(lib().dsa_indexer_cache_append(_ptr(k_new), ctypes.byref(layout), T, dim, _ptr(k_cache),
                                           _ptr(k_scale), _stream(stream)))
     return k_cache, k_scale
+
+
+def dsa_latent_cache_append_fp8(kv_new, kv_codes, kv_scale, block_table, seq_lens, *, max_seq_len: int,
+                                num_pages: int | None = None, stream=None):
+    """Appends kv_new [B, T, 576] bf16 (the T newest latent rows of each sequence) to the FP8 latent
+    cache kv_codes [P, 64, 576] uint8 / kv_scale [P, 64, 8] fp32, in place."""
+    assert kv_new.dtype == torch.bfloat16 and kv_new.is_contiguous() and kv_new.shape[-1] == 576
+    B, T, _ = kv_new.shape
+    P = kv_codes.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    _check(lib().dsa_latent_cache_append_fp8(_ptr(kv_new), ctypes.byref(layout), T, _ptr(kv_codes),
+                                             _ptr(kv_scale), _stream(stream)))
+    return kv_codes, kv_scale
 
 
 def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float, max_seq_len: int,

@@ -173,6 +173,26 @@ dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* l
   return DSA_OK;
 }
 
+dsa_status dsa_latent_cache_append_fp8(const void* kv_new, const dsa_paged_layout* layout, int32_t T,
+                                       void* kv_codes, float* kv_scale, hipStream_t stream) {
+  if (T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", T);
+  dsa_status st = check_layout(layout, T);
+  if (st != DSA_OK) return st;
+  if (kv_new == nullptr || kv_codes == nullptr || kv_scale == nullptr)
+    return fail(DSA_ERR_NULL, "kv_new / kv_codes / kv_scale is NULL");
+  if (!aligned(kv_new, 16) || !aligned(kv_codes, 16) || !aligned(kv_scale, 16))
+    return fail(DSA_ERR_ALIGN, "kv_new / kv_codes / kv_scale need 16-byte alignment");
+  if ((long long)layout->batch * T > 0x7FFFFFFFLL) return fail(DSA_ERR_SHAPE, "batch * T exceeds 2^31 - 1");
+  dsa::Kv8Launch q;
+  q.src = kv_new; q.codes = kv_codes; q.scales = kv_scale;
+  q.block_table = layout->block_table; q.seq_lens = layout->seq_lens;
+  q.rows = (long long)layout->batch * T; q.T = T;
+  q.max_pages = layout->max_pages; q.num_pages = layout->num_pages; q.max_seq_len = layout->max_seq_len;
+  const hipError_t e = dsa::launch_kv8_append(q, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "latent cache append launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout* layout, const dsa_attn_shape* shape) {
   if (check_attn_shape(shape) != DSA_OK || check_layout(layout, shape->T) != DSA_OK) return 0;
   return dsa::plan_attn(*layout, *shape).total;

@@ -54,6 +54,17 @@ hipError_t attn_take_input_flags(uint32_t* flags);
 hipError_t quant_take_input_flags(uint32_t* flags);
 
 // MXFP8 quantisation of bf16 rows (quant.hip): to contiguous rows, or appended to the paged cache.
+struct Kv8Launch {
+  const void* src;          // [B * T, 576] bf16
+  void* codes;              // [P, 64, 576] E4M3
+  float* scales;            // [P, 64, 8] fp32
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  long long rows;
+  int T, max_pages, num_pages, max_seq_len;
+};
+hipError_t launch_kv8_append(const Kv8Launch& q, hipStream_t stream);
+
 struct QuantLaunch {
   const void* src;            // bf16 [rows, dim]
   void* codes;                // E4M3 destination

@@ -1,6 +1,6 @@
-// quant.hip -- MXFP8 quantisation of indexer rows for gfx950: the step that writes the new keys of
-// a decode or prefill step into the paged MXFP8 indexer-K cache, and the same quantiser for the
-// indexer queries.
+// quant.hip -- quantisation kernels of the prolog for gfx950: MXFP8 indexer rows (the step that
+// writes the new keys of a decode or prefill step into the paged MXFP8 indexer-K cache, and the
+// same quantiser for the indexer queries), and the FP8 latent-row append for the SFA cache.
 //
 // Pages: "Inference Optimization for Kimi K3.1 Pro: Decoding Architecture Evolution and Systems
 // Engineering Practices" §3 (the indexer prolog produces the indexer q and k and writes k into the
@@ -79,6 +79,151 @@ __global__ __launch_bounds__(256) void mx_quant_rows(QuantArgs a) {
   dst[0] = out[0];
   dst[1] = out[1];
   a.scales[row * G + g] = (unsigned char)(s + 127);
+}
+
+// FP8 latent rows ("Inference Optimization for Kimi K3.1 Pro" §4: the SFA cache in FP8 with
+// per-token scales over 128-wide tiles).  Per token and per 128-column tile of the 576-wide row
+// (columns 0-127, ..., 384-511 and the rope remainder 512-575): scale = amax / 448 (1 for an
+// all-zero tile), codes = E4M3 of x / scale (both divisions rounded to nearest even, the
+// conversion nearest even, clamped to +-448).  One wave per 8 rows: for each row lane l holds
+// columns 8l..8l+7 of the value part (a value tile's amax is a max over 16 lanes), and lane l also
+// holds columns 512 + 8(l % 8).. of row l / 8 (a rope tile's amax is a max over 8 lanes).
+struct Kv8Args {
+  const uint16_t* src;        // [rows, 576] bf16, row = b * T + t
+  unsigned char* codes;       // [P, 64, 576]
+  float* scales;              // [P, 64, 8]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  long long rows;
+  int T, max_pages, num_pages, max_seq_len;
+};
+
+__device__ __forceinline__ void bf16x8_to_f32(const u32x4 v, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = __uint_as_float(v[j] << 16);
+    x[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ uint2 e4m3x8_scaled(const float (&x)[8], float sc) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(__fdiv_rn(x[i], sc), -448.f), 448.f);
+  return make_uint2(e4m3x4(y[0], y[1], y[2], y[3]), e4m3x4(y[4], y[5], y[6], y[7]));
+}
+
+constexpr int kKv8RowsPerWave = 8;   // rows per wave: lane l also holds rope chunk l % 8 of row l / 8
+
+// Max over each row of 16 lanes, left in every lane of the row (DPP: swap neighbours, swap pairs,
+// rotate the row by 4 and by 8).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true)));
+  return v;
+}
+
+// Max over each group of 8 lanes (swap neighbours, swap pairs, mirror the half row).
+__device__ __forceinline__ float row8_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true)));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
+  constexpr int RPW = kKv8RowsPerWave;
+  const long long r0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+  const int lane = threadIdx.x & 63;
+  if (r0 >= a.rows) return;                                  // whole waves
+  auto row_of = [&](int i) { return (int)(r0 + i < a.rows ? r0 + i : r0); };   // past the end: row r0
+  // The table lookups of all rows go out together with the row loads, so a wave waits for memory
+  // twice (lengths, then pages and rows), not twice per row.  Rows < 2^31: checked by the host.
+  int sl[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) sl[i] = a.seq_lens[row_of(i) / a.T];
+  u32x4 v[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) v[i] = *reinterpret_cast<const u32x4*>(a.src + (size_t)row_of(i) * kDimQK + 8 * lane);
+  const int ri = lane >> 3;                                  // this lane's rope row and chunk
+  const u32x4 vr = *reinterpret_cast<const u32x4*>(a.src + (size_t)row_of(ri) * kDimQK + kDimV + 8 * (lane & 7));
+  // token t of sequence b is logical position seq_len - T + t; a length outside [T, cap] is
+  // flagged and clamped, as everywhere in the library
+  int pg[RPW], slot[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = row_of(i);
+    const int b = r / a.T, t = r % a.T;
+    int L = sl[i];
+    if (L < a.T || L > a.max_seq_len) {
+      flag_input(kFlagLen);
+      L = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+    }
+    const int n = max(L - a.T + t + 1, 0);
+    const int pos = n > 0 ? n - 1 : 0;
+    pg[i] = a.block_table[(size_t)b * a.max_pages + pos / kPage];
+    slot[i] = pos % kPage;
+  }
+  long long dst_row[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) dst_row[i] = (long long)clamp_page(pg[i], a.num_pages) * kPage + slot[i];
+
+  // rope tiles of the wave's 8 rows, one chunk per lane
+  float xr[8];
+  bf16x8_to_f32(vr, xr);
+  float amr = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) amr = fmaxf(amr, fabsf(xr[j]));
+  amr = row8_max(amr);
+  const float scr = amr > 0.f ? __fdiv_rn(amr, 448.f) : 1.f;
+  if (r0 + ri < a.rows) {
+    long long dr = dst_row[0];
+#pragma unroll
+    for (int i = 1; i < RPW; ++i) dr = ri == i ? dst_row[i] : dr;
+    *reinterpret_cast<uint2*>(a.codes + dr * kDimQK + kDimV + 8 * (lane & 7)) = e4m3x8_scaled(xr, scr);
+  }
+
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (r0 + i >= a.rows) break;                             // wave-uniform
+    float x[8];
+    bf16x8_to_f32(v[i], x);
+    float am = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+    am = row16_max(am);                                      // lanes 16k..16k+15: value tile k
+    const float sc = am > 0.f ? __fdiv_rn(am, 448.f) : 1.f;
+    // scale row: value tiles 0-3 (from lanes 0, 16, 32, 48), the rope tile (lane 8i), then 1
+    float s_out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(scr), 8 * i));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 16 * k));
+      s_out = lane == k ? sk : s_out;
+    }
+    s_out = lane > 4 ? 1.f : s_out;
+    *reinterpret_cast<uint2*>(a.codes + dst_row[i] * kDimQK + 8 * lane) = e4m3x8_scaled(x, sc);
+    if (lane < 8) a.scales[dst_row[i] * 8 + lane] = s_out;
+  }
+}
+
+hipError_t launch_kv8_append(const Kv8Launch& q, hipStream_t st) {
+  Kv8Args a;
+  a.src = static_cast<const uint16_t*>(q.src);
+  a.codes = static_cast<unsigned char*>(q.codes);
+  a.scales = q.scales;
+  a.block_table = q.block_table;
+  a.seq_lens = q.seq_lens;
+  a.rows = q.rows;
+  a.T = q.T; a.max_pages = q.max_pages; a.num_pages = q.num_pages; a.max_seq_len = q.max_seq_len;
+  if (q.rows == 0) return hipSuccess;
+  const long long blocks = (q.rows + 4 * kKv8RowsPerWave - 1) / (4 * kKv8RowsPerWave);
+  {
+    LaunchScope ls("kv8_cache_append", st);
+    hipLaunchKernelGGL(kv8_append_rows, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t quant_take_input_flags(uint32_t* flags) {

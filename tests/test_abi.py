@@ -110,6 +110,14 @@ def test_attn_rejects(kw, status):
     assert _attn_call(**kw) == status
 
 
+def test_latent_append_rejects():
+    lib = dsa.lib()
+    assert lib.dsa_latent_cache_append_fp8(None, ctypes.byref(_layout()), 1, FAKE, FAKE, None) == 1
+    assert lib.dsa_latent_cache_append_fp8(FAKE, ctypes.byref(_layout()), 1, FAKE, FAKE + 4, None) == 3
+    assert lib.dsa_latent_cache_append_fp8(FAKE, ctypes.byref(_layout()), 0, FAKE, FAKE, None) == 2
+    assert lib.dsa_latent_cache_append_fp8(FAKE, ctypes.byref(_layout(B=0)), 1, FAKE, FAKE, None) == 2
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(kvs=None), 1), (dict(kv=None), 1), (dict(kvs=FAKE + 4), 3), (dict(kv=FAKE + 8), 3),
     (dict(shape=_ashape(H=100)), 4), (dict(shape=_ashape(K=2048), ws=None), 5),

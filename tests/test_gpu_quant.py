@@ -95,3 +95,61 @@ def test_prolog_then_indexer_end_to_end():
     ref, extra = oracle.indexer_topk_ref(**args, T=1, K=spec.K, dtype="mxfp8", return_scores=True)
     from tests._gpu import check_indices_band
     check_indices_band(got, ref, extra, spec.K, c.seq_lens, 1)
+
+
+# ---------------------------------------------------------------- FP8 latent-cache append
+from oracle.quant import latent_cache_append_fp8_ref  # noqa: E402
+
+
+def _latent_rows(B, T, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((B, T, 576)) * 10.0 ** rng.integers(-5, 3, (B, T, 5)).repeat(
+        [128, 128, 128, 128, 64], axis=-1)).astype(np.float32)
+    x[0, 0, :128] = 0.0                                   # an all-zero tile
+    x[0, -1, 512:] *= 1e-5                                # rope tile far below the value tiles
+    x[-1, 0, 3] = -0.0
+    x[-1, -1, 130] = np.float32(448.0) * np.float32(2.0 ** -7)
+    return W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("B,T,lens", [(3, 1, (70, 1, 3000)), (2, 5, (64, 4100)), (1, 300, (300,))])
+def test_latent_fp8_append_bit_exact(B, T, lens):
+    print(f"[case] latent fp8 append B={B} T={T} lens={lens}", flush=True)
+    spec = W.custom("kv8_append", B, 1, lens, 8, 64, 64, 16, kv_dtype="fp8")
+    c = W.make_case(spec, poison=False)
+    new = _latent_rows(B, T, seed=B * 7 + T)
+    codes_d, scale_d = up(c.kv_codes), up(c.kv_scale)
+    dsa.dsa_latent_cache_append_fp8(up(new), codes_d, scale_d, up(c.block_table), up(c.seq_lens),
+                                    max_seq_len=spec.max_len, num_pages=c.num_pages)
+    torch.cuda.synchronize()
+    kc_ref, ks_ref = latent_cache_append_fp8_ref(_decode_bf16(new).astype(np.float32), c.kv_codes,
+                                                 c.kv_scale, c.block_table, c.seq_lens, T)
+    np.testing.assert_array_equal(codes_d.cpu().numpy(), kc_ref)
+    np.testing.assert_array_equal(scale_d.cpu().numpy().view(np.uint32), ks_ref.view(np.uint32))
+
+
+def test_latent_fp8_append_then_attend():
+    """Appended rows are read back by the FP8-cache attention like the generator's own rows."""
+    spec = W.custom("kv8_append_attn", 2, 1, (2600, 4100), 8, 64, 64, 128, kv_dtype="fp8")
+    c = W.make_case(spec, poison=False)
+    T = 40
+    # unit-scale rows like the generator's (N(0, 1) / 24): the attention gates assume that scale
+    rng0 = np.random.default_rng(5)
+    new = W.f32_to_bf16_bits((rng0.standard_normal((2, T, 576)) / 24).astype(np.float32))
+    codes_d, scale_d = up(c.kv_codes), up(c.kv_scale)
+    dsa.dsa_latent_cache_append_fp8(up(new), codes_d, scale_d, up(c.block_table), up(c.seq_lens),
+                                    max_seq_len=spec.max_len, num_pages=c.num_pages)
+    kc, ks = latent_cache_append_fp8_ref(_decode_bf16(new).astype(np.float32), c.kv_codes, c.kv_scale,
+                                         c.block_table, c.seq_lens, T)
+    rng = np.random.default_rng(6)
+    idx = np.full((2, 1, 64), -1, np.int32)
+    for b in range(2):
+        n = int(c.seq_lens[b])
+        idx[b, 0] = np.sort(np.r_[np.arange(n - T, n), rng.choice(n - T, 24, replace=False)])
+    out, lse = dsa.dsa_sparse_attn_fp8kv(up(c.q_attn), codes_d, scale_d, up(idx), up(c.block_table),
+                                         up(c.seq_lens), sm_scale=spec.sm_scale, max_seq_len=spec.max_len,
+                                         num_pages=c.num_pages)
+    torch.cuda.synchronize()
+    from tests._gpu import check_attn
+    o_ref, l_ref = oracle.sparse_attn_fp8kv_ref(c.q_attn, kc, ks, c.block_table, c.seq_lens, idx, spec.sm_scale)
+    check_attn(to_np(out), to_np(lse), o_ref, l_ref)
