@@ -49,3 +49,57 @@ def test_decode_indexer_graph_replays(cfg):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(to_np(out), ref, err_msg=f"replay {r}")
         assert (ref[:, 0, :] >= 0).sum() > 0
+
+
+def test_fp8_latent_append_and_attention_graph_replays():
+    """The FP8 latent-cache append followed by the FP8-cache attention, captured once and replayed
+    on new rows and queries (eager work and synchronisations between replays); every replay must
+    equal the eager calls bit for bit."""
+    spec = W.custom("kv8_graph", 2, 1, (2600, 4100), 8, 64, 256, 128, kv_dtype="fp8")
+    print(f"[case] graph {spec.name}", flush=True)
+    c = W.make_case(spec, poison=False)
+    d = Dev(c)
+    T = 16
+    dev = d.q_attn.device
+    rng = np.random.default_rng(8)
+    idx = np.full((2, 1, spec.K), -1, np.int32)
+    for b in range(2):
+        n = int(c.seq_lens[b])
+        idx[b, 0, :200] = np.sort(np.r_[np.arange(n - T, n), rng.choice(n - T, 184, replace=False)])
+    idx_t = torch.from_numpy(idx).to(dev)
+    new = torch.empty((2, T, 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((2, 1, spec.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((2, 1, spec.H), dtype=torch.float32, device=dev)
+    layout = dsa.make_layout(d.bt, d.sl, c.num_pages, spec.max_len)
+    ws = torch.empty(max(256, dsa.dsa_sparse_attn_workspace_size(
+        layout, dsa.AttnShape(1, spec.H, 576, 512, spec.K, spec.sm_scale))), dtype=torch.uint8, device=dev)
+
+    def calls(o, l):
+        dsa.dsa_latent_cache_append_fp8(new, d.kv, d.kv_scale, d.bt, d.sl, max_seq_len=spec.max_len,
+                                        num_pages=c.num_pages)
+        d.attn(idx_t, out=o, lse=l, workspace=ws)
+
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    new.copy_((torch.randn((2, T, 576), generator=gen) / 24).to(torch.bfloat16))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls(out, lse)                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(out, lse)
+    torch.cuda.synchronize()
+    q0 = d.q_attn.clone()
+    for r in range(4):
+        new.copy_((torch.randn((2, T, 576), generator=gen) / 24).to(torch.bfloat16))
+        d.q_attn.copy_(q0 * (1.0 + 0.25 * r))
+        o_ref = torch.empty_like(out)
+        l_ref = torch.empty_like(lse)
+        calls(o_ref, l_ref)                               # eager on the same buffers
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}"
+        assert torch.equal(lse, l_ref), f"replay {r}"
