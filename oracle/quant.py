@@ -15,6 +15,10 @@ how the prolog fills it): per token and per 128-column tile of the 576-wide row 
 ..., 384-511, 512-575), scale = amax / 448 in float32 (1 for an all-zero tile), element code =
 E4M3 of float32(x / scale) (nearest even, clamped to +-448).  Both divisions are single float32
 operations, rounded to nearest even.
+
+Per-head fp8 queries ([P1] §3: the prolog quantises the indexer q and folds the head weights in;
+reading): per query row and head, sq = amax / 448 in float32 (1 for an all-zero head), code = E4M3
+of float32(q / sq); the indexer then weights head h by w[t, h] * sq[t, h].
 """
 import numpy as np
 
@@ -99,3 +103,13 @@ def latent_cache_append_fp8_ref(kv_new, kv_codes, kv_scale, block_table, seq_len
             kc[p, slot] = codes[b, t]
             ks[p, slot] = sc[b, t]
     return kc, ks
+
+
+def fp8_quantize_heads(x):
+    """x [..., d] finite (one head row per leading index) -> (codes uint8 [..., d], scales float32
+    [...]): per row sq = amax / 448 (1 for zeros), code = E4M3 of float32(x / sq)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    sq = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / sq[..., None]).astype(np.float32)
+    return _e4m3_rne(y.astype(np.float64)), sq

@@ -164,3 +164,30 @@ def test_latent_fp8_append_positions():
             touched[p, s] = True
     np.testing.assert_array_equal(kc2[~touched], kc[~touched])
     np.testing.assert_array_equal(ks2[~touched], ks[~touched])
+
+
+# ---------------------------------------------------------------- per-head fp8 queries ([P1] §3)
+from oracle.quant import fp8_quantize_heads  # noqa: E402
+
+
+def test_fp8_heads_match_torch_cast():
+    rng = np.random.default_rng(31)
+    x = _bits_to_f32(_bf16_rows(rng, (500, 128), 10.0 ** rng.integers(-4, 3, (500, 1))))
+    x[0] = 0.0
+    codes, sq = fp8_quantize_heads(x)
+    t = torch.from_numpy(x)
+    amax = t.abs().amax(-1)
+    s_t = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    c_t = (t / s_t[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(sq, s_t.numpy())
+    np.testing.assert_array_equal(codes, c_t)
+
+
+def test_fp8_heads_closed_forms():
+    x = np.zeros((3, 64), np.float32)
+    x[0, 7] = -448.0                               # scale 1, code of -448
+    x[1, :] = 2.0 ** -10                           # uniform row: every code is 448
+    codes, sq = fp8_quantize_heads(x)
+    assert sq.tolist() == [1.0, np.float32(2.0 ** -10) / np.float32(448.0), 1.0]
+    assert e4m3_codes_to_f64(codes[0, 7:8])[0] == -448.0 and (codes[0, :7] == 0).all()
+    assert (e4m3_codes_to_f64(codes[1]) == 448.0).all() and (codes[2] == 0).all()
