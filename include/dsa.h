@@ -205,6 +205,16 @@ dsa_status dsa_sparse_attn_fp8kv(const void *q, const void *kv_codes, const floa
                                  const dsa_attn_shape *shape, void *out, float *lse, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream);
 
+/* Per-head fp8 quantisation of indexer queries for DSA_FP8_E4M3 ([P1] §3: the prolog quantises the
+ * indexer q; dsa_indexer_topk folds each head's weight and scale together, w * sq, when it loads a
+ * query row).  x [rows, dim] bf16 (rows = batch * T * heads, one head row each; dim 64 or 128;
+ * 16-byte aligned) -> codes [rows, dim] E4M3FN (16-byte aligned) and scales [rows] fp32 (the
+ * q_scale of dsa_indexer_topk): per row sq = amax / 448 (1 for an all-zero row), code = E4M3(x / sq),
+ * both divisions fp32 nearest even, codes nearest even, clamped to +-448.  Finite inputs.  rows = 0
+ * is a no-op.  DSA_ERR_UNSUPPORTED for another dim, DSA_ERR_NULL / DSA_ERR_ALIGN as named. */
+dsa_status dsa_fp8_quantize_heads(const void *x, int64_t rows, int32_t dim, void *codes, float *scales,
+                                  hipStream_t stream);
+
 /* FP8 latent-cache append (the prolog step that writes a step's new latent rows into the cache
  * that dsa_sparse_attn_fp8kv reads; [P1] §4: FP8 SFA cache with per-token scales over tiles of
  * 128).  kv_new [batch, T, 576] bf16 (16-byte aligned): token t of sequence b is logical position

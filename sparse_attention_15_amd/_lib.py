@@ -56,7 +56,7 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_profile_start",
+           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_fp8_quantize_heads", "dsa_profile_start",
            "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_cache_append.restype = ctypes.c_int
     L.dsa_latent_cache_append_fp8.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, vp, vp, vp]
     L.dsa_latent_cache_append_fp8.restype = ctypes.c_int
+    L.dsa_fp8_quantize_heads.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    L.dsa_fp8_quantize_heads.restype = ctypes.c_int
     L.dsa_last_error.argtypes = []
     L.dsa_last_error.restype = ctypes.c_char_p
     L.dsa_debug_status.argtypes = [vp]
@@ -188,6 +190,20 @@ def dsa_indexer_cache_append(k_new, k_cache, k_scale, block_table, seq_lens, *, 
     _check(lib().dsa_indexer_cache_append(_ptr(k_new), ctypes.byref(layout), T, dim, _ptr(k_cache),
                                           _ptr(k_scale), _stream(stream)))
     return k_cache, k_scale
+
+
+def dsa_fp8_quantize_heads(x, codes=None, scales=None, stream=None):
+    """Per-head fp8 quantisation of indexer queries x [..., dim] bf16 (dim 64 or 128).  Returns
+    (codes uint8 [..., dim], scales fp32 [...]): the q and q_scale of the fp8 indexer."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    dim = x.shape[-1]
+    rows = x.numel() // dim
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib().dsa_fp8_quantize_heads(_ptr(x), rows, dim, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 def dsa_latent_cache_append_fp8(kv_new, kv_codes, kv_scale, block_table, seq_lens, *, max_seq_len: int,

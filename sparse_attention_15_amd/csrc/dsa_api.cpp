@@ -173,6 +173,20 @@ dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* l
   return DSA_OK;
 }
 
+dsa_status dsa_fp8_quantize_heads(const void* x, int64_t rows, int32_t dim, void* codes, float* scales,
+                                  hipStream_t stream) {
+  if (rows < 0) return fail(DSA_ERR_SHAPE, "rows %lld < 0", (long long)rows);
+  if (rows > (1LL << 40)) return fail(DSA_ERR_SHAPE, "rows %lld too large", (long long)rows);
+  if (dim != 64 && dim != 128) return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (64 or 128)", dim);
+  if (rows == 0) return DSA_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return fail(DSA_ERR_NULL, "x / codes / scales is NULL");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(DSA_ERR_ALIGN, "x / codes need 16-byte alignment, scales 4-byte");
+  const hipError_t e = dsa::launch_fp8_heads(x, rows, dim, codes, scales, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "fp8 head quantisation launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
 dsa_status dsa_latent_cache_append_fp8(const void* kv_new, const dsa_paged_layout* layout, int32_t T,
                                        void* kv_codes, float* kv_scale, hipStream_t stream) {
   if (T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", T);

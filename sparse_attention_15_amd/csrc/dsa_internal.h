@@ -64,6 +64,8 @@ struct Kv8Launch {
   int T, max_pages, num_pages, max_seq_len;
 };
 hipError_t launch_kv8_append(const Kv8Launch& q, hipStream_t stream);
+hipError_t launch_fp8_heads(const void* src, long long rows, int dim, void* codes, float* scales,
+                            hipStream_t stream);
 
 struct QuantLaunch {
   const void* src;            // bf16 [rows, dim]

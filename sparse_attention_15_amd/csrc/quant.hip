@@ -208,6 +208,57 @@ __global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
   }
 }
 
+// Per-head fp8 queries ("Inference Optimization for Kimi K3.1 Pro" §3: the prolog quantises the
+// indexer q; the indexer folds the head weights and these scales together, w * sq, when it loads a
+// query row): per head row sq = amax / 448 (1 for an all-zero row), codes = E4M3 of q / sq (both
+// divisions nearest even, codes nearest even, clamped to +-448).  D / 8 lanes per head row (a DPP
+// max over 8 or 16 lanes), 64 / (D / 8) rows per wave.
+struct HeadArgs {
+  const uint16_t* src;        // [rows, D] bf16
+  unsigned char* codes;       // [rows, D] E4M3
+  float* scales;              // [rows]
+  long long rows;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fp8_quant_heads(HeadArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPW = 64 / LPR;
+  static_assert(LPR == 8 || LPR == 16, "head dims 64 and 128");
+  const int lane = threadIdx.x & 63;
+  const long long r = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int c = lane % LPR;
+  const bool valid = r < a.rows;
+  const long long rr = valid ? r : 0;                        // lanes past the end read row 0
+  float x[8];
+  bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.src + rr * D + 8 * c), x);
+  float am = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(x[j]));
+  am = LPR == 16 ? row16_max(am) : row8_max(am);
+  const float sq = am > 0.f ? __fdiv_rn(am, 448.f) : 1.f;
+  if (valid) {
+    *reinterpret_cast<uint2*>(a.codes + rr * D + 8 * c) = e4m3x8_scaled(x, sq);
+    if (c == 0) a.scales[rr] = sq;
+  }
+}
+
+hipError_t launch_fp8_heads(const void* src, long long rows, int dim, void* codes, float* scales,
+                            hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  HeadArgs a;
+  a.src = static_cast<const uint16_t*>(src);
+  a.codes = static_cast<unsigned char*>(codes);
+  a.scales = scales;
+  a.rows = rows;
+  const long long per_block = 4LL * (64 / (dim / 8));
+  const long long blocks = (rows + per_block - 1) / per_block;
+  LaunchScope ls("fp8_quant_heads", st);
+  if (dim == 128) hipLaunchKernelGGL(fp8_quant_heads<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(fp8_quant_heads<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv8_append(const Kv8Launch& q, hipStream_t st) {
   Kv8Args a;
   a.src = static_cast<const uint16_t*>(q.src);

@@ -110,6 +110,15 @@ def test_attn_rejects(kw, status):
     assert _attn_call(**kw) == status
 
 
+def test_fp8_heads_rejects():
+    lib = dsa.lib()
+    assert lib.dsa_fp8_quantize_heads(FAKE, 4, 96, FAKE, FAKE, None) == 4
+    assert lib.dsa_fp8_quantize_heads(None, 4, 128, FAKE, FAKE, None) == 1
+    assert lib.dsa_fp8_quantize_heads(FAKE + 8, 4, 128, FAKE, FAKE, None) == 3
+    assert lib.dsa_fp8_quantize_heads(FAKE, -1, 128, FAKE, FAKE, None) == 2
+    assert lib.dsa_fp8_quantize_heads(None, 0, 64, None, None, None) == 0
+
+
 def test_latent_append_rejects():
     lib = dsa.lib()
     assert lib.dsa_latent_cache_append_fp8(None, ctypes.byref(_layout()), 1, FAKE, FAKE, None) == 1

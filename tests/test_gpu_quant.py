@@ -13,7 +13,7 @@ import oracle
 import sparse_attention_15_amd as dsa
 import workloads as W
 from oracle.quant import cache_append_ref, mxfp8_quantize_rows
-from tests._gpu import DEV, oracle_args, to_np, up
+from tests._gpu import DEV, Dev, oracle_args, to_np, up
 
 pytestmark = pytest.mark.gpu
 
@@ -153,3 +153,42 @@ def test_latent_fp8_append_then_attend():
     from tests._gpu import check_attn
     o_ref, l_ref = oracle.sparse_attn_fp8kv_ref(c.q_attn, kc, ks, c.block_table, c.seq_lens, idx, spec.sm_scale)
     check_attn(to_np(out), to_np(lse), o_ref, l_ref)
+
+
+# ---------------------------------------------------------------- per-head fp8 queries
+from oracle.quant import fp8_quantize_heads  # noqa: E402
+
+
+@pytest.mark.parametrize("rows,dim", [(1, 64), (37, 128), (4099, 64), (2050, 128)])
+def test_fp8_heads_bit_exact(rows, dim):
+    print(f"[case] fp8 heads rows={rows} dim={dim}", flush=True)
+    rng = np.random.default_rng(rows + dim)
+    x = (rng.standard_normal((rows, dim)) * 10.0 ** rng.integers(-6, 4, (rows, 1))).astype(np.float32)
+    x[::9] = 0.0
+    x[1::7, 1:] *= 1e-5
+    x[2::11, 5] = -0.0
+    bits = W.f32_to_bf16_bits(x)
+    codes, sc = dsa.dsa_fp8_quantize_heads(up(bits))
+    torch.cuda.synchronize()
+    c_ref, s_ref = fp8_quantize_heads(_decode_bf16(bits).astype(np.float32))
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_fp8_heads_feed_the_fp8_indexer():
+    """Queries quantised on the device drive the fp8 indexer to the oracle's selection on the same
+    codes and scales."""
+    spec = W.config(4, "small")
+    c = W.make_case(spec)
+    rng = np.random.default_rng(41)
+    qf = W.f32_to_bf16_bits((rng.standard_normal((spec.B, spec.T, spec.HI, spec.DI)) / np.sqrt(spec.DI)).astype(np.float32))
+    codes, sq = dsa.dsa_fp8_quantize_heads(up(qf))
+    d = Dev(c)
+    d.q_idx, d.q_scale = codes, sq
+    idx = to_np(d.indexer())
+    torch.cuda.synchronize()
+    import dataclasses
+    c2 = dataclasses.replace(c, q_idx=codes.cpu().numpy(), q_scale=sq.cpu().numpy())
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c2), T=1, K=spec.K, dtype="fp8", return_scores=True)
+    from tests._gpu import check_indices_band
+    check_indices_band(idx, ref, extra, spec.K, c.seq_lens, 1)
