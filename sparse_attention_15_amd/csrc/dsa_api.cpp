@@ -137,6 +137,9 @@ dsa_status dsa_indexer_topk(const void* q, const void* q_scale, const float* w, 
   return DSA_OK;
 }
 
+// One thread per 32-element group, 256 per block: the grid's block count must fit 31 bits.
+static constexpr long long kMaxQuantGroups = 256LL * 0x7FFFFFFFLL;
+
 dsa_status dsa_mxfp8_quantize(const void* x, int64_t rows, int32_t dim, void* codes, void* scales,
                               hipStream_t stream) {
   if (x == nullptr || codes == nullptr || scales == nullptr)
@@ -145,6 +148,7 @@ dsa_status dsa_mxfp8_quantize(const void* x, int64_t rows, int32_t dim, void* co
   if (dim < 32 || dim > 4096 || dim % 32 != 0)
     return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (a multiple of 32, 32..4096)", dim);
   if (!aligned(x, 16) || !aligned(codes, 16)) return fail(DSA_ERR_ALIGN, "x / codes need 16-byte alignment");
+  if (rows > kMaxQuantGroups / (dim / 32)) return fail(DSA_ERR_SHAPE, "rows %lld too large", (long long)rows);
   dsa::QuantLaunch q;
   q.src = x; q.codes = codes; q.scales = scales; q.rows = rows; q.dim = dim;
   const hipError_t e = dsa::launch_mx_quant(q, stream);
@@ -162,6 +166,8 @@ dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* l
   if (dim < 32 || dim > 4096 || dim % 32 != 0)
     return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (a multiple of 32, 32..4096)", dim);
   if (!aligned(k_new, 16) || !aligned(k_cache, 16)) return fail(DSA_ERR_ALIGN, "k_new / k_cache need 16-byte alignment");
+  if ((long long)layout->batch * T > kMaxQuantGroups / (dim / 32))
+    return fail(DSA_ERR_SHAPE, "batch * T = %lld rows too large", (long long)layout->batch * T);
   dsa::QuantLaunch q;
   q.src = k_new; q.codes = k_cache; q.scales = k_scale;
   q.block_table = layout->block_table; q.seq_lens = layout->seq_lens;
@@ -176,7 +182,7 @@ dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* l
 dsa_status dsa_fp8_quantize_heads(const void* x, int64_t rows, int32_t dim, void* codes, float* scales,
                                   hipStream_t stream) {
   if (rows < 0) return fail(DSA_ERR_SHAPE, "rows %lld < 0", (long long)rows);
-  if (rows > (1LL << 40)) return fail(DSA_ERR_SHAPE, "rows %lld too large", (long long)rows);
+  if (rows > 0x7FFFFFFFLL) return fail(DSA_ERR_SHAPE, "rows %lld too large", (long long)rows);
   if (dim != 64 && dim != 128) return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (64 or 128)", dim);
   if (rows == 0) return DSA_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return fail(DSA_ERR_NULL, "x / codes / scales is NULL");

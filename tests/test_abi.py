@@ -110,6 +110,15 @@ def test_attn_rejects(kw, status):
     assert _attn_call(**kw) == status
 
 
+def test_quantisers_reject_grids_past_31_bits():
+    lib = dsa.lib()
+    assert lib.dsa_mxfp8_quantize(FAKE, 1 << 40, 32, FAKE, FAKE, None) == 2
+    assert lib.dsa_fp8_quantize_heads(FAKE, 1 << 31, 128, FAKE, FAKE, None) == 2
+    big = L.Layout(FAKE, FAKE + 256, 1 << 30, 1 << 14, 64, 9, 1 << 20)
+    assert lib.dsa_indexer_cache_append(FAKE, ctypes.byref(big), 1 << 10, 4096, FAKE, FAKE, None) == 2
+    assert lib.dsa_latent_cache_append_fp8(FAKE, ctypes.byref(big), 1 << 10, FAKE, FAKE, None) == 2
+
+
 def test_fp8_heads_rejects():
     lib = dsa.lib()
     assert lib.dsa_fp8_quantize_heads(FAKE, 4, 96, FAKE, FAKE, None) == 4
