@@ -53,3 +53,38 @@ def test_block_table_entry_outside_the_pool_is_clamped_and_reported():
     d.indexer()
     with pytest.raises(dsa.DsaError, match="block_table"):
         dsa.dsa_debug_status()
+
+
+def test_fp8_cache_paths_record_nothing_on_valid_inputs():
+    spec = W.custom("kv8_checks", 2, 1, (300, 700), 8, 64, 64, 16, kv_dtype="fp8")
+    c = W.make_case(spec, poison=False)
+    d = Dev(c)
+    _clear()
+    new = torch.zeros((2, 3, 576), dtype=torch.bfloat16, device=d.kv.device)
+    dsa.dsa_latent_cache_append_fp8(new, d.kv, d.kv_scale, d.bt, d.sl, max_seq_len=spec.max_len,
+                                    num_pages=c.num_pages)
+    d.attn(d.indexer())
+    dsa.dsa_debug_status()
+
+
+def test_latent_append_clamps_and_reports_bad_length_and_page():
+    """A sequence length past max_seq_len is clamped to it, a page id outside the pool into it;
+    both land inside the cache and are reported."""
+    spec = W.custom("kv8_bad", 2, 1, (300, 700), 8, 64, 64, 16, kv_dtype="fp8")
+    c = W.make_case(spec, poison=False)
+    d = Dev(c)
+    new = torch.zeros((2, 2, 576), dtype=torch.bfloat16, device=d.kv.device)
+    _clear()
+    sl = d.sl.clone()
+    sl[1] = spec.max_len + 50
+    dsa.dsa_latent_cache_append_fp8(new, d.kv, d.kv_scale, d.bt, sl, max_seq_len=spec.max_len,
+                                    num_pages=c.num_pages)
+    with pytest.raises(dsa.DsaError, match="seq_lens"):
+        dsa.dsa_debug_status()
+    bt = d.bt.clone()
+    bt[0, 4] = c.num_pages + 9                   # the page of positions 256..319 (sequence 0 ends at 299)
+    dsa.dsa_latent_cache_append_fp8(new, d.kv, d.kv_scale, bt, d.sl, max_seq_len=spec.max_len,
+                                    num_pages=c.num_pages)
+    with pytest.raises(dsa.DsaError, match="block_table"):
+        dsa.dsa_debug_status()
+    dsa.dsa_debug_status()
