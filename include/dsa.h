@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DSA_VERSION 2
+#define DSA_VERSION 3             /* 3: FP8 latent cache (attention, append), per-head fp8 q quantiser */
 #define DSA_PAGE_SIZE 64          /* tokens per cache page */
 #define DSA_DIM_QK 576            /* MLA latent row: 512 "nope" + 64 rope columns */
 #define DSA_DIM_V 512             /* V = the first 512 columns of the latent row */
@@ -87,8 +87,7 @@ typedef struct {
   int32_t heads;                /* indexer heads H_I: 8, 16, 32 or 64 */
   int32_t dim;                  /* indexer head dim d_I: 64 or 128 */
   int32_t top_k;                /* K, 1..DSA_MAX_TOP_K */
-  dsa_dtype dtype;              /* storage of q and the indexer-K cache (DSA_MXFP8_E4M3: not
-                                   for T = 2..4 with batch <= 512) */
+  dsa_dtype dtype;              /* storage of q and the indexer-K cache (any T for all three) */
 } dsa_indexer_shape;
 
 typedef struct {

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert dsa.lib().dsa_version() == 2
+    assert dsa.lib().dsa_version() == 3
 
 
 def _layout(B=2, max_pages=4, max_len=256, num_pages=9, page=64):
