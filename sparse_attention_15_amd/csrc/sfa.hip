@@ -97,7 +97,6 @@ constexpr int kCodeChunks8 = kBK * kRowBytes8 / 16;     // 1152
 constexpr int kChunks8 = kCodeChunks8 + kBK * 2;        // 1216
 constexpr int kDmaPerTile8 = 20;
 constexpr int kSlotBytes8 = kDmaPerTile8 * 1024;        // 20480
-constexpr int kUnits8 = kBK * kDimQK / 8;               // 8-code conversion units per tile (2304)
 static_assert(kDmaPerTile8 * 64 >= kChunks8 && kTileBytes + 4 * kSlotBytes8 <= 4 * kTileBytes, "fp8 ring");
 
 // Waits until this wave's loads of the tile being consumed have landed; `later` of its later
@@ -240,46 +239,61 @@ void sfa_main(SfaArgs a) {
       lds_dma16(src, slot + 1024 * L);
     }
   };
-  // fp8 cache: dequantise ring slot `buf` into the bf16 tile (unit v: row v / 72, 8 codes from
-  // column 8 * (v % 72), i.e. bf16 chunk v % 72 of the row, stored at its swizzled slot).
-  // Units go in batches: a batch's LDS reads are all issued before its first conversion, so each
-  // batch waits for LDS once.
-  constexpr int kUnitsPT = kUnits8 / NT;                 // 9, 18 or 36 units per thread
-  constexpr int kBatch8 = NW == 4 ? 9 : 3;
-  static_assert(kUnits8 % NT == 0 && kUnitsPT % kBatch8 == 0, "dequant units per thread");
+  // fp8 cache: dequantise ring slot `buf` into the bf16 tile.  Value part: lane l converts codes
+  // 8l..8l+7 (bf16 chunk l) of rows wave, wave + NW, ...: the row is wave-uniform, so its swizzle
+  // and scale address are too.  Rope part: thread t converts chunk t % 8 of row t / 8 (NT <= 256:
+  // 256 / NT rounds).  All LDS reads go out before the first conversion (one wave per SIMD: nothing
+  // else hides their latency), and no offset needs a division or a branch.
+  constexpr int kValRows = kBK / NW;                      // value rows per wave
+  constexpr int kRopeRounds = (kBK * 8) / NT;             // rope units per thread
+  auto cvt8 = [&](const uint2 w, float sc) __attribute__((always_inline)) {
+    u32x4 o8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t word = h ? w.y : w.x;
+      const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      o8[2 * h] = pack_bf16(lo[0] * sc, lo[1] * sc);
+      o8[2 * h + 1] = pack_bf16(hi[0] * sc, hi[1] * sc);
+    }
+    return o8;
+  };
   auto dequant8 = [&](int buf) __attribute__((always_inline)) {
     const unsigned char* slot = &lds_kv[0][0] + kTileBytes + kSlotBytes8 * buf;
     unsigned char* dst = &lds_kv[0][0];
-    // offsets are recomputed per tile from an opaque copy of the thread id: hoisted out of the
-    // tile loop they would hold 3 registers per unit across the products
-    int t0 = tid;
-    asm volatile("" : "+v"(t0));
+    // opaque copies of the thread ids: offsets hoisted out of the tile loop would hold registers
+    // across the products
+    int ln = lane, td = tid;
+    asm volatile("" : "+v"(ln), "+v"(td));
+    constexpr int VB = kValRows < 8 ? kValRows : 8;        // value rows per batch of reads
 #pragma unroll
-    for (int j0 = 0; j0 < kUnitsPT; j0 += kBatch8) {
-      uint2 w[kBatch8];
-      float sc[kBatch8];
-      int off[kBatch8];
+    for (int j0 = 0; j0 < kValRows; j0 += VB) {
+      uint2 wv[VB];
+      float sv[VB];
 #pragma unroll
-      for (int jj = 0; jj < kBatch8; ++jj) {
-        const int v = t0 + NT * (j0 + jj);
-        const int r = v / 72, e = v % 72;
-        w[jj] = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + 8 * e);
-        sc[jj] = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 4 * min(e >> 4, 4));
-        off[jj] = e < 64 ? 1024 * r + 16 * (e ^ swa(r)) : kRegionB + 128 * r + 16 * ((e - 64) ^ swb(r));
+      for (int j = 0; j < VB; ++j) {
+        const int r = wave + NW * (j0 + j);
+        wv[j] = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + 8 * ln);
+        sv[j] = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 4 * (ln >> 4));
       }
 #pragma unroll
-      for (int jj = 0; jj < kBatch8; ++jj) {
-        u32x4 o8;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t word = h ? w[jj].y : w[jj].x;
-          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-          o8[2 * h] = pack_bf16(lo[0] * sc[jj], lo[1] * sc[jj]);
-          o8[2 * h + 1] = pack_bf16(hi[0] * sc[jj], hi[1] * sc[jj]);
-        }
-        *reinterpret_cast<u32x4*>(dst + off[jj]) = o8;
+      for (int j = 0; j < VB; ++j) {
+        const int r = wave + NW * (j0 + j);
+        *reinterpret_cast<u32x4*>(dst + 1024 * r + 16 * (ln ^ swa(r))) = cvt8(wv[j], sv[j]);
       }
+    }
+    uint2 wr[kRopeRounds];
+    float sr[kRopeRounds];
+#pragma unroll
+    for (int j = 0; j < kRopeRounds; ++j) {
+      const int u = td + NT * j, r = u >> 3;
+      wr[j] = *reinterpret_cast<const uint2*>(slot + kRowBytes8 * r + kDimV + 8 * (u & 7));
+      sr[j] = *reinterpret_cast<const float*>(slot + kBK * kRowBytes8 + 32 * r + 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kRopeRounds; ++j) {
+      const int u = td + NT * j, r = u >> 3;
+      *reinterpret_cast<u32x4*>(dst + kRegionB + 128 * r + 16 * ((u & 7) ^ swb(r))) = cvt8(wr[j], sr[j]);
     }
   };
   auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
