@@ -45,7 +45,7 @@ def visible(spec, seq_lens):
 
 
 def algorithmic_bytes(spec, seq_lens):
-    """Bytes the method must move per step (no over-fetch, no scratch): see the design doc."""
+    """Bytes the method must move per step (no over-fetch, no scratch)."""
     fp8, mx = spec.idx_dtype == "fp8", spec.idx_dtype == "mxfp8"
     elt = 1 if (fp8 or mx) else 2
     mxs = spec.DI // 32 if mx else 0      # MXFP8: one E8M0 byte per 32 elements
@@ -175,7 +175,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -49,7 +49,7 @@ typedef enum {
   DSA_ERR_NULL = 1,          /* a required pointer is NULL */
   DSA_ERR_SHAPE = 2,         /* inconsistent or out-of-range size */
   DSA_ERR_ALIGN = 3,         /* pointer not aligned as documented */
-  DSA_ERR_UNSUPPORTED = 4,   /* valid request this build has no kernel for */
+  DSA_ERR_UNSUPPORTED = 4,   /* valid request the library has no kernel for */
   DSA_ERR_WORKSPACE = 5,     /* workspace NULL or smaller than *_workspace_size */
   DSA_ERR_HIP = 6            /* the HIP runtime reported an error at launch */
 } dsa_status;
