@@ -37,6 +37,7 @@ def _row_properties(idx, spec, seq_lens):
     (6, [(0, 0), (3, 0), (7, 0)]),
     (8, [(0, 0), (0, 3), (11, 2)]),
     (9, [(0, 0), (13, 0), (31, 0)]),
+    (7, [(0, 0), (0, 2047), (0, 2048), (0, 8191)]),
 ])
 def test_full_size_sampled(cfg, rows):
     spec = W.config(cfg)

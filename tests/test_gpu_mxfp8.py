@@ -109,7 +109,7 @@ def test_mx_small_prefill_gaussian():
 
 
 # ---------------------------------------------------------------- verify kernel: 2-4 rows per sequence
-@pytest.mark.parametrize("T,lens", [(4, (3000, 4100, 2051)), (2, (2600, 70, 4545))])
+@pytest.mark.parametrize("T,lens", [(4, (3000, 4100, 2051)), (2, (2600, 70, 4545)), (3, (2300, 5000))])
 def test_mx_verify_grid_exact(T, lens):
     spec = W.custom(f"mxgrid_verify_T{T}", len(lens), T, lens, 64, 128, 2048, 16, idx_dtype="mxfp8",
                     values="mxgrid")

@@ -192,3 +192,29 @@ def test_fp8_heads_feed_the_fp8_indexer():
     ref, extra = oracle.indexer_topk_ref(**oracle_args(c2), T=1, K=spec.K, dtype="fp8", return_scores=True)
     from tests._gpu import check_indices_band
     check_indices_band(idx, ref, extra, spec.K, c.seq_lens, 1)
+
+
+def test_latent_fp8_append_bench_size_sampled():
+    """The append at the benchmark's size (8 sequences x 16384 rows into 2049 permuted pages):
+    sampled rows bit-exact against the oracle's quantiser."""
+    B, T, D = 8, 16384, 576
+    P = B * T // 64 + 1
+    gen = torch.Generator(device=DEV).manual_seed(16)
+    perm = torch.randperm(P, device=DEV, generator=gen).to(torch.int32)
+    bt = perm[:B * T // 64].view(B, T // 64).contiguous()
+    sl = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    src = (torch.randn(B, T, D, device=DEV, generator=gen) / 24).to(torch.bfloat16)
+    kc = torch.zeros(P, 64, D, dtype=torch.uint8, device=DEV)
+    ks = torch.zeros(P, 64, 8, dtype=torch.float32, device=DEV)
+    dsa.dsa_latent_cache_append_fp8(src, kc, ks, bt, sl, max_seq_len=T, num_pages=P)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(17)
+    rows = [(int(b), int(t)) for b, t in zip(rng.integers(0, B, 64), rng.integers(0, T, 64))] + [(0, 0), (B - 1, T - 1)]
+    x = src.float().cpu().numpy()
+    btn, kcn, ksn = bt.cpu().numpy(), kc.cpu().numpy(), ks.cpu().numpy()
+    from oracle.quant import latent_fp8_quantize_rows
+    for b, t in rows:
+        c_ref, s_ref = latent_fp8_quantize_rows(x[b, t])
+        p, slot = btn[b, t // 64], t % 64
+        np.testing.assert_array_equal(kcn[p, slot], c_ref, err_msg=f"row {(b, t)}")
+        np.testing.assert_array_equal(ksn[p, slot].view(np.uint32), s_ref.view(np.uint32))
