@@ -103,3 +103,54 @@ def test_fp8_latent_append_and_attention_graph_replays():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}"
         assert torch.equal(lse, l_ref), f"replay {r}"
+
+
+@pytest.mark.parametrize("cfg", [5, 3])
+def test_indexer_and_attention_step_graph_replays(cfg):
+    """A whole step (indexer, then attention on its indices) of the verify (T = 4) and causal
+    prefill shapes, captured once and replayed on new queries with eager steps on the same
+    buffers in between; every replay equals the eager step bit for bit."""
+    spec = W.config(cfg, "small")
+    print(f"[case] graph step {spec.name}", flush=True)
+    c = W.make_case(spec)
+    d = Dev(c)
+    dev = d.q_idx.device
+    layout = dsa.make_layout(d.bt, d.sl, c.num_pages, spec.max_len)
+    ishape = dsa.IndexerShape(spec.T, spec.HI, spec.DI, spec.K, dsa.DSA_BF16)
+    ashape = dsa.AttnShape(spec.T, spec.H, 576, 512, spec.K, spec.sm_scale)
+    iws = torch.empty(max(256, dsa.dsa_indexer_workspace_size(layout, ishape)), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(256, dsa.dsa_sparse_attn_workspace_size(layout, ashape)), dtype=torch.uint8, device=dev)
+    idx = torch.empty((spec.B, spec.T, spec.K), dtype=torch.int32, device=dev)
+    out = torch.empty((spec.B, spec.T, spec.H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((spec.B, spec.T, spec.H), dtype=torch.float32, device=dev)
+
+    def step(i_out, o, l):
+        d.indexer(idx_out=i_out, workspace=iws)
+        d.attn(i_out, out=o, lse=l, workspace=aws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(idx, out, lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(idx, out, lse)
+    torch.cuda.synchronize()
+    qi0, qa0 = d.q_idx.clone(), d.q_attn.clone()
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    for r in range(3):
+        perm = torch.randperm(spec.HI, generator=gen)
+        d.q_idx.copy_(qi0[:, :, perm].contiguous())
+        d.q_attn.copy_(qa0 * (1.0 + 0.5 * r))
+        i_ref = torch.empty_like(idx)
+        o_ref = torch.empty_like(out)
+        l_ref = torch.empty_like(lse)
+        step(i_ref, o_ref, l_ref)                          # eager, same workspaces
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, i_ref), f"replay {r}: indices"
+        assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}: out"
+        assert torch.equal(lse, l_ref), f"replay {r}: lse"
