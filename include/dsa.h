@@ -64,8 +64,8 @@ typedef enum {
                                 every query-row count (decode, verify, causal prefill) */
 } dsa_dtype;
 
-/* Geometry of the paged caches ([P1] §2 "on-demand in-page addressing"; [P3] §3.1, the paged K
- * cache is read in place).  Logical token s of sequence b lives in physical page
+/* Geometry of the paged caches ([P1] §2: indices resolve to page slots on demand; [P3] §3.1: the
+ * paged K cache is read in place).  Logical token s of sequence b lives in physical page
  * block_table[b * max_pages + s / page_size], slot s % page_size.  The indexer-K cache and the
  * latent-KV cache share this geometry. */
 typedef struct {

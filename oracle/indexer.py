@@ -40,8 +40,8 @@ def _mx_scales(scale_bytes, dim):
 
 
 def _keys_of_sequence(k_cache, k_scale, block_table, b, n, dtype):
-    """Logical key rows 0..n-1 of sequence b, resolved through the block table ([P1] §2,
-    "on-demand in-page addressing")."""
+    """Logical key rows 0..n-1 of sequence b, resolved through the block table ([P1] §2: indices
+    resolve to page slots on demand)."""
     s = np.arange(n)
     pages = block_table[b, s // PAGE]
     k = _decode(k_cache[pages, s % PAGE], dtype)
