@@ -174,7 +174,9 @@ size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_
  *     z_j = sm_scale * q[b,t,h,:] . X[s_j,:]     (X = 576-wide latent row of token s_j)
  *     out[b,t,h,:] = sum_j softmax(z)_j * X[s_j, 0:512],   lse[b,t,h] = ln sum_j exp(z_j)
  * with fp32 accumulation; out is rounded to bf16 (round to nearest even).  An empty set gives
- * out = 0 and lse = -inf.  Entries outside [0, seq_lens[b]) are treated as -1.
+ * out = 0 and lse = -inf.  An entry outside [0, pos], pos = seq_lens[b] - T + t (the positions
+ * query t may attend to), is skipped like -1 and sets the attention-index check that
+ * dsa_debug_status() reports.
  *
  *   q         [batch, T, heads, 576] bf16 (MLA-absorbed query), 16-byte aligned
  *   kv_cache  [num_pages, page_size, 576] bf16 latent rows, 16-byte aligned

@@ -71,7 +71,10 @@ __global__ __launch_bounds__(256) void mx_quant_rows(QuantArgs a) {
     // token t of sequence b is logical position seq_len - T + t
     const int b = (int)(r / a.T), t = (int)(r % a.T);
     const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
-    const int pos = n > 0 ? n - 1 : 0;
+    // a length below T (flagged by row_visible) leaves this token without a slot: store nothing
+    // rather than overwrite a valid cached row
+    if (n <= 0) return;
+    const int pos = n - 1;
     const int page = clamp_page(a.block_table[(size_t)b * a.max_pages + pos / kPage], a.num_pages);
     row = (long long)page * kPage + pos % kPage;
   }
@@ -152,6 +155,7 @@ __global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
   // token t of sequence b is logical position seq_len - T + t; a length outside [T, cap] is
   // flagged and clamped, as everywhere in the library
   int pg[RPW], slot[RPW];
+  bool has_slot[RPW];                 // false for a token whose flagged length leaves it no slot
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = row_of(i);
@@ -163,6 +167,7 @@ __global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
     }
     const int n = max(L - a.T + t + 1, 0);
     const int pos = n > 0 ? n - 1 : 0;
+    has_slot[i] = n > 0;
     pg[i] = a.block_table[(size_t)b * a.max_pages + pos / kPage];
     slot[i] = pos % kPage;
   }
@@ -178,7 +183,10 @@ __global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
   for (int j = 0; j < 8; ++j) amr = fmaxf(amr, fabsf(xr[j]));
   amr = row8_max(amr);
   const float scr = amr > 0.f ? __fdiv_rn(amr, 448.f) : 1.f;
-  if (r0 + ri < a.rows) {
+  bool rope_ok = has_slot[0];
+#pragma unroll
+  for (int i = 1; i < RPW; ++i) rope_ok = ri == i ? has_slot[i] : rope_ok;
+  if (r0 + ri < a.rows && rope_ok) {
     long long dr = dst_row[0];
 #pragma unroll
     for (int i = 1; i < RPW; ++i) dr = ri == i ? dst_row[i] : dr;
@@ -203,6 +211,7 @@ __global__ __launch_bounds__(256) void kv8_append_rows(Kv8Args a) {
       s_out = lane == k ? sk : s_out;
     }
     s_out = lane > 4 ? 1.f : s_out;
+    if (!has_slot[i]) continue;                              // wave-uniform
     *reinterpret_cast<uint2*>(a.codes + dst_row[i] * kDimQK + 8 * lane) = e4m3x8_scaled(x, sc);
     if (lane < 8) a.scales[dst_row[i] * 8 + lane] = s_out;
   }
