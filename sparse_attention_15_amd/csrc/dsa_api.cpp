@@ -4,10 +4,27 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <string>
 
 #include "dsa.h"
 #include "dsa_internal.h"
+
+namespace dsa {
+
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
+      (unsigned long long)(uintptr_t)&counter};
+  unsigned long long z = counter.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z | 1ull;
+}
+
+}  // namespace dsa
 
 namespace {
 

@@ -22,6 +22,11 @@ class LaunchScope {
   hipEvent_t stop_;
 };
 
+// A fresh 64-bit tag per call (never 0): a random start mixed with a call counter (SplitMix64
+// finaliser), so a tag that an earlier call left in a workspace cannot match by accident.  Kernels
+// that hand work between workgroups mark a handshake word with it.
+unsigned long long next_call_tag();
+
 // Workspace carving and grid sizes of one dsa_indexer_topk call.
 struct IndexerPlan {
   int rows = 0;          // batch * T query rows
@@ -89,8 +94,9 @@ struct AttnPlan {
   int groups_per_wg = 1; // head groups per workgroup
   int head_chunks = 1;   // workgroups per (row, split) along the heads
   int n_splits = 1;      // workgroups per query row along the selected set
+  int comb_parts = 1;    // combine workgroups per (row, head group) of a split row
   int keys_per_split = 0;
-  size_t off_ml = 0, off_part = 0, total = 0;
+  size_t off_ml = 0, off_part = 0, off_sync = 0, total = 0;
 };
 
 struct AttnArgs {

@@ -24,8 +24,6 @@
 //                   lowest-position ties up to the quota, and merges both lists into idx_out.
 // A row with n <= K selects every visible position and skips the score scratch.
 #include <algorithm>
-#include <atomic>
-#include <chrono>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -1383,19 +1381,6 @@ static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int g
 
 // MXFP8 runs on every score path (decode, verify, chunked prefill).
 bool indexer_mx_supported(int batch, int T) { return batch >= 1 && T >= 1; }
-
-// A fresh 64-bit tag per decode call (never 0): a random start mixed with a call counter
-// (splitmix64), so a tag left in a workspace by any earlier call cannot match by accident.
-static unsigned long long next_call_tag() {
-  static std::atomic<unsigned long long> counter{
-      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() ^
-      (unsigned long long)(uintptr_t)&counter};
-  unsigned long long z = counter.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  z ^= z >> 31;
-  return z | 1ull;
-}
 
 // Compute units of the current device (cached per device).
 static int device_cus() {

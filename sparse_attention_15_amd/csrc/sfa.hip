@@ -14,10 +14,19 @@
 // need one cross-half exchange, and the probabilities feed the value product O^T += V^T P^T as
 // operand B without leaving the lane.  The value product reads V^T straight from the row-major
 // tile with transposed LDS reads.  The accumulator O^T (512 x 32 per wave, 256 registers) lives in
-// the accumulation registers; the running max is kept in the log2 domain (exp2 with log2(e) folded
-// into the scale).  With one split the workgroup normalises and writes bf16 output and the
-// natural-log LSE; with several, each writes (m, l, O) partials and sfa_combine merges them:
-// M = max m_i, L = sum_i 2^(m_i - M) l_i, O = sum_i 2^(m_i - M) O_i / L.
+// the accumulation registers; the softmax runs in the log2 domain (exp2 with log2(e) folded into
+// the scale) against a fixed per-head reference, so the accumulator is never rescaled.
+//
+// The bf16 kernel is software-pipelined by one tile: iteration i issues the score product of tile
+// i+1 (with the gathers of tile i+3 spread between its MFMAs) and then the value product of tile
+// i, with the softmax of tile i+1 spread between those MFMAs.  The matrix pipe thus never waits
+// for the exponentials or the gather issue of the same tile.
+//
+// A row with several splits is merged in the same launch: each split publishes its partial
+// (m, l and the unnormalised O in bf16) and counts it in a per-(row, head group) word; combine
+// workgroups, placed after all split workgroups in the grid, wait for their row's count and merge
+//     M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) O_i / L,  lse = (M + log2 L) ln 2
+// summing the splits in index order, so the output does not depend on which split finished first.
 //
 // FP8 latent cache ([P1] §4: the SFA cache in FP8 with per-token scales over 128-wide tiles, BF16
 // products, the dequantised BF16 tile filling the matrix unit's input buffer directly): rows are
@@ -42,6 +51,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRefMargin = 64.f;         // reference max = first tile's max + this (log2 units)
 constexpr float kRefLimit = 100.f;         // a logit above reference + this restarts the split
+constexpr float kNoRef = -1e30f;           // no reference yet (finite: masked logits stay at p = 0)
+constexpr unsigned kMergeSpinCap = 1u << 20;   // a merge wait gives up after ~50 ms (flagged)
+constexpr int kPartWords = kVBlocks * 2 * 64 * 4;   // partial O of one 32-head group: 8192 bf16 pairs
 
 struct SfaArgs {
   const unsigned char* q;       // [rows, H, 576] bf16
@@ -52,9 +64,13 @@ struct SfaArgs {
   const int32_t* seq_lens;
   __bf16* out;                  // [rows, H, 512]
   float* lse;                   // [rows, H] or null
-  float* part_ml;               // [rows, splits, H, 2]
+  float* part_ml;               // [rows, splits, H, 2]: (m, l) of a published partial
   uint32_t* part_o;             // [rows, splits, head groups, 16 blocks, 2 halves, 64 lanes, 4] bf16 pairs
+  unsigned long long* sync;     // [rows, head groups, combine parts, splits]: ready flags
+  unsigned long long tag;       // this call's tag (never 0)
   int T, H, K, max_pages, num_pages, n_splits, keys_per_split, max_seq_len;
+  int rows, head_chunks, comb_parts;   // grid roles (see sfa_role)
+  uint32_t kv_bytes;            // bytes of the latent cache when it spans less than 4 GiB, else 0
   float scale_log2;             // sm_scale * log2(e)
 };
 
@@ -78,6 +94,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -100,38 +118,700 @@ constexpr int kSlotBytes8 = kDmaPerTile8 * 1024;        // 20480
 static_assert(kDmaPerTile8 * 64 >= kChunks8 && kTileBytes + 4 * kSlotBytes8 <= 4 * kTileBytes, "fp8 ring");
 
 // Waits until this wave's loads of the tile being consumed have landed; `later` of its later
-// tiles (n loads each) may stay in flight.
+// tiles (n loads each) may stay in flight.  The counter saturates at 63: a larger count is
+// clamped, which only waits longer.
 template <int n>
 __device__ __forceinline__ void wait_ring(int later) {
-  if (later >= 2) wait_vmcnt<(2 * n > 63 ? 63 : 2 * n)>();   // the counter saturates at 63
-  else if (later == 1) wait_vmcnt<n>();
+  if (later >= 2) wait_vmcnt<(2 * n > 63 ? 63 : 2 * n)>();
+  else if (later == 1) wait_vmcnt<(n > 63 ? 63 : n)>();
   else wait_vmcnt<0>();
 }
 
-template <int NW, bool KV8 = false>
+// Register-class pins (empty asm, no instruction of its own): the output accumulator O^T takes
+// 256 registers, the whole accumulation file.  Every MFMA result is selected into that file, so
+// the score accumulator S (16 registers) only fits if it leaves right after its product and one
+// O^T block waits in the VGPR file during it.  Pinning those points keeps the compiler from
+// shuffling several blocks per tile; in the merge, each updated block is pinned back.
+__device__ __forceinline__ void pin_v(f32x16& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin_a(f32x16& x) { asm volatile("" : "+a"(x)); }
+
+// Partial O of one 32-head group as a buffer resource (its 32 KiB are the bound: the hardware
+// drops any access outside).  Its loads and stores carry the agent-scope coherence bit (sc1), as
+// agent-scope atomics do, so they bypass the per-XCD L2s; unlike atomics they are ordinary
+// 16-byte accesses that the compiler batches.
+constexpr int kCoherent = 16;                       // cache policy: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(uint32_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, kPartWords * 4, 0x00020000);
+}
+
+// Ready flags of a split row: flag[row][head group][part][split] holds the call's tag once that
+// split's partial of that head group is published.  Every combine part has its own copy of the
+// flags, so no word is shared by two writers or two readers; a part resets its copies once it has
+// read them, so a replay of the same launch (same tag) starts from clean flags.
+
+// ------------------------------------------------------------------------------------------------
+// End of a split.  One split: write out = O / l (bf16) and lse.  Several: publish this split's
+// partial (m, l and the unnormalised O in bf16, in the accumulator's own lane order) and count it
+// in the (row, head group) word; the combine workgroups (sfa_combine_part) merge the row.
+template <int NW>
+__device__ __forceinline__ void finish_split(const SfaArgs& a, f32x16 (&o)[kVBlocks], float m_run, float l_run,
+                                             int row, int split, int gg, int tid) {
+  const int lane = tid & 63, nl = lane & 31, hh = lane >> 5;
+  const int NGT = (a.H + 31) / 32;
+  const int head = gg * 32 + nl;
+  const bool hvalid = head < a.H;
+  if (a.n_splits > 1) {
+    if (gg >= NGT) return;
+    const size_t ps = (size_t)row * a.n_splits + split;
+    if (hvalid && hh == 0)
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(a.part_ml + (ps * a.H + head) * 2),
+                         (uint64_t)__float_as_uint(m_run) | ((uint64_t)__float_as_uint(l_run) << 32),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // this lane's 16 bytes of every 1 KiB unit (block, half); the unit's offset goes in the
+    // instructions' scalar offset, so one VGPR serves all 32 units
+    int lane16 = 16 * lane;
+    asm volatile("" : "+v"(lane16));
+    const __amdgpu_buffer_rsrc_t po = part_rsrc(a.part_o + (ps * NGT + gg) * kPartWords);
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; ++mb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = pack_bf16(o[mb][8 * half + 2 * q], o[mb][8 * half + 2 * q + 1]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, po, lane16, 1024 * (mb * 2 + half), kCoherent);
+      }
+    // the stores are complete (device-coherent) before the flags that publish them
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (lane < a.comb_parts)
+      __hip_atomic_store(a.sync + (((size_t)row * NGT + gg) * a.comb_parts + lane) * a.n_splits + split, a.tag,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (hvalid) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV;
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * mb + 8 * j + 4 * hh;
+        uint2 v;
+        v.x = pack_bf16(o[mb][4 * j] * inv, o[mb][4 * j + 1] * inv);
+        v.y = pack_bf16(o[mb][4 * j + 2] * inv, o[mb][4 * j + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + d) = v;
+      }
+    if (a.lse != nullptr && hh == 0)
+      a.lse[(size_t)row * a.H + head] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  }
+}
+
+// Combine workgroup: merges part `part` (of comb_parts) of head group g of a split row once all S
+// splits have published.  With unnormalised partials O_i the weight of split i is
+// 2^(m_i - M) / L, M = max_i m_i, L = sum_i 2^(m_i - M) l_i, and lse = (M + log2 L) ln 2.  The
+// splits are summed in index order, so the result does not depend on which split finished first.
+// These workgroups come after every split workgroup in the grid; the hardware dispatches
+// workgroups in index order, so the splits a combine part waits for are already running (the wait
+// is bounded all the same: past it the merge goes ahead and the debug flag records it).
+//
+// Each thread owns NU 16-byte units (4 bf16 pairs of one head) of the group's [block][half][lane]
+// layout and keeps 32 loads in flight: NU units x 32/NU splits per batch.
+template <int NT, int NU>
+__device__ __forceinline__ void combine_units(const SfaArgs& a, int row, int g, int part, const float* wgt) {
+  constexpr int SB = 32 / NU;                               // splits per batch
+  const int S = a.n_splits, NGT = (a.H + 31) / 32;
+  const int tid = threadIdx.x;
+  const int u0 = part * NT * NU + tid;                      // units u0, u0 + NT, ...
+  float acc[NU][8];
+#pragma unroll
+  for (int j = 0; j < NU; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += SB) {
+    u32x4 v[NU][SB];
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (s0 + k < S) {
+        const __amdgpu_buffer_rsrc_t rs = part_rsrc(a.part_o + (((size_t)row * S + s0 + k) * NGT + g) * kPartWords);
+#pragma unroll
+        for (int j = 0; j < NU; ++j) v[j][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (u0 + j * NT), 0, kCoherent);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SB; ++k) {
+      if (s0 + k < S) {
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+          const int nl = (u0 + j * NT) & 31;
+          const float wk = wgt[2 * ((s0 + k) * 32 + nl)];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[j][2 * q] = fmaf(wk, bf16_lo(v[j][k][q]), acc[j][2 * q]);
+            acc[j][2 * q + 1] = fmaf(wk, bf16_hi(v[j][k][q]), acc[j][2 * q + 1]);
+          }
+        }
+      }
+    }
+  }
+  // register pair k = 4*half + q holds columns 32mb + 8(k >> 1) + 4hh + 2(k & 1) + {0, 1}
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    const int u = u0 + j * NT;
+    const int ln = u & 63, half = (u >> 6) & 1, mb = u >> 7;
+    const int nl = ln & 31, hh = ln >> 5;
+    const int head = g * 32 + nl;
+    if (head < a.H) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + 32 * mb + 16 * half + 4 * hh;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc[j][0], acc[j][1]), pack_bf16(acc[j][2], acc[j][3]));
+      *reinterpret_cast<uint2*>(dst + 8) = make_uint2(pack_bf16(acc[j][4], acc[j][5]), pack_bf16(acc[j][6], acc[j][7]));
+    }
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void sfa_combine_part(const SfaArgs& a, int row, int g, int part, float* wgt) {
+  constexpr int NT = NW * 64;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int S = a.n_splits, NGT = (a.H + 31) / 32;
+  unsigned long long* flags = a.sync + (((size_t)row * NGT + g) * a.comb_parts + part) * S;
+  if (tid < 64) {
+    // lane i watches the flags of splits i, i + 64, ...; polls back off (up to ~4000 cycles apart)
+    unsigned spins = 0, nap = 1;
+    for (;;) {
+      bool ready = true;
+      for (int sp = lane; sp < S; sp += 64)
+        ready &= __hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag;
+      if (__builtin_amdgcn_readfirstlane(__ballot(!ready) == 0ull ? 1 : 0)) break;
+      if (++spins > kMergeSpinCap / 16) { if (lane == 0) flag_input(kFlagSync); break; }
+      for (unsigned k = 0; k < nap; ++k) __builtin_amdgcn_s_sleep(4);
+      nap = nap < 16 ? 2 * nap : 16;
+    }
+    // only this part reads these flags: reset them for the next call
+    for (int sp = lane; sp < S; sp += 64)
+      __hip_atomic_store(&flags[sp], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  lds_barrier();
+  // merge weights of every split and head of the group (wgt[S][32]), the row's lse from part 0
+  for (int i = tid; i < S * 32; i += NT) {
+    const int sp = i >> 5, h = g * 32 + (i & 31);
+    const uint64_t ml = h < a.H ? __hip_atomic_load(reinterpret_cast<const uint64_t*>(
+                                      a.part_ml + (((size_t)row * S + sp) * a.H + h) * 2), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0ull;
+    wgt[2 * i] = h < a.H ? __uint_as_float((uint32_t)ml) : -INFINITY;
+    wgt[2 * i + 1] = __uint_as_float((uint32_t)(ml >> 32));
+  }
+  lds_barrier();
+  if (tid < 32) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wgt[2 * (sp * 32 + tid)]);
+    float L = 0.f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float e = M != -INFINITY ? __builtin_amdgcn_exp2f(wgt[2 * (sp * 32 + tid)] - M) : 0.f;
+      L += e * wgt[2 * (sp * 32 + tid) + 1];
+      wgt[2 * (sp * 32 + tid)] = e;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int sp = 0; sp < S; ++sp) wgt[2 * (sp * 32 + tid)] *= inv;
+    const int h = g * 32 + tid;
+    if (a.lse != nullptr && part == 0 && h < a.H)
+      a.lse[(size_t)row * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  }
+  lds_barrier();
+  // units per thread: the group's 2048 units over comb_parts parts of NT threads
+  const int nu = (kPartWords / 4) / (a.comb_parts * NT);
+  if (nu >= 8) combine_units<NT, 8>(a, row, g, part, wgt);
+  else if (nu == 4) combine_units<NT, 4>(a, row, g, part, wgt);
+  else if (nu == 2) combine_units<NT, 2>(a, row, g, part, wgt);
+  else combine_units<NT, 1>(a, row, g, part, wgt);
+}
+
+// Workgroup roles of the 1-D grid: the first rows * splits * head chunks workgroups run the
+// splits (row fastest, so the splits of a row share an XCD when the row count is a multiple of
+// 8); the rest are combine parts, (row, head group, part), row fastest.
+struct SfaRole {
+  bool combine;
+  int row, split, chunk, g, part;
+};
+__device__ __forceinline__ SfaRole sfa_role(const SfaArgs& a) {
+  SfaRole r;
+  const int rows = a.rows;
+  const int n_main = rows * a.n_splits * a.head_chunks;
+  int b = blockIdx.x;
+  r.combine = b >= n_main;
+  if (!r.combine) {
+    r.row = b % rows; b /= rows;
+    r.split = b % a.n_splits; r.chunk = b / a.n_splits;
+    r.g = r.part = 0;
+  } else {
+    b -= n_main;
+    const int NGT = (a.H + 31) / 32;
+    r.row = b % rows; b /= rows;
+    r.g = b % NGT; r.part = b / NGT;
+    r.split = r.chunk = 0;
+  }
+  return r;
+}
+
+// Direct-to-LDS load of 16 bytes per lane through a buffer resource: lane i's 16 bytes from
+// byte offset soff + voff (soff wave-uniform, voff per lane) land at LDS address lds_dst + 16 i.
+// Inline assembly for the reason given at lds_dma16; the resource's size bounds every access.
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t soff, uint32_t voff,
+                                              const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(base), "v"(voff),
+               "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// ------------------------------------------------------------------------------------------------
+// Softmax pieces shared by both kernels (same arithmetic, so an FP8-cache call over a cache that
+// holds exact bf16 values gives the bf16 call's bits).  Register r of a lane holds key
+// 8(r/4) + 4hh + r%4 of the tile.
+// Keys that are not selected get logit -inf (a wave-uniform test skips this for full tiles).
+__device__ __forceinline__ void mask_keys(f32x16& s, uint32_t valid, int hh) {
+  if (valid == 0xFFFFFFFFu) return;
+  const uint32_t vmask = valid >> (4 * hh);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = ((vmask >> (8 * (r >> 2) + (r & 3))) & 1u) ? s[r] : -INFINITY;
+}
+// Max of the raw logits r0..r1-1 (positive scaling commutes with max, rounding included).
+__device__ __forceinline__ float raw_max(const f32x16& s, int r0, int r1, float m) {
+#pragma unroll
+  for (int r = r0; r < r1; ++r) m = fmaxf(m, s[r]);
+  return m;
+}
+// 2^(z - m) with z = scale * s rounded once (fma): masked keys (-inf) give 0.
+__device__ __forceinline__ float prob(float s, float scale, float m) {
+  return __builtin_amdgcn_exp2f(fmaf(s, scale, -m));
+}
+
+// ------------------------------------------------------------------------------------------------
+// bf16 latent cache, software-pipelined (see the file comment).  BUF: the cache spans less than
+// 4 GiB, so the row table holds each selected row's 32-bit byte offset and the gathers address it
+// through a buffer resource (a scalar offset per value row, no 64-bit address arithmetic).
+template <int NW, bool BUF>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void sfa_main(SfaArgs a) {
+void sfa_pipe(SfaArgs a) {
   constexpr int NT = NW * 64;               // one wave per 32-head group
-  constexpr int kDmaWave = (KV8 ? kDmaPerTile8 : kDmaPerTile) / NW;
-  static_assert(kDmaPerTile % NW == 0 && kDmaPerTile8 % NW == 0, "per-wave load count must be uniform");
+  constexpr int kRows = kBK / NW, kRope = 4 / NW;
+  constexpr int kDmaWave = kRows + kRope;   // wave-wide loads per tile: value rows, then rope blocks
+  constexpr int kPerSlot = kDmaWave / 9;    // loads issued after every fourth score MFMA (9 places)
+  static_assert(kDmaPerTile % NW == 0 && kDmaWave % 9 == 0, "per-wave load count must be uniform");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_kv[kStages][kTileBytes];
+  __shared__ int lds_rows[kMaxSplitKeys];   // physical row of each selected index, -1 = skip
+  __shared__ uint32_t lds_valid[kMaxSplitKeys / kBK];   // per tile: its selected keys as a bit mask
+  __shared__ int lds_first, lds_last;       // first and last j with a visible position
+  __shared__ int lds_epoch;                 // restarts requested by any wave (see below)
+
+  const SfaRole role = sfa_role(a);
+  if (role.combine) {
+    sfa_combine_part<NW>(a, role.row, role.g, role.part, reinterpret_cast<float*>(&lds_kv[0][0]));
+    return;
+  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS DMA bases stay in SGPRs
+  const int nl = lane & 31, hh = lane >> 5;
+  const int row = role.row, split = role.split;
+  const int gg = role.chunk * NW + wave;    // this wave's global head group
+  const int b = row / a.T, t = row % a.T;
+  const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
+  const int k_begin = split * a.keys_per_split;
+  const int nkeys = max(0, min(a.K, k_begin + a.keys_per_split) - k_begin);
+  const int ntiles = (nkeys + kBK - 1) / kBK;
+  const int head = gg * 32 + nl;
+  const bool hvalid = head < a.H;
+  const int32_t* idx = a.idx + (size_t)row * a.K + k_begin;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+
+  if (tid == 0) { lds_first = kMaxSplitKeys; lds_last = -1; lds_epoch = 0; }
+  // Prologue, split between the waves: the counter that orders a wave's loads is per wave, so wave
+  // 0 resolves the first index batch (index loads, then their block-table loads) without waiting
+  // for the q copy, which the other waves issue meanwhile (with one wave, it does both).
+  //
+  // q copy: the B operand of the score product is this lane's head row of q, columns 16 ks + 8 hh
+  // .. + 7 for K step ks.  The workgroup's q rows (NW x 32 heads x 1152 bytes: one ring slot per
+  // head group, free until the first gathers) go to LDS with direct-to-LDS loads of eight whole
+  // 128-byte lines each; read straight into the MFMA layout, every load instruction would touch 32
+  // rows, a quarter of a line each.  16-byte chunk c of head h sits at slot 72h + (c ^ ((h >> 1) &
+  // 7)): the XOR stays inside a 128-byte line and keeps the fragment reads (16 lanes = 16 heads,
+  // one chunk) free of bank conflicts.  Heads beyond H copy head 0; their results are never stored.
+  constexpr int kCopyWaves = NW > 1 ? NW - 1 : 1;
+  constexpr int kCopyLoads = (NW * kQSteps + kCopyWaves - 1) / kCopyWaves;   // per copying wave
+  if (NW == 1 || wave > 0) {
+    const unsigned char* qrow = a.q + (size_t)row * a.H * kRowBytes;
+    const int head0 = role.chunk * NW * 32;
+    const int w0 = NW > 1 ? wave - 1 : 0;
+#pragma unroll 4
+    for (int u = 0; u < kCopyLoads; ++u) {
+      const int i = w0 * kCopyLoads + u;                 // fills image bytes 1024 i .. of the workgroup
+      if (i < NW * kQSteps) {
+        const int sl = 64 * i + lane;
+        const int hl = sl / 72, cp = sl % 72;
+        const int hq = head0 + hl < a.H ? head0 + hl : 0;
+        lds_dma16(qrow + (size_t)hq * kRowBytes + 16 * (cp ^ ((hl >> 1) & 7)), &lds_kv[0][0] + 1024 * i);
+      }
+    }
+  }
+  // Row table: lds_rows[j] = physical row of selected index j, -1 if it is not a visible position;
+  // lds_valid[tile] = its mask.  Eight index loads per lane go out together, then their block-table
+  // loads: wave 0 takes the first 512 keys, all waves the rest (after the copy).
+  constexpr int kBatch = 8;
+  // first and last selected j of this wave, from the batches' ballots (scalar ops: a per-lane LDS
+  // atomic would become a loop over the active lanes)
+  int w_first = kMaxSplitKeys, w_last = -1;
+  auto table = [&](int j0, int stride, int lid) __attribute__((always_inline)) {
+    int s[kBatch], pg[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u * stride + lid;
+      s[u] = j < nkeys ? idx[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) pg[u] = s[u] >= 0 && s[u] < n ? bt[s[u] / kPage] : 0;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u * stride + lid;
+      if (s[u] < -1 || s[u] >= n) flag_input(kFlagIndex);
+      const int r = s[u] >= 0 && s[u] < n ? clamp_page(pg[u], a.num_pages) * kPage + (s[u] % kPage) : -1;
+      const uint64_t bal = __ballot(r >= 0);
+      if (j < ntiles * kBK) {
+        lds_rows[j] = BUF && r >= 0 ? (int)((uint32_t)r * kRowBytes) : r;   // BUF: byte offset
+        if ((lane & 31) == 0) lds_valid[j >> 5] = (uint32_t)(bal >> (lane & 32));
+      }
+      if (bal != 0) {                       // lanes hold consecutive j from jw on
+        const int jw = j0 + u * stride + (lid - lane);
+        w_first = min(w_first, jw + (int)__builtin_ctzll(bal));
+        w_last = max(w_last, jw + 63 - (int)__builtin_clzll(bal));
+      }
+    }
+  };
+  constexpr int kFirstKeys = kBatch * 64;
+  lds_barrier();                            // the bounds are initialised
+  if (wave == 0) table(0, 64, lane);
+  if (ntiles * kBK > kFirstKeys) {          // long splits: the rest with every wave
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    lds_barrier();
+    for (int j0 = kFirstKeys; j0 < ntiles * kBK; j0 += kBatch * NT) table(j0, NT, tid);
+  }
+  if (lane == 0 && w_last >= 0) { atomicMin(&lds_first, w_first); atomicMax(&lds_last, w_last); }
+  // the q copy and the table's loads have landed (a compiler-visible vmcnt(0): no wait for them is
+  // left for the main loop, whose gathers the compiler does not count) ... for every wave
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  lds_barrier();
+  bf16x8 qf[kQSteps];
+  {
+    const unsigned char* qh = lds_kv[wave] + nl * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks)
+      qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ((2 * ks + hh) ^ ((nl >> 1) & 7))));
+  }
+  lds_barrier();                            // every wave holds its q: the ring is free
+  // Tiles run from the first through the last tile holding a selected key (a causal row with
+  // fewer visible positions than K leaves its trailing tiles empty).  Keys that are not selected
+  // are gathered from the first selected row (finite data: their zero probabilities never meet a
+  // NaN).
+  const int first = lds_first, last = lds_last;
+  const int ft = first / kBK;
+  const int nt = last >= 0 ? last / kBK - ft + 1 : 0;
+  const int fill_row = last >= 0 ? lds_rows[first] : 0;   // BUF: its byte offset
+
+  // Gathers.  This wave loads the value columns of rows wave, wave + NW, ... (one load per row:
+  // the row id is wave-uniform, so the row's address is a scalar base and each lane adds its own
+  // swizzled 16-byte chunk) and the rope blocks wave, wave + NW, ... < 4 (8 rows x 8 chunks per
+  // load, lane i: row 8k + i/8, slot i%8).  Every wave issues the same number of loads per tile,
+  // which the counter waits rely on.  Load L < kRows is value row u = L; the rest are rope blocks.
+  // row_id(i, L): the physical row (value load: wave-uniform; rope load: this lane's) of load L.
+  auto row_id = [&](int i, int L) __attribute__((always_inline)) {
+    const int* tr = &lds_rows[(ft + i) * kBK];
+    return L < kRows ? tr[wave + L * NW] : tr[8 * (wave + (L - kRows) * NW) + (lane >> 3)];
+  };
+  // BUF: the cache as a buffer (its size, at most 2^32 - 1 bytes, bounds the gathers)
+  const __amdgpu_buffer_rsrc_t kv_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(a.kv), 0, BUF ? (int)a.kv_bytes : 0, 0x00020000);
+  auto gather_one = [&](int L, unsigned char* slot, int id) __attribute__((always_inline)) {
+    if (L < kRows) {
+      const int r = wave + L * NW;
+      int pr = __builtin_amdgcn_readfirstlane(id);
+      pr = pr == -1 ? fill_row : pr;        // -1: not selected (a BUF offset may exceed 2^31)
+      if constexpr (BUF)
+        lds_dma16_buf(kv_rsrc, (uint32_t)pr, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)), slot + 1024 * r);
+      else
+        lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
+                       slot + 1024 * r);
+    } else {
+      const int k = wave + (L - kRows) * NW;
+      const int r = 8 * k + (lane >> 3);
+      const int pr = id == -1 ? fill_row : id;
+      if constexpr (BUF)
+        lds_dma16_buf(kv_rsrc, 0u, (uint32_t)pr + 2 * kDimV + 16 * ((lane & 7) ^ swb(r)), slot + kRegionB + 1024 * k);
+      else
+        lds_dma16(a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r)),
+                  slot + kRegionB + 1024 * k);
+    }
+  };
+  auto issue_tile = [&](int i, unsigned char* slot) __attribute__((always_inline)) {
+    int ids[kDmaWave];
+#pragma unroll
+    for (int L = 0; L < kDmaWave; ++L) ids[L] = row_id(i, L);
+#pragma unroll
+    for (int L = 0; L < kDmaWave; ++L) gather_one(L, slot, ids[L]);
+  };
+
+  // O^T: 512 latent columns (16 blocks of 32) x 32 heads
+  f32x16 o[kVBlocks];
+#pragma unroll
+  for (int mb = 0; mb < kVBlocks; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+  // Fixed softmax reference per head (log2 units), set from the split's first tile (which holds a
+  // selected key): its max plus kRefMargin.  Probabilities 2^(s - m_ref) stay below 2^kRefLimit
+  // as long as no logit exceeds m_ref + kRefLimit, so the accumulator never needs rescaling.  A
+  // logit beyond that (a spread of more than 164 log2 units inside the split) raises the reference
+  // and restarts the split from its first tile.
+  float m_run = kNoRef, l_run = 0.f;
+  int epoch = 0;                            // restarts seen by this wave
+
+  // Per-lane LDS byte offsets.  Score A operand: row nl, chunk c = 2*ks + hh.  For ks < 32
+  // (region A) write ks = 8g + v: the slot is 16g + ((2v + hh) ^ swa), i.e. byte
+  // 256g + 16*((hh ^ swa) & 1) + 32*(v ^ (swa >> 1)); the last term only uses bits 5-7, so the
+  // address is qa ^ 32v (+ 256g).  Region B likewise: qb ^ 32v' for ks = 32 + v'.
+  const int sa_nl = swa(nl), sb_nl = swb(nl);
+  const int qa = 1024 * nl + 16 * ((hh ^ sa_nl) & 1) + 32 * (sa_nl >> 1);
+  const int qb = kRegionB + 128 * nl + 16 * ((hh ^ sb_nl) & 1) + 32 * (sb_nl >> 1);
+  // Value A operand (transposed 8-byte reads): key = 16*k2 + 8*q + kq, columns 8*cl + 4*(lane&1)
+  // + 32*mb, cl = chunk within the 32-column block.  With mb = 4g + m' the byte offset is
+  // 16384*k2 + 256g + (pv[q] ^ 64m'): swa(key) only sees key bits 0-3 = 8q + kq.
+  const int kq = 4 * hh + ((lane & 15) >> 2);
+  const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  int pv[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int sa = swa(8 * q + kq);
+    pv[q] = 1024 * (8 * q + kq) + 16 * (cl ^ (sa & 3)) + 64 * (sa >> 2) + 8 * (lane & 1);
+  }
+
+  // S^T = X q^T for the tile in ring slot `buf`: rows = the tile's 32 keys, columns = this wave's
+  // 32 heads.  The A fragments stream through a 4-deep register ring (the read for step ks + 4
+  // goes out right behind the MFMA of step ks).  With GATHER, the loads of tile gi into slot
+  // `gbuf` go out after every fourth MFMA, kPerSlot at a time; the row ids of each group are read
+  // one group (four MFMAs) ahead.  Slots are runtime bases: every per-lane offset below only
+  // touches address bits 4-11 and a slot starts at a multiple of 36864 = 0x9000, so slot base and
+  // offset add without carries into the XORed bits.
+  auto score = [&](int buf, int gi, int gbuf, auto gather_c) __attribute__((always_inline)) {
+    constexpr bool GATHER = decltype(gather_c)::value;
+    int ids[kPerSlot];
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int e = 0; e < kPerSlot; ++e) ids[e] = row_id(gi, e);
+    }
+    const unsigned char* tile = lds_kv[0];
+    int qa_t = qa + buf * kTileBytes, qb_t = qb + buf * kTileBytes;
+    asm volatile("" : "+v"(qa_t), "+v"(qb_t));
+    auto a_frag = [&](int ks) {
+      const int off = ks < 32 ? (qa_t ^ (32 * (ks & 7))) + 256 * (ks >> 3) : qb_t ^ (32 * (ks - 32));
+      return *reinterpret_cast<const u32x4*>(tile + off);
+    };
+    u32x4 aring[kRingA];
+#pragma unroll
+    for (int j = 0; j < kRingA; ++j) aring[j] = a_frag(j);
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const bf16x8 af = as_bf16x8(aring[ks % kRingA]);
+      if (ks + kRingA < kQSteps) aring[ks % kRingA] = a_frag(ks + kRingA);
+      s = mfma_bf16(af, qf[ks], s);
+      if constexpr (GATHER) {
+        if ((ks & 3) == 1) {
+          const int g = ks >> 2;
+#pragma unroll
+          for (int e = 0; e < kPerSlot; ++e) gather_one(g * kPerSlot + e, lds_kv[gbuf], ids[e]);
+          if (g + 1 < 9) {
+#pragma unroll
+            for (int e = 0; e < kPerSlot; ++e) ids[e] = row_id(gi, (g + 1) * kPerSlot + e);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return s;
+  };
+
+  // P^T as the B operand of the value product: K step k2 covers keys 16*k2 .. 16*k2 + 15; this
+  // lane's 8 values are keys 16*k2 + {0..3, 8..11} + 4*hh (accumulator rows of the score tile)
+  auto pack_p = [&](const f32x16& p, int k2) {
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = pack_bf16(p[8 * k2 + 2 * e], p[8 * k2 + 2 * e + 1]);
+    return as_bf16x8(v);
+  };
+  // The whole softmax of one tile at once (the split's first tile: it sets the reference).
+  // Logits are in log2 units (the scale carries log2 e).
+  auto softmax_now = [&](f32x16& s, uint32_t valid, bf16x8 (&pn)[2]) {
+    mask_keys(s, valid, hh);
+    const float mx = xor32_max(raw_max(s, 0, 16, -INFINITY) * a.scale_log2);
+    if (m_run == kNoRef) m_run = mx + kRefMargin;   // the first tile holds a selected key: mx > -inf
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s[r] = prob(s[r], a.scale_log2, m_run); psum += s[r]; }
+    l_run += xor32_sum(psum);
+    if (mx > m_run + kRefLimit) { m_run = mx + kRefMargin; lds_epoch = epoch + 1; }
+    pn[0] = pack_p(s, 0);
+    pn[1] = pack_p(s, 1);
+  };
+
+  // O^T += V^T P^T for the tile in slot `buf` with probabilities pc.  The A operand (latent column
+  // m, the same 8 keys) comes from two transposed reads of the row-major tile: a 16-lane group
+  // reading 8 bytes (4 columns) of 4 consecutive keys hands lane i the 4 keys of column i.  Same
+  // 4-deep ring as the score product; consecutive MFMAs go to different accumulators, block 15
+  // first in each K step (it moves to the VGPR file for the next score product, which then does
+  // not wait for its last MFMA).  With SOFT, the next tile's logits s leave the accumulation
+  // registers after the first MFMA and its softmax (mask `valid`) runs between the following
+  // MFMAs, one slice after each, leaving its probabilities in pn.
+  auto value = [&](int buf, const bf16x8 (&pc)[2], f32x16& s, uint32_t valid, bf16x8 (&pn)[2], auto soft_c)
+      __attribute__((always_inline)) {
+    constexpr bool SOFT = decltype(soft_c)::value;
+    const unsigned char* tile = lds_kv[0];
+    int pv0 = pv[0] + buf * kTileBytes, pv1 = pv[1] + buf * kTileBytes;
+    asm volatile("" : "+v"(pv0), "+v"(pv1));
+    auto block_of = [](int j) { return ((j & 15) + 15) & 15; };   // MFMA j's O^T block: 15, 0, 1, ..., 14
+    auto v_frag = [&](int j, int q) {
+      const int mb = block_of(j), k2 = j >> 4;
+      return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+          tile + ((q ? pv1 : pv0) ^ (64 * (mb & 3))) + 256 * (mb >> 2) + 16384 * k2));
+    };
+    s16x4 vring[kRingV][2];
+#pragma unroll
+    for (int j = 0; j < kRingV; ++j) { vring[j][0] = v_frag(j, 0); vring[j][1] = v_frag(j, 1); }
+    float mraw = -INFINITY, psum = 0.f, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2 * kVBlocks; ++j) {
+      const int k2 = j >> 4, mb = block_of(j);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vring[j % kRingV][0], vring[j % kRingV][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      if (j + kRingV < 2 * kVBlocks) {
+        vring[j % kRingV][0] = v_frag(j + kRingV, 0);
+        vring[j % kRingV][1] = v_frag(j + kRingV, 1);
+      }
+      o[mb] = mfma_bf16(vf, pc[k2], o[mb]);
+      if constexpr (SOFT) {
+        if (j == 0) {
+          pin_v(s);                         // S leaves the accumulation registers
+          mask_keys(s, valid, hh);
+        } else if (j == 1) {
+          mraw = raw_max(s, 0, 8, mraw);
+        } else if (j == 2) {
+          mraw = raw_max(s, 8, 16, mraw);
+        } else if (j < 11) {
+          const int r = 2 * (j - 3);
+          s[r] = prob(s[r], a.scale_log2, m_run);
+          s[r + 1] = prob(s[r + 1], a.scale_log2, m_run);
+        } else if (j == 11) {
+          pn[0] = pack_p(s, 0);
+        } else if (j == 12) {
+          pn[1] = pack_p(s, 1);
+        } else if (j == 13) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) psum += s[r];
+        } else if (j == 14) {
+          psum = xor32_sum(psum);
+          mx = xor32_max(mraw * a.scale_log2);
+        } else if (j == 15) {
+          l_run += psum;
+          if (mx > m_run + kRefLimit) {     // too far above the reference: restart with a new one
+            m_run = mx + kRefMargin;
+            lds_epoch = epoch + 1;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Iteration `it` of the pipelined loop; the ring slot of tile i is i % 4.  MODE 0: score tile
+  // it+1 while gathering tile it+3, then the value product of tile it with the softmax of tile
+  // it+1; MODE 1: the same without a gather (it+3 is past the end); MODE 2: the value product of
+  // the last tile only.  Before the score product, tile it+1 must have landed (tile it+2 may stay
+  // in flight); the barrier also tells every wave that the previous iteration's value product is
+  // done, so slot (it+3) % 4, which held tile it-1, takes tile it+3.
+  bf16x8 pc[2];
+  auto iter = [&](int it, auto mode_c) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode_c)::value;
+    f32x16 s;
+    uint32_t valid = 0;
+    bf16x8 pn[2];
+    if constexpr (MODE < 2) {
+      wait_ring<kDmaWave>(MODE == 0 ? 1 : min(1, nt - 2 - it));
+      lds_barrier();
+      valid = lds_valid[ft + it + 1];
+      pin_v(o[kVBlocks - 1]);
+      s = score((it + 1) & 3, it + 3, (it + 3) & 3, std::integral_constant<bool, MODE == 0>{});
+      value(it & 3, pc, s, valid, pn, std::true_type{});
+      pc[0] = pn[0];
+      pc[1] = pn[1];
+    } else {
+      value(it & 3, pc, s, valid, pn, std::false_type{});
+    }
+  };
+
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < nt) issue_tile(i, lds_kv[i]);
+    if (nt > 0) {
+      wait_ring<kDmaWave>(min(2, nt - 1));   // tile 0 landed; tiles 1 and 2 may be in flight
+      lds_barrier();
+      f32x16 s = score(0, 0, 0, std::false_type{});
+      softmax_now(s, lds_valid[ft], pc);
+    }
+    static_assert(kStages == 4, "slot (i % 4) and the two tiles of lead assume a 4-slot ring");
+    int it = 0;
+    for (; it < nt - 3; ++it) iter(it, std::integral_constant<int, 0>{});
+    for (; it < nt - 1; ++it) iter(it, std::integral_constant<int, 1>{});
+    if (it < nt) iter(it, std::integral_constant<int, 2>{});
+    // every wave sees the same restart request after the barrier; the gathers of this pass have
+    // all been waited for (the last wait of the loop is for the last tile with no later one)
+    lds_barrier();
+    const int req = lds_epoch;
+    if (req == epoch) break;
+    epoch = req;                            // raised references stay; accumulation starts over
+    l_run = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kVBlocks; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+    lds_barrier();                          // all waves read the request before slot 0 is refilled
+  }
+  finish_split<NW>(a, o, m_run, l_run, row, split, gg, tid);
+}
+
+// ------------------------------------------------------------------------------------------------
+// FP8 latent cache: the same products over tiles dequantised from E4M3 codes and tile scales.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sfa_main_kv8(SfaArgs a) {
+  constexpr int NT = NW * 64;               // one wave per 32-head group
+  constexpr int kDmaWave = kDmaPerTile8 / NW;
+  static_assert(kDmaPerTile8 % NW == 0, "per-wave load count must be uniform");
   static_assert(kStages - 2 <= 2, "wait_ring handles up to two later tiles");
   __shared__ __attribute__((aligned(1024))) unsigned char lds_kv[kStages][kTileBytes];
   __shared__ int lds_rows[kMaxSplitKeys];   // physical row of each selected index, -1 = skip
 
+  const SfaRole role = sfa_role(a);
+  if (role.combine) {
+    sfa_combine_part<NW>(a, role.row, role.g, role.part, reinterpret_cast<float*>(&lds_kv[0][0]));
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS DMA bases stay in SGPRs
   const int nl = lane & 31, hh = lane >> 5;
-  const int row = blockIdx.x, split = blockIdx.y;
-  const int NGT = (a.H + 31) / 32;          // 32-head groups over all workgroups of a row
-  const int gg = blockIdx.z * NW + wave;    // this wave's global head group
+  const int row = role.row, split = role.split;
+  const int gg = role.chunk * NW + wave;    // this wave's global head group
   const int b = row / a.T, t = row % a.T;
   const int n = row_visible(a.seq_lens, b, a.T, t, a.max_seq_len);
   const int k_begin = split * a.keys_per_split;
-  const int k_end = min(a.K, k_begin + a.keys_per_split);
-  const int nkeys = k_end - k_begin;
+  const int nkeys = max(0, min(a.K, k_begin + a.keys_per_split) - k_begin);
   const int ntiles = (nkeys + kBK - 1) / kBK;
-  const int head = gg * 32 + nl;
-  const bool hvalid = head < a.H;
 
   // Row table for this split (one round of idx + block-table loads): lds_rows[j] = physical row
   // of selected index j, -1 if it is not a visible position; lds_valid[tile] = its 32-bit mask.
@@ -147,16 +827,15 @@ void sfa_main(SfaArgs a) {
 
   // B operand of the score product: this lane's head row of q (36 K steps of 16 columns).  The
   // workgroup's q rows (NW * 32 heads x 1152 bytes = NW ring slots, free until the first gathers)
-  // are first copied into LDS with direct-to-LDS loads that each read eight whole 128-byte lines;
-  // read straight into the MFMA layout, every load instruction would touch 32 rows, a quarter of
-  // a line each.  16-byte chunk c of head h sits at slot 72h + (c ^ ((h >> 1) & 7)): the XOR stays
-  // inside a 128-byte line and makes the fragment reads (16 lanes = 16 heads, one chunk) free of
-  // bank conflicts.  Heads beyond H copy head 0; their results are never stored.
+  // are first copied into LDS with direct-to-LDS loads that each read eight whole 128-byte lines.
+  // 16-byte chunk c of head h sits at slot 72h + (c ^ ((h >> 1) & 7)): the XOR stays inside a
+  // 128-byte line and makes the fragment reads (16 lanes = 16 heads, one chunk) free of bank
+  // conflicts.  Heads beyond H copy head 0; their results are never stored.
   bf16x8 qf[kQSteps];
   unsigned char* const q_img = &lds_kv[0][0];
   {
     const unsigned char* qrow = a.q + (size_t)row * a.H * kRowBytes;
-    const int head0 = blockIdx.z * NW * 32;
+    const int head0 = role.chunk * NW * 32;
 #pragma unroll 4
     for (int u = 0; u < kQSteps; ++u) {
       const int i = wave * kQSteps + u;        // this load fills q image bytes 1024*i ..
@@ -167,6 +846,7 @@ void sfa_main(SfaArgs a) {
     }
   }
   lds_barrier();
+  int w_fill = kMaxSplitKeys;               // first selected j of this wave (from the ballots)
   for (int j = tid; j < ntiles * kBK; j += NT) {   // NT is a multiple of 64: whole waves
     const int s = j == tid ? s_first : (j < nkeys ? idx[j] : -1);
     if (s < -1 || s >= n) flag_input(kFlagIndex);
@@ -174,8 +854,9 @@ void sfa_main(SfaArgs a) {
     lds_rows[j] = r;
     const uint64_t bal = __ballot(r >= 0);
     if ((lane & 31) == 0) lds_valid[j >> 5] = (uint32_t)(bal >> (lane & 32));
-    if (r >= 0) atomicMin(&lds_fill, j);
+    if (bal != 0) w_fill = min(w_fill, j - lane + (int)__builtin_ctzll(bal));
   }
+  if (lane == 0 && w_fill < kMaxSplitKeys) atomicMin(&lds_fill, w_fill);
   // the table's loads and this wave's q image loads have landed (vmcnt 0) ... for every wave
   __builtin_amdgcn_s_waitcnt(0x0F70);
   lds_barrier();
@@ -193,26 +874,6 @@ void sfa_main(SfaArgs a) {
   }
   lds_barrier();                            // every wave holds its q: the ring is free
 
-  // Gather tile `tile` into ring slot `buf`.  This wave loads the value columns of rows
-  // wave, wave + NW, ... (one load per row: the row id is wave-uniform, so the row's address is a
-  // scalar base and each lane adds its own swizzled 16-byte chunk) and the rope blocks
-  // wave, wave + NW, ... < 4 (8 rows x 8 chunks per load, lane i: row 8k + i/8, slot i%8).  Every
-  // wave issues the same number of loads per tile, which the ring's counter waits rely on.
-  constexpr int kRows = kBK / NW, kRope = 4 / NW;
-  auto gather_row = [&](int pr, int buf, int u) __attribute__((always_inline)) {   // pr: physical row (wave-uniform) or -1
-    const int r = wave + u * NW;
-    pr = pr < 0 ? fill_row : pr;
-    lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
-                   lds_kv[buf] + 1024 * r);
-  };
-  auto gather_rope = [&](int pr, int buf, int u) __attribute__((always_inline)) {  // pr: this lane's row, read by rope_row()
-    const int k = wave + u * NW;
-    const int r = 8 * k + (lane >> 3);
-    pr = pr < 0 ? fill_row : pr;
-    const unsigned char* src = a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r));
-    lds_dma16(src, lds_kv[buf] + kRegionB + 1024 * k);
-  };
-  auto rope_row = [&](int tile, int u) __attribute__((always_inline)) { return lds_rows[tile * kBK + 8 * (wave + u * NW) + (lane >> 3)]; };
   // fp8 cache: load L = u * NW + wave of the tile covers 16-byte chunks 64L .. 64L + 63 (lane i:
   // chunk 64L + i): code chunk c of row r for k < 1152 (k = 36r + c), then the two scale chunks of
   // each row, then a spare load that rereads fill_row's codes into the slot's unused tail.
@@ -296,16 +957,6 @@ void sfa_main(SfaArgs a) {
       *reinterpret_cast<u32x4*>(dst + kRegionB + 128 * r + 16 * ((u & 7) ^ swb(r))) = cvt8(wr[j], sr[j]);
     }
   };
-  auto issue = [&](int tile, int buf) __attribute__((always_inline)) {
-    if constexpr (KV8) { issue8(tile, buf); return; }
-    int prow[kRows];                        // read together, made scalar one at a time
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) prow[u] = lds_rows[tile * kBK + wave + u * NW];
-#pragma unroll
-    for (int u = 0; u < kRope; ++u) gather_rope(rope_row(tile, u), buf, u);
-#pragma unroll
-    for (int u = 0; u < kRows; ++u) gather_row(__builtin_amdgcn_readfirstlane(prow[u]), buf, u);
-  };
 
   // O^T: 512 latent columns (16 blocks of 32) x 32 heads
   f32x16 o[kVBlocks];
@@ -314,24 +965,13 @@ void sfa_main(SfaArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
   // Fixed softmax reference per head (log2 units), set from the first tile with a valid key:
-  // its max plus kRefMargin.  Probabilities 2^(s - m_ref) stay below 2^kRefLimit as long as no
-  // logit exceeds m_ref + kRefLimit, so the accumulator never needs rescaling.  A logit beyond
-  // that (a spread of more than 164 log2 units inside the row) raises the reference and restarts
-  // the split from its first tile.  The finite floor keeps masked (-inf) logits at probability 0.
-  constexpr float kNoRef = -1e30f;
+  // its max plus kRefMargin (see sfa_pipe).
   float m_run = kNoRef, l_run = 0.f;
   int epoch = 0;                            // restarts seen by this wave
 
-  // Per-lane LDS byte offsets.  Score A operand: row nl, chunk c = 2*ks + hh.  For ks < 32
-  // (region A) write ks = 8g + v: the slot is 16g + ((2v + hh) ^ swa), i.e. byte
-  // 256g + 16*((hh ^ swa) & 1) + 32*(v ^ (swa >> 1)); the last term only uses bits 5-7, so the
-  // address is qa ^ 32v (+ 256g).  Region B likewise: qb ^ 32v' for ks = 32 + v'.
   const int sa_nl = swa(nl), sb_nl = swb(nl);
   const int qa = 1024 * nl + 16 * ((hh ^ sa_nl) & 1) + 32 * (sa_nl >> 1);
   const int qb = kRegionB + 128 * nl + 16 * ((hh ^ sb_nl) & 1) + 32 * (sb_nl >> 1);
-  // Value A operand (transposed 8-byte reads): key = 16*k2 + 8*q + kq, columns 8*cl + 4*(lane&1)
-  // + 32*mb, cl = chunk within the 32-column block.  With mb = 4g + m' the byte offset is
-  // 16384*k2 + 256g + (pv[q] ^ 64m'): swa(key) only sees key bits 0-3 = 8q + kq.
   const int kq = 4 * hh + ((lane & 15) >> 2);
   const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
   int pv[2];
@@ -341,25 +981,18 @@ void sfa_main(SfaArgs a) {
     pv[q] = 1024 * (8 * q + kq) + 16 * (cl ^ (sa & 3)) + 64 * (sa >> 2) + 8 * (lane & 1);
   }
 
-  // One tile of the main loop.  The ring slot is a compile-time constant (the loop is unrolled by
-  // the ring depth), so every LDS address below is a per-lane base plus an immediate offset.
+  // One tile: gathers for a later tile, dequantisation, then the two products with the softmax
+  // spread over the value product.
   auto step = [&](int it, auto slot) {
     constexpr int buf = decltype(slot)::value;
     wait_ring<kDmaWave>(min(kStages - 2, ntiles_run - 1 - it));
     lds_barrier();                          // tile `it` landed for every wave; slot it-1 is free
-    if (it + kStages - 1 < ntiles_run) issue(it + kStages - 1, (buf + kStages - 1) % kStages);
-    if constexpr (KV8) {                    // every wave is past the previous tile's products
-      dequant8(buf);
-      lds_barrier();
-    }
-    const unsigned char* tile = KV8 ? lds_kv[0] : lds_kv[buf];
+    if (it + kStages - 1 < ntiles_run) issue8(it + kStages - 1, (buf + kStages - 1) % kStages);
+    dequant8(buf);                          // every wave is past the previous tile's products
+    lds_barrier();
+    const unsigned char* tile = lds_kv[0];
     const uint32_t valid = lds_valid[it];
 
-    // S^T = X q^T: rows = the tile's 32 keys, columns = this wave's 32 heads.  The A fragments
-    // stream through a 4-deep register ring: the read for step ks + 4 is issued right behind the
-    // MFMA of step ks, so LDS latency hides under the MFMAs in between.
-    // The XOR-ed offsets are formed per read (one VALU op each) from bases the compiler may not
-    // hoist: precomputing all 36 + 64 of them would hold that many registers across the loop.
     int qa_t = qa, qb_t = qb, pv0 = pv[0], pv1 = pv[1];
     asm volatile("" : "+v"(qa_t), "+v"(qb_t), "+v"(pv0), "+v"(pv1));
     auto a_frag = [&](int ks) {
@@ -384,43 +1017,19 @@ void sfa_main(SfaArgs a) {
       s = mfma_bf16(af, qf[ks], s);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the first value-product fragments load while the softmax runs
     s16x4 vring[kRingV][2];
 #pragma unroll
     for (int j = 0; j < kRingV; ++j) { vring[j][0] = v_frag(j, 0); vring[j][1] = v_frag(j, 1); }
 
-    // Online softmax over the 16 keys this lane holds (+ the other half-wave's 16).  The
-    // probabilities 2^(s - m_ref) need only the fixed reference, not this tile's max, which serves
-    // the first tile (it sets the reference) and the restart check.  So the keys of the value
-    // product's first K step are exponentiated right away and the rest of the softmax (the other 8
-    // exponentials, the sums, the cross-half max) runs between its MFMAs, under the matrix pipe.
-    // A restart discards this pass, so a tile exponentiated against a reference it then raises
-    // never reaches the output.
-    float mloc = -INFINITY;
-    if (valid == 0xFFFFFFFFu) {             // wave-uniform: every key of the tile is selected
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] *= a.scale_log2;
-        mloc = fmaxf(mloc, s[r]);
-      }
-    } else {
-      const uint32_t vmask = valid >> (4 * hh);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 8 * (r >> 2) + (r & 3);        // + 4*hh, folded into `vmask`
-        s[r] = ((vmask >> key) & 1u) ? s[r] * a.scale_log2 : -INFINITY;
-        mloc = fmaxf(mloc, s[r]);
-      }
-    }
+    mask_keys(s, valid, hh);
+    const float mloc = raw_max(s, 0, 16, -INFINITY) * a.scale_log2;
     // every lane sets its reference on the same tile (the first with a selected key): uniform
     if (__builtin_amdgcn_readfirstlane(m_run == kNoRef ? 1 : 0)) {
       const float m0 = xor32_max(mloc);
       if (m0 > -INFINITY) m_run = m0 + kRefMargin;
     }
 #pragma unroll
-    for (int r = 0; r < 8; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_run);
-    // P^T as the B operand of the value product: K step k2 covers keys 16*k2 .. 16*k2 + 15; this
-    // lane's 8 values are keys 16*k2 + {0..3, 8..11} + 4*hh (accumulator rows of the score tile)
+    for (int r = 0; r < 8; ++r) s[r] = prob(s[r], a.scale_log2, m_run);
     auto pack_p = [&](int k2) {
       u32x4 v;
 #pragma unroll
@@ -430,10 +1039,6 @@ void sfa_main(SfaArgs a) {
     bf16x8 pf[2];
     pf[0] = pack_p(0);
     float mx = mloc, psum = 0.f;
-    // O^T += V^T P^T.  The A operand (latent column m, the same 8 keys) comes from two transposed
-    // reads of the row-major tile: a 16-lane group reading 8 bytes (4 columns) of 4 consecutive
-    // keys hands lane i the 4 keys of column i.  Same 4-deep ring as the score product;
-    // consecutive MFMAs go to different accumulators.
 #pragma unroll
     for (int j = 0; j < 2 * kVBlocks; ++j) {
       const int k2 = j >> 4, mb = j & 15;
@@ -443,9 +1048,8 @@ void sfa_main(SfaArgs a) {
         vring[j % kRingV][1] = v_frag(j + kRingV, 1);
       }
       o[mb] = mfma_bf16(vf, pf[k2], o[mb]);
-      // the rest of the softmax, one slice after each MFMA of the first K step
       if (j < 8) {
-        s[8 + j] = __builtin_amdgcn_exp2f(s[8 + j] - m_run);
+        s[8 + j] = prob(s[8 + j], a.scale_log2, m_run);
       } else if (j == 8) {
         pf[1] = pack_p(1);
       } else if (j == 9) {
@@ -464,10 +1068,9 @@ void sfa_main(SfaArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // First gathers; the first step waits for tile 0 alone and computes while tiles 1 and 2 land.
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i)
-    if (i < ntiles_run) issue(i, i);
+    if (i < ntiles_run) issue8(i, i);
   for (;;) {
     for (int it = 0; it < ntiles_run; it += kStages) {
       step(it, std::integral_constant<int, 0>{});
@@ -476,8 +1079,6 @@ void sfa_main(SfaArgs a) {
       if (it + 3 < ntiles_run) step(it + 3, std::integral_constant<int, 3>{});
     }
     static_assert(kStages == 4, "the main loop above is unrolled for a 4-slot ring");
-    // every wave sees the same restart request after the barrier; the gathers of this pass have
-    // all been waited for (the last step waits for vmcnt 0)
     lds_barrier();
     const int req = lds_epoch;
     if (req == epoch) break;
@@ -490,149 +1091,9 @@ void sfa_main(SfaArgs a) {
     lds_barrier();                          // all waves read the request before slot 0 is refilled
 #pragma unroll
     for (int i = 0; i < kStages - 1; ++i)
-      if (i < ntiles_run) issue(i, i);
+      if (i < ntiles_run) issue8(i, i);
   }
-  if (a.n_splits == 1) {
-    if (hvalid) {
-      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV;
-#pragma unroll
-      for (int mb = 0; mb < kVBlocks; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 32 * mb + 8 * j + 4 * hh;
-          uint2 v;
-          v.x = pack_bf16(o[mb][4 * j] * inv, o[mb][4 * j + 1] * inv);
-          v.y = pack_bf16(o[mb][4 * j + 2] * inv, o[mb][4 * j + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + d) = v;
-        }
-      if (a.lse != nullptr && hh == 0)
-        a.lse[(size_t)row * a.H + head] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    }
-  } else {
-    const size_t ps = (size_t)row * a.n_splits + split;
-    if (hvalid && hh == 0) {
-      a.part_ml[(ps * a.H + head) * 2] = m_run;
-      a.part_ml[(ps * a.H + head) * 2 + 1] = l_run;
-    }
-    // Partial O (not divided by l: the combine folds 1/l into its weights) as bf16 pairs
-    // (registers 2k, 2k+1) in the accumulator's own lane order, [head group][block][half][lane]
-    // [4 pairs]: each store instruction writes 1 KB contiguous (16 bytes per lane).  Half the
-    // bytes of fp32 partials; bf16 keeps 2^-9 relative to each value, far inside the output
-    // tolerance, and its range covers the accumulator's (probabilities stay below 2^kRefLimit).
-    if (gg >= NGT) return;
-    uint32_t* dst = a.part_o + ((ps * NGT + gg) * kVBlocks) * 8 * 64;
-#pragma unroll
-    for (int mb = 0; mb < kVBlocks; ++mb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 v;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int k = 4 * half + q;
-          v[q] = pack_bf16(o[mb][2 * k], o[mb][2 * k + 1]);
-        }
-        *reinterpret_cast<u32x4*>(dst + ((mb * 2 + half) * 64 + lane) * 4) = v;
-      }
-  }
-}
-
-// Merges the split partials.  Grid (query row, 32-head group, chunk): the 8*SG chunks of a
-// (row, group) share its 8192 bf16 pairs, 4 pairs (one 16-byte load) of one head per thread;
-// with SG > 1 the workgroup's SG thread groups take every SG-th split and are summed in LDS at
-// the end (more workgroups in flight when there are many splits).  Every workgroup first rebuilds
-// the per-head merge weights of its group: with unnormalised partials O_i the weight of split i
-// is 2^(m_i - M) / L, L = sum_i 2^(m_i - M) l_i.
-
-struct CombineArgs {
-  const float* part_ml;
-  const uint32_t* part_o;
-  __bf16* out;
-  float* lse;
-  int H, n_splits, waves;
-};
-
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-
-template <int SG>
-__global__ __launch_bounds__(256) void sfa_combine(CombineArgs a) {
-  constexpr int kMaxSplits = 64;
-  __shared__ float wgt[kMaxSplits][32];
-  __shared__ float sm[kMaxSplits][32];
-  const int tid = threadIdx.x;
-  const int row = blockIdx.x, g = blockIdx.y, chunk = blockIdx.z;
-  const int S = a.n_splits, NG = a.waves;
-  // (m_i, l_i) of every split and head of the group: all loads in one round
-  for (int i = tid >> 5; i < S; i += 8) {
-    const int head = g * 32 + (tid & 31);
-    float m = -INFINITY, l = 0.f;
-    if (head < a.H) {
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (((size_t)row * S + i) * a.H + head) * 2);
-      m = ml.x; l = ml.y;
-    }
-    sm[i][tid & 31] = m;
-    wgt[i][tid & 31] = l;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    const int head = g * 32 + tid;
-    float M = -INFINITY;
-    for (int i = 0; i < S; ++i) M = fmaxf(M, sm[i][tid]);
-    float L = 0.f;
-    for (int i = 0; i < S; ++i) {
-      const float e = M != -INFINITY ? exp2f(sm[i][tid] - M) : 0.f;
-      L += e * wgt[i][tid];
-      wgt[i][tid] = e;
-    }
-    const float inv_L = L > 0.f ? 1.f / L : 0.f;
-    for (int i = 0; i < S; ++i) wgt[i][tid] *= inv_L;
-    if (a.lse != nullptr && head < a.H && chunk == 0)
-      a.lse[(size_t)row * a.H + head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  __syncthreads();
-  // this thread's 16-byte unit u of the group's [mb][half][lane][4 pairs] block (8192 pairs):
-  // 4 register pairs of one head (accumulator lane), i.e. output columns d0 .. d0 + 3 and
-  // d0 + 8 .. d0 + 11
-  constexpr int TG = 256 / SG;              // threads per split group
-  const int sg = tid / TG, t64 = tid % TG;
-  const int u = chunk * TG + t64;
-  const int lane = u & 63, half = (u >> 6) & 1, mb = u >> 7;
-  const int nl = lane & 31, hh = lane >> 5;
-  const size_t per_split = (size_t)NG * kVBlocks * 8 * 64;
-  const uint32_t* src = a.part_o + (size_t)row * S * per_split + (size_t)g * kVBlocks * 8 * 64 + 4 * (size_t)u;
-  float acc[4][2] = {};
-#pragma unroll 4
-  for (int sp = sg; sp < S; sp += SG) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + sp * per_split);
-    const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
-    const float wq = wgt[sp][nl];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[q][0] = fmaf(wq, bf16_lo(vv[q]), acc[q][0]);
-      acc[q][1] = fmaf(wq, bf16_hi(vv[q]), acc[q][1]);
-    }
-  }
-  if constexpr (SG > 1) {
-    __shared__ float red[SG - 1][TG][8];
-    if (sg > 0) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { red[sg - 1][t64][2 * q] = acc[q][0]; red[sg - 1][t64][2 * q + 1] = acc[q][1]; }
-    }
-    __syncthreads();
-    if (sg != 0) return;
-#pragma unroll
-    for (int k = 0; k < SG - 1; ++k)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) { acc[q][0] += red[k][t64][2 * q]; acc[q][1] += red[k][t64][2 * q + 1]; }
-  }
-  // register pair k = 4*half + q holds columns 32mb + 8(k >> 1) + 4hh + 2(k & 1) + {0, 1}
-  const int head = g * 32 + nl;
-  if (head < a.H) {
-    uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)row * a.H + head) * kDimV + 32 * mb + 16 * half + 4 * hh;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc[0][0], acc[0][1]), pack_bf16(acc[1][0], acc[1][1]));
-    *reinterpret_cast<uint2*>(dst + 8) = make_uint2(pack_bf16(acc[2][0], acc[2][1]), pack_bf16(acc[3][0], acc[3][1]));
-  }
+  finish_split<NW>(a, o, m_run, l_run, row, split, gg, tid);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -653,9 +1114,8 @@ AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   const int rows = L.batch * S.T;
   // splits: enough workgroups (rows x head chunks x splits) to cover the GPU's 256 compute units,
   // at most 64 splits, each holding a whole number of 32-row tiles.  A split of fewer than 4 tiles
-  // pays more for its partial output (written, then read back by the combine) and its prologue
-  // than its extra parallelism returns, so splits keep 4 tiles as long as the grid still has 128
-  // workgroups (8 rows at K = 2048: 16 splits of 4 tiles measured faster than 32 of 2).
+  // pays more for its partial output and its prologue than its extra parallelism returns, so
+  // splits keep 4 tiles as long as the grid still has 128 workgroups.
   const int tiles = (S.top_k + kBK - 1) / kBK;
   const int per_split = std::max(rows * p.head_chunks, 1);
   int splits = (256 + per_split - 1) / per_split;
@@ -665,10 +1125,19 @@ AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S) {
   const int tiles_per = (tiles + splits - 1) / splits;
   p.keys_per_split = tiles_per * kBK;
   p.n_splits = (tiles + tiles_per - 1) / tiles_per;
+  // combine parts per (row, head group): about 256 combine workgroups in all; a part gives each
+  // of its threads 1, 2, 4 or 8 of the group's 2048 units
+  const int groups = std::max(rows * p.waves, 1);
+  const int nt = 64 * p.groups_per_wg;
+  const int max_parts = 2048 / nt, min_parts = std::max(1, 2048 / (8 * nt));
+  int parts = min_parts;
+  while (parts < max_parts && groups * parts * 2 <= 256) parts *= 2;
+  p.comb_parts = parts;
   size_t off = 0;
   if (p.n_splits > 1) {
     p.off_ml = off; off = align_up(off + (size_t)rows * p.n_splits * S.heads * 2 * 4, 256);
-    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kVBlocks * 8 * 64 * 4, 256);
+    p.off_part = off; off = align_up(off + (size_t)rows * p.n_splits * p.waves * kPartWords * 4, 256);
+    p.off_sync = off; off = align_up(off + (size_t)rows * p.waves * parts * p.n_splits * 8, 256);
   }
   p.total = off;
   return p;
@@ -685,35 +1154,38 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   s.out = static_cast<__bf16*>(a.out);
   s.lse = a.lse;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  s.part_ml = p.n_splits > 1 ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
-  s.part_o = p.n_splits > 1 ? reinterpret_cast<uint32_t*>(ws + p.off_part) : nullptr;
+  const bool split = p.n_splits > 1;
+  s.part_ml = split ? reinterpret_cast<float*>(ws + p.off_ml) : nullptr;
+  s.part_o = split ? reinterpret_cast<uint32_t*>(ws + p.off_part) : nullptr;
+  s.sync = split ? reinterpret_cast<unsigned long long*>(ws + p.off_sync) : nullptr;
+  s.tag = split ? next_call_tag() : 0ull;
   s.T = a.T; s.H = a.heads; s.K = a.top_k; s.max_pages = a.max_pages; s.num_pages = a.num_pages;
-  s.n_splits = p.n_splits; s.keys_per_split = p.keys_per_split; s.max_seq_len = a.max_seq_len;
+  s.n_splits = p.n_splits; s.keys_per_split = p.keys_per_split;
+  s.max_seq_len = a.max_seq_len;
   s.scale_log2 = a.sm_scale * kLog2e;
   const int rows = a.B * a.T;
-  const dim3 grid(rows, p.n_splits, p.head_chunks);
-  {
-    LaunchScope ls("sfa_main", st);
-    const bool kv8 = a.kv_scale != nullptr;
-    if (p.groups_per_wg == 4) {
-      if (kv8) hipLaunchKernelGGL((sfa_main<4, true>), grid, dim3(256), 0, st, s);
-      else hipLaunchKernelGGL(sfa_main<4>, grid, dim3(256), 0, st, s);
-    } else if (p.groups_per_wg == 2) {
-      if (kv8) hipLaunchKernelGGL((sfa_main<2, true>), grid, dim3(128), 0, st, s);
-      else hipLaunchKernelGGL(sfa_main<2>, grid, dim3(128), 0, st, s);
-    } else {
-      if (kv8) hipLaunchKernelGGL((sfa_main<1, true>), grid, dim3(64), 0, st, s);
-      else hipLaunchKernelGGL(sfa_main<1>, grid, dim3(64), 0, st, s);
-    }
-  }
-  if (p.n_splits > 1) {
-    LaunchScope ls("sfa_combine", st);
-    CombineArgs c;
-    c.part_ml = s.part_ml; c.part_o = s.part_o; c.out = s.out; c.lse = a.lse;
-    c.H = a.heads; c.n_splits = p.n_splits; c.waves = p.waves;
-    if (p.n_splits > 16) hipLaunchKernelGGL(sfa_combine<4>, dim3(rows, p.waves, 32), dim3(256), 0, st, c);
-    else if (p.n_splits > 8) hipLaunchKernelGGL(sfa_combine<2>, dim3(rows, p.waves, 16), dim3(256), 0, st, c);
-    else hipLaunchKernelGGL(sfa_combine<1>, dim3(rows, p.waves, 8), dim3(256), 0, st, c);
+  s.rows = rows; s.head_chunks = p.head_chunks; s.comb_parts = p.comb_parts;
+  // split workgroups first, then (several splits) the combine parts
+  const long long n_main = (long long)rows * p.n_splits * p.head_chunks;
+  const long long n_comb = split ? (long long)rows * p.waves * p.comb_parts : 0;
+  const dim3 grid((unsigned)(n_main + n_comb));
+  LaunchScope ls("sfa_main", st);
+  const bool kv8 = a.kv_scale != nullptr;
+  const unsigned long long kv_bytes = (unsigned long long)a.num_pages * kPage * kRowBytes;
+  const bool buf = kv_bytes < 0xFFFFFFFFull;
+  s.kv_bytes = buf ? (uint32_t)kv_bytes : 0u;
+  if (p.groups_per_wg == 4) {
+    if (kv8) hipLaunchKernelGGL(sfa_main_kv8<4>, grid, dim3(256), 0, st, s);
+    else if (buf) hipLaunchKernelGGL((sfa_pipe<4, true>), grid, dim3(256), 0, st, s);
+    else hipLaunchKernelGGL((sfa_pipe<4, false>), grid, dim3(256), 0, st, s);
+  } else if (p.groups_per_wg == 2) {
+    if (kv8) hipLaunchKernelGGL(sfa_main_kv8<2>, grid, dim3(128), 0, st, s);
+    else if (buf) hipLaunchKernelGGL((sfa_pipe<2, true>), grid, dim3(128), 0, st, s);
+    else hipLaunchKernelGGL((sfa_pipe<2, false>), grid, dim3(128), 0, st, s);
+  } else {
+    if (kv8) hipLaunchKernelGGL(sfa_main_kv8<1>, grid, dim3(64), 0, st, s);
+    else if (buf) hipLaunchKernelGGL((sfa_pipe<1, true>), grid, dim3(64), 0, st, s);
+    else hipLaunchKernelGGL((sfa_pipe<1, false>), grid, dim3(64), 0, st, s);
   }
   return hipGetLastError();
 }
