@@ -13,6 +13,7 @@
  *   - Tensor pointers are DEVICE pointers into caller-owned memory, contiguous, row-major, with
  *     the alignment stated per argument.  The library never allocates, frees or retains device
  *     memory; scratch comes from the caller's `workspace` (size from the *_workspace_size call).
+ *     The one exception is dsa_sparse_attn_noalloc, which uses a static per-GPU array instead.
  *   - Calls are asynchronous on `stream` (NULL = the null stream); nothing is synchronised and
  *     nothing is allocated, so a call may be captured into a hipGraph.  Buffers must stay alive
  *     until the stream has passed the call.  Calls are deterministic: identical inputs give
@@ -190,6 +191,21 @@ dsa_status dsa_sparse_attn(const void *q, const void *kv_cache, const int32_t *i
                            const dsa_paged_layout *layout, const dsa_attn_shape *shape,
                            void *out, float *lse, void *workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* Sparse Flash Attention for callers that cannot allocate device memory or own a workspace (code
+ * under hipGraph capture, tight serving loops, harnesses that forbid allocation).  Same operation,
+ * arguments, output and errors as dsa_sparse_attn, minus the workspace: the scratch comes from a
+ * static array of DSA_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU, held from
+ * the first call on that GPU until the process ends.  The call allocates nothing (no hipMalloc,
+ * no hipFree).  A shape whose scratch need (dsa_sparse_attn_workspace_size) exceeds
+ * DSA_NOALLOC_SCRATCH_BYTES returns DSA_ERR_WORKSPACE and launches nothing; every shape the
+ * library supports fits today.  All calls on one GPU share its array: calls that may overlap on
+ * one GPU (different streams, no ordering between them) race and give wrong results; calls
+ * ordered on one stream are safe and need no clearing between them. */
+#define DSA_NOALLOC_SCRATCH_BYTES (72u << 20)
+dsa_status dsa_sparse_attn_noalloc(const void *q, const void *kv_cache, const int32_t *idx,
+                                   const dsa_paged_layout *layout, const dsa_attn_shape *shape,
+                                   void *out, float *lse, hipStream_t stream);
 
 /* Sparse Flash Attention over an FP8 latent cache ([P1] §4: the SFA cache stored in FP8 with
  * per-token scales over 128-wide tiles; the products stay BF16 and the dequantised BF16 tile feeds

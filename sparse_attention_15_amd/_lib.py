@@ -56,7 +56,7 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_fp8_quantize_heads", "dsa_profile_start",
+           "dsa_sparse_attn", "dsa_sparse_attn_noalloc", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_fp8_quantize_heads", "dsa_profile_start",
            "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_sparse_attn.argtypes = [vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
                                   vp, vp, vp, sz, vp]
     L.dsa_sparse_attn.restype = ctypes.c_int
+    L.dsa_sparse_attn_noalloc.argtypes = [vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
+                                          vp, vp, vp]
+    L.dsa_sparse_attn_noalloc.restype = ctypes.c_int
     L.dsa_sparse_attn_fp8kv.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Layout), ctypes.POINTER(AttnShape),
                                         vp, vp, vp, sz, vp]
     L.dsa_sparse_attn_fp8kv.restype = ctypes.c_int
@@ -240,6 +243,25 @@ def dsa_sparse_attn(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float,
     _check(lib().dsa_sparse_attn(_ptr(q), _ptr(kv_cache), _ptr(idx), ctypes.byref(layout),
                                  ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(workspace), wsb,
                                  _stream(stream)))
+    return out, lse
+
+
+def dsa_sparse_attn_noalloc(q, kv_cache, idx, block_table, seq_lens, *, sm_scale: float,
+                            max_seq_len: int, num_pages: int | None = None, out=None, lse=None,
+                            want_lse: bool = True, stream=None):
+    """dsa_sparse_attn without a workspace: the library's static per-GPU scratch is used instead
+    (outputs are still allocated here when not given)."""
+    B, T, H, D = q.shape
+    K = idx.shape[-1]
+    P = kv_cache.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    shape = AttnShape(T, H, D, DIM_V, K, float(sm_scale))
+    if out is None:
+        out = torch.empty((B, T, H, DIM_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device)
+    _check(lib().dsa_sparse_attn_noalloc(_ptr(q), _ptr(kv_cache), _ptr(idx), ctypes.byref(layout),
+                                         ctypes.byref(shape), _ptr(out), _ptr(lse), _stream(stream)))
     return out, lse
 
 

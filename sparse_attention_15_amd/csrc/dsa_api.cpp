@@ -238,7 +238,7 @@ size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout* layout, const dsa_
 static dsa_status sparse_attn_impl(const void* q, const void* kv_cache, const float* kv_scale, bool kv8,
                                    const int32_t* idx, const dsa_paged_layout* layout,
                                    const dsa_attn_shape* shape, void* out, float* lse, void* workspace,
-                                   size_t workspace_bytes, hipStream_t stream) {
+                                   size_t workspace_bytes, bool own_scratch, hipStream_t stream) {
   dsa_status st = check_attn_shape(shape);
   if (st != DSA_OK) return st;
   if ((st = check_layout(layout, shape->T)) != DSA_OK) return st;
@@ -249,7 +249,17 @@ static dsa_status sparse_attn_impl(const void* q, const void* kv_cache, const fl
       (lse != nullptr && !aligned(lse, 4)) || (kv8 && !aligned(kv_scale, 16)))
     return fail(DSA_ERR_ALIGN, "q / kv_cache / out / kv_scale need 16-byte alignment, idx / lse 4-byte");
   const dsa::AttnPlan plan = dsa::plan_attn(*layout, *shape);
-  if (plan.total > 0) {
+  if (own_scratch) {
+    // the library's static per-device scratch stands in for the caller's workspace
+    if (plan.total > dsa::attn_scratch_bytes())
+      return fail(DSA_ERR_WORKSPACE, "this shape needs %zu bytes of scratch; the library holds %zu",
+                  plan.total, dsa::attn_scratch_bytes());
+    workspace = nullptr;
+    if (plan.total > 0) {
+      const hipError_t e = dsa::attn_scratch(&workspace);
+      if (e != hipSuccess) return fail(DSA_ERR_HIP, "resolving the scratch address: %s", hipGetErrorString(e));
+    }
+  } else if (plan.total > 0) {
     if (workspace == nullptr || workspace_bytes < plan.total)
       return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, plan.total);
     if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace must be 256-byte aligned");
@@ -270,7 +280,14 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv_cache, const int32_t* i
                            const dsa_paged_layout* layout, const dsa_attn_shape* shape, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return sparse_attn_impl(q, kv_cache, nullptr, false, idx, layout, shape, out, lse, workspace,
-                          workspace_bytes, stream);
+                          workspace_bytes, false, stream);
+}
+
+dsa_status dsa_sparse_attn_noalloc(const void* q, const void* kv_cache, const int32_t* idx,
+                                   const dsa_paged_layout* layout, const dsa_attn_shape* shape,
+                                   void* out, float* lse, hipStream_t stream) {
+  return sparse_attn_impl(q, kv_cache, nullptr, false, idx, layout, shape, out, lse, nullptr, 0, true,
+                          stream);
 }
 
 dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_codes, const float* kv_scale,
@@ -278,7 +295,7 @@ dsa_status dsa_sparse_attn_fp8kv(const void* q, const void* kv_codes, const floa
                                  const dsa_attn_shape* shape, void* out, float* lse, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
   return sparse_attn_impl(q, kv_codes, kv_scale, true, idx, layout, shape, out, lse, workspace,
-                          workspace_bytes, stream);
+                          workspace_bytes, false, stream);
 }
 
 }  // extern "C"

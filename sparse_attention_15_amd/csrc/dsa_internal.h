@@ -116,4 +116,10 @@ struct AttnArgs {
 AttnPlan plan_attn(const dsa_paged_layout& L, const dsa_attn_shape& S);
 hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t stream);
 
+// The attention library's own scratch for callers that cannot allocate: its size, and its device
+// address on the current device (resolved on the first call per device, then cached).
+constexpr int kMaxDevices = 64;
+size_t attn_scratch_bytes();
+hipError_t attn_scratch(void** ptr);
+
 }  // namespace dsa

@@ -23,8 +23,9 @@
 // for the exponentials or the gather issue of the same tile.
 //
 // A row with several splits is merged in the same launch: each split publishes its partial
-// (m, l and the unnormalised O in bf16) and counts it in a per-(row, head group) word; combine
-// workgroups, placed after all split workgroups in the grid, wait for their row's count and merge
+// (m, l and the unnormalised O in bf16), then sets its ready flags (one per combine part) to the
+// call's 64-bit tag; combine workgroups, placed after all split workgroups in the grid, wait until
+// every split of their (row, head group) shows the tag, clear those flags again, and merge
 //     M = max_i m_i,  L = sum_i 2^(m_i - M) l_i,  out = sum_i 2^(m_i - M) O_i / L,  lse = (M + log2 L) ln 2
 // summing the splits in index order, so the output does not depend on which split finished first.
 //
@@ -36,6 +37,7 @@
 // gathered into, so the products run unchanged.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "dsa_device.h"
@@ -1098,6 +1100,33 @@ void sfa_main_kv8(SfaArgs a) {
 
 // ------------------------------------------------------------------------------------------------
 static size_t align_up(size_t x, size_t al) { return (x + al - 1) / al * al; }
+
+// Scratch of dsa_sparse_attn_noalloc: one copy per GPU, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a handle); it resolves the device
+// address once per device with hipGetSymbolAddress and passes that.  Nothing in it has to start at
+// zero: the ready flags are compared with the call's own tag and cleared by their reader.
+constexpr size_t kAttnScratchBytes = DSA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+size_t attn_scratch_bytes() { return kAttnScratchBytes; }
+
+hipError_t attn_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t attn_take_input_flags(uint32_t* flags) {
   uint32_t z = 0;

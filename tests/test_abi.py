@@ -110,6 +110,39 @@ def test_attn_rejects(kw, status):
     assert _attn_call(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(idx=None), 1), (dict(out=None), 1),
+    (dict(q=FAKE + 2), 3), (dict(lse=FAKE + 2), 3), (dict(shape=_ashape(H=100)), 4),
+    (dict(layout=_layout(num_pages=0)), 2),
+])
+def test_attn_noalloc_rejects(kw, status):
+    kw = {k: v for k, v in kw.items() if k not in ("ws", "wsb")}
+    layout = kw.pop("layout", None) or _layout()
+    shape = kw.pop("shape", None) or _ashape(K=2048)
+    a = dict(q=FAKE, kv=FAKE, idx=FAKE, out=FAKE, lse=None)
+    a.update(kw)
+    st = dsa.lib().dsa_sparse_attn_noalloc(a["q"], a["kv"], a["idx"], ctypes.byref(layout),
+                                           ctypes.byref(shape), a["out"], a["lse"], None)
+    assert st == status
+    assert dsa.lib().dsa_last_error().decode() != ""
+
+
+def test_noalloc_scratch_covers_every_supported_attention_shape():
+    """The static scratch of the no-alloc entry point holds the workspace of every shape the
+    attention plan accepts (heads 16..128, K up to 2048, any row count)."""
+    limit = 72 << 20
+    text = open(HEADER).read()
+    assert re.search(r"#define DSA_NOALLOC_SCRATCH_BYTES \(72u << 20\)", text)
+    worst = 0
+    for rows in list(range(1, 600)) + [1024, 4096, 8192]:
+        for heads in range(16, 129, 16):
+            for k in (2048, 2047, 1000, 256, 33):
+                need = dsa.dsa_sparse_attn_workspace_size(_layout(B=rows, max_pages=4, max_len=256),
+                                                          _ashape(H=heads, K=k))
+                worst = max(worst, need)
+    assert 0 < worst <= limit, worst
+
+
 def test_quantisers_reject_grids_past_31_bits():
     lib = dsa.lib()
     assert lib.dsa_mxfp8_quantize(FAKE, 1 << 40, 32, FAKE, FAKE, None) == 2
