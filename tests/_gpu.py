@@ -30,8 +30,36 @@ def up(a: np.ndarray, dtype=None) -> torch.Tensor:
     return torch.from_numpy(a).to(DEV)
 
 
+GUARD = 4096          # bytes of canary before and after every guarded buffer
+CANARY = 0xA5
+
+
+class Guarded:
+    """A device buffer with GUARD canary bytes on both sides (the interior keeps 256-byte
+    alignment); intact() tells whether a call wrote outside the interior."""
+
+    def __init__(self, shape, dtype, nbytes=None):
+        item = torch.empty((), dtype=dtype).element_size()
+        n = int(np.prod(shape)) * item if nbytes is None else int(nbytes)
+        n = max(n, item)
+        self.raw = torch.full((n + 2 * GUARD,), CANARY, dtype=torch.uint8, device=DEV)
+        inner = self.raw[GUARD:GUARD + n]
+        self.t = inner.view(dtype).view(shape) if nbytes is None else inner
+        self.nbytes = n
+
+    def intact(self) -> bool:
+        return bool((self.raw[:GUARD] == CANARY).all()) and bool((self.raw[-GUARD:] == CANARY).all())
+
+
+def check_guards(*bufs):
+    torch.cuda.synchronize()
+    for name, g in bufs:
+        assert g.intact(), f"write outside {name}"
+
+
 class Dev:
-    """A case's tensors in device memory."""
+    """A case's tensors in device memory.  Calls made without explicit output or workspace
+    buffers run on guarded buffers, and the canaries around each are checked after the call."""
 
     def __init__(self, c):
         self.c = c
@@ -52,6 +80,15 @@ class Dev:
 
     def indexer(self, **kw) -> torch.Tensor:
         s = self.c.spec
+        if not kw:
+            g_out = Guarded((s.B, s.T, s.K), torch.int32)
+            lay = dsa.make_layout(self.bt, self.sl, self.c.num_pages, s.max_len)
+            dt = dsa.DSA_MXFP8_E4M3 if self.mx else (dsa.DSA_FP8_E4M3 if self.fp8 else dsa.DSA_BF16)
+            need = dsa.dsa_indexer_workspace_size(lay, dsa.IndexerShape(s.T, s.HI, s.DI, s.K, dt))
+            g_ws = Guarded(None, torch.uint8, nbytes=need)
+            r = self.indexer(idx_out=g_out.t, workspace=g_ws.t)
+            check_guards(("idx_out", g_out), ("indexer workspace", g_ws))
+            return r
         return dsa.dsa_indexer_topk(self.q_idx, self.q_scale, self.w, self.k, self.k_scale, self.bt,
                                     self.sl, T=s.T, top_k=s.K, max_seq_len=s.max_len, fp8=self.fp8,
                                     mx=self.mx, num_pages=self.c.num_pages, **kw)
@@ -60,6 +97,16 @@ class Dev:
         s = self.c.spec
         if isinstance(idx, np.ndarray):
             idx = up(idx.astype(np.int32))
+        if not kw:
+            g_o = Guarded((s.B, s.T, s.H, 512), torch.bfloat16)
+            g_l = Guarded((s.B, s.T, s.H), torch.float32)
+            lay = dsa.make_layout(self.bt, self.sl, self.c.num_pages, s.max_len)
+            need = dsa.dsa_sparse_attn_workspace_size(lay, dsa.AttnShape(s.T, s.H, 576, 512, idx.shape[-1],
+                                                                         float(s.sm_scale)))
+            g_ws = Guarded(None, torch.uint8, nbytes=need)
+            r = self.attn(idx, out=g_o.t, lse=g_l.t, workspace=g_ws.t)
+            check_guards(("out", g_o), ("lse", g_l), ("attention workspace", g_ws))
+            return r
         if self.kv8:
             return dsa.dsa_sparse_attn_fp8kv(self.q_attn, self.kv, self.kv_scale, idx, self.bt, self.sl,
                                              sm_scale=s.sm_scale, max_seq_len=s.max_len,

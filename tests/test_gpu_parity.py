@@ -74,6 +74,16 @@ def test_wide_grid_exact(T, lens):
     _run(spec, exact=True)
 
 
+@pytest.mark.parametrize("T", [1, 4])
+def test_large_batch_grid_exact(T):
+    """More than 512 sequences: decode and verify leave the persistent score kernels for the
+    chunked one; the whole index tensor must still equal the oracle's."""
+    lens = np.random.default_rng([15, 77, T]).integers(100, 1200, size=520)
+    lens[:3] = (T, 257, 1199)
+    spec = W.custom("grid8_b520", len(lens), T, lens, 64, 128, 256, 32, values="grid8")
+    _run(spec, exact=True, sfa_rows=[(0, 0), (1, T - 1), (2, 0), (519, T - 1)])
+
+
 def test_tie_heavy_exact():
     spec = W.custom("ties_wide", 2, 1, (3500, 6000), 64, 128, 2048, 128, values="ties")
     _run(spec, exact=True, check_sfa=False)
