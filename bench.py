@@ -13,7 +13,13 @@ Prints ONE JSON line on stdout.  Progress goes to stderr.
               the kernel's measured HBM bytes per launch (FETCH_SIZE and WRITE_SIZE counters,
               calibrated against a copy of known size) from profiles/traffic.json, used only when
               the recorded source hash and workload match the kernel being timed, else null
-  path        whole-step algorithmic bytes / step time, against the same peak
+  path        whole-step algorithmic bytes / step time, against the same peak and (frac_of_ceiling)
+              against the measured streaming-read ceiling
+  step_us     median / p10 / p90 of single steps, from a separate pass with an event between steps
+  ceiling_gbs HBM streaming-read ceiling measured here: a read-only kernel (libdsa_ceiling.so) over
+              256 MiB buffers rotated across 2 GiB, best of several launch shapes
+  workloads   with the default workload 2: the same figures for workload 4 (B=8 x 131072, fp8
+              indexer) and workload 5 (B=16 x T=4 verify at 65536)
   cpu_baseline  the float64 CPU oracle timed on this host on the first rows of the same batch
 """
 from __future__ import annotations
@@ -164,6 +170,9 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=32)
     ap.add_argument("--cpu-budget", type=float, default=25.0)
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="with workload 2, skip the additional workload 4 and 5 entries")
     ap.add_argument("--append-kv8", action="store_true",
                     help="time dsa_latent_cache_append_fp8 instead: 8 sequences x 16384 new latent "
                          "rows (576 bf16) into the FP8 latent cache")
@@ -199,7 +208,79 @@ def main():
     if args.append_kv8:
         return bench_append_kv8(args, dev, dsa)
 
-    spec = W.config(args.workload)
+    ceiling = measure_ceiling(dev, torch) if not args.no_ceiling else None
+    if ceiling:
+        log(f"streaming-read ceiling: {ceiling['gbs']:.1f} GB/s ({ceiling['config']})")
+    r = run_workload(args.workload, args, dev, torch, dsa, W, ceiling, cpu=not args.no_cpu_baseline)
+    res = r["line"]
+    res["ceiling_gbs"] = None if ceiling is None else ceiling["gbs"]
+    res["ceiling"] = ceiling
+    if args.workload == 2 and not args.no_extra:
+        res["workloads"] = {}
+        for w in (4, 5):
+            e = run_workload(w, args, dev, torch, dsa, W, ceiling, cpu=False)["line"]
+            res["workloads"][str(w)] = {
+                "workload": e["config"]["workload"], "ms_per_step": e["ms_per_step"],
+                "queries_per_s": e["value"], "step_us": e["step_us"], "path": e["path"],
+                "roofline": e["roofline"], "kernels": e["kernels"]}
+    print(json.dumps(res), flush=True)
+
+
+def measure_ceiling(dev, torch, total_gib: float = 2.0, chunk_mib: int = 256, launches: int = 24):
+    """HBM streaming-read ceiling: the read-only kernel of libdsa_ceiling.so over chunk_mib-MiB
+    buffers, rotated across total_gib GiB so the 256 MiB last-level cache holds none of the next
+    chunk, timed with HIP events for several launch shapes; the best shape is the ceiling."""
+    import ctypes
+    from sparse_attention_15_amd.build import CEILING_LIB
+    if not os.path.exists(CEILING_LIB):
+        raise ImportError(f"{CEILING_LIB} not found: build it first")
+    L = ctypes.CDLL(CEILING_LIB)
+    L.dsa_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    L.dsa_stream_read.restype = ctypes.c_int
+    nbuf = max(2, int(total_gib * 1024 // chunk_mib))
+    nbytes = chunk_mib << 20
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i + 1) for i in range(nbuf)]
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = None
+    for blocks in (512, 1024, 2048, 4096, 8192):
+        for unroll in (2, 4, 8, -4, -8):
+            def run(k):
+                st = L.dsa_stream_read(ctypes.c_void_p(bufs[k % nbuf].data_ptr()), nbytes, blocks, unroll,
+                                       ctypes.c_void_p(sink.data_ptr()), stream)
+                if st:
+                    raise RuntimeError(f"dsa_stream_read returned {st}")
+            for k in range(3):
+                run(k)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for k in range(launches):
+                run(k + 3)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = nbytes * launches / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, blocks, unroll)
+    del bufs
+    torch.cuda.empty_cache()
+    gbs, blocks, unroll = best
+    return {"gbs": round(gbs, 1), "kernel": "stream_read_kernel (libdsa_ceiling.so)",
+            "config": f"{blocks} workgroups x 256 threads, {abs(unroll)} 16-B loads in flight per thread"
+                      + (", nontemporal" if unroll < 0 else "") + f", {chunk_mib} MiB per launch rotated over "
+                      f"{nbuf * chunk_mib / 1024:.0f} GiB, best of 25 launch shapes"}
+
+
+def percentiles(xs):
+    a = np.sort(np.asarray(xs, dtype=np.float64))
+    return {"median": round(float(np.percentile(a, 50)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "n": int(a.size)}
+
+
+def run_workload(wid, args, dev, torch, dsa, W, ceiling, cpu: bool):
+    """One named workload: upload rotated copies, warm up, time exactly args.steps steps, then a
+    per-step pass and a profiled pass.  Returns {"line": the JSON fields for this workload}."""
+    spec = W.config(wid)
     log("workload", describe(spec))
     t0 = time.perf_counter()
     case = W.make_case(spec)
@@ -272,6 +353,17 @@ def main():
     qps = spec.B * spec.T / (ms * 1e-3)
     log(f"timed {args.steps} steps: {ms * 1e3:.1f} us/step, {qps:,.0f} queries/s")
 
+    # per-step distribution: a separate pass with an event between consecutive steps
+    n_ps = max(100, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ps + 1)]
+    evs[0].record()
+    for i in range(n_ps):
+        step(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    step_us = percentiles([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(n_ps)])
+    log(f"per-step us over {n_ps} steps: {step_us}")
+
     kernels = {}
     roof = None
     if not args.no_profile:
@@ -298,16 +390,17 @@ def main():
                 ach = ab[kern] / mean_s / 1e9
                 roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBS, 4),
-                        "traffic": recorded_traffic(kern, args.workload), "kernel": kern,
+                        "frac_of_ceiling": None if ceiling is None else round(ach / ceiling["gbs"], 4),
+                        "traffic": recorded_traffic(kern, wid), "kernel": kern,
                         "kernel_mean_us": round(mean_s * 1e6, 2),
                         "algorithmic_bytes_per_launch": int(ab[kern])}
 
     path_gbs = ab["step"] / (ms * 1e-3) / 1e9
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_res = None
+    if cpu:
         log("timing the CPU oracle ...")
-        cpu = cpu_baseline(case, args.cpu_rows, args.cpu_budget)
-        log("cpu baseline:", cpu)
+        cpu_res = cpu_baseline(case, args.cpu_rows, args.cpu_budget)
+        log("cpu baseline:", cpu_res)
 
     lens = np.asarray(spec.lens)
     res = {
@@ -328,12 +421,14 @@ def main():
                    "top_k": spec.K, "indexer_heads": spec.HI, "indexer_dim": spec.DI,
                    "attn_heads": spec.H, "page": 64, "rotation_copies": R},
         "roofline": roof,
+        "step_us": step_us,
         "path": {"algorithmic_bytes_per_step": int(ab["step"]), "achieved": round(path_gbs, 1),
-                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4)},
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(path_gbs / HBM_PEAK_GBS, 4),
+                 "frac_of_ceiling": None if ceiling is None else round(path_gbs / ceiling["gbs"], 4)},
         "kernels": kernels,
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu_res,
     }
-    print(json.dumps(res), flush=True)
+    return {"line": res}
 
 
 def bench_append_kv8(args, dev, dsa):
