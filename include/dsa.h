@@ -22,6 +22,17 @@
  *     too small) are detected on the host before anything is launched; the call then returns a
  *     non-OK status, launches nothing and leaves outputs untouched.  A launch failure returns
  *     DSA_ERR_HIP.  dsa_last_error() gives a thread-local description of the last failure.
+ *   - Workgroups of one launch meet through device memory in two places: a decode indexer
+ *     workgroup waits for the workgroup that clears its row's histogram, and an attention combine
+ *     workgroup waits for the split workgroups of its row.  The workgroup waited for always has a
+ *     lower index than the waiting one, so the waits end as long as the GPU dispatches the
+ *     workgroups of a launch in index order (which AMD GPUs do).  Each wait is bounded (about 50 ms
+ *     of polling): if it ever gives up, the affected outputs are not computed from partial data --
+ *     the indexer row is written as all -1, the attention outputs of the row (out and lse) as NaN --
+ *     and dsa_debug_status() reports the timeout.  Test hooks, read at each indexer call and unset
+ *     in normal use: DSA_TEST_SYNC_SPIN_CAP=<n> bounds the indexer wait at n polls, and
+ *     DSA_TEST_WITHHOLD_TAG=1 makes the clearing workgroups skip their signal, so every indexer
+ *     row with more than top_k visible keys takes the timeout path.
  *   - Device-side preconditions (not checked on the host because the data lives on the device):
  *     T <= seq_lens[b] <= max_seq_len <= max_pages * page_size, block_table entries used by a
  *     sequence lie in [0, num_pages), fp8 scales are finite and > 0.  The kernels clamp page ids
@@ -175,7 +186,13 @@ size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_
  *     z_j = sm_scale * q[b,t,h,:] . X[s_j,:]     (X = 576-wide latent row of token s_j)
  *     out[b,t,h,:] = sum_j softmax(z)_j * X[s_j, 0:512],   lse[b,t,h] = ln sum_j exp(z_j)
  * with fp32 accumulation; out is rounded to bf16 (round to nearest even).  An empty set gives
- * out = 0 and lse = -inf.  An entry outside [0, pos], pos = seq_lens[b] - T + t (the positions
+ * out = 0 and lse = -inf.  The softmax runs against a fixed per-head reference taken from the first
+ * 32 selected keys of each split (their maximum logit + 64 in log2 units); a later logit more than
+ * 100 log2 units above it raises the reference and restarts the split from its first key, so the
+ * result is exact for any logits, and the extra cost is at most one more pass over the split per
+ * raise: a split of t 32-key tiles whose largest logit climbs by more than 164 log2 units (about
+ * 114 in natural units, after sm_scale) from each tile to the next restarts up to t - 1 times,
+ * about t^2 / 2 tile passes in all; real attention logits stay within one reference.  An entry outside [0, pos], pos = seq_lens[b] - T + t (the positions
  * query t may attend to), is skipped like -1 and sets the attention-index check that
  * dsa_debug_status() reports.
  *
@@ -272,7 +289,8 @@ int dsa_version(void);
  * see the conventions above, and record which kind failed).  Returns DSA_OK when none failed;
  * DSA_ERR_SHAPE when some did, with dsa_last_error() naming them (a block_table entry outside
  * [0, num_pages) for a visible position, a seq_lens entry outside [T, max_seq_len], an attention
- * index that is neither -1 nor a visible position); DSA_ERR_HIP if the synchronisation fails.
+ * index that is neither -1 nor a visible position, a timed-out wait between workgroups (see the
+ * conventions above)); DSA_ERR_HIP if the synchronisation fails.
  * Reading clears the record.  The checks cost a compare per page or index in the kernels'
  * set-up code and run in every build. */
 dsa_status dsa_debug_status(hipStream_t stream);

@@ -23,9 +23,20 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def build_library(verbose: bool = False, extra_flags=()) -> str:
-    """Compiles every source and links libdsa.so; returns its path.  Always rebuilds."""
-    objdir = os.path.join(PKG, "_build")
+TIMELINE_LIB = os.path.join(PKG, "libdsa_timeline.so")
+
+
+def build_timeline_library(verbose: bool = False) -> str:
+    """The timeline variant of libdsa.so (-DDSA_TIMELINE: per-workgroup time stamps in the decode
+    score and attention kernels, read by sparse_attention_15_amd.timeline); returns its path."""
+    return build_library(verbose, ["-DDSA_TIMELINE"], out=TIMELINE_LIB, objdir_name="_build_timeline",
+                         ceiling=False)
+
+
+def build_library(verbose: bool = False, extra_flags=(), out: str = LIB, objdir_name: str = "_build",
+                  ceiling: bool = True) -> str:
+    """Compiles every source and links libdsa.so (or `out`); returns its path.  Always rebuilds."""
+    objdir = os.path.join(PKG, objdir_name)
     os.makedirs(objdir, exist_ok=True)
 
     def compile_one(src):
@@ -42,12 +53,14 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    if not ceiling:
+        return out
     # the streaming-read ceiling kernel bench.py measures against, in a library of its own
     obj = os.path.join(objdir, "stream_read.hip.o")
     for cmd in ([HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "stream_read.hip"), "-o", obj],
@@ -56,7 +69,7 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"building {os.path.basename(CEILING_LIB)} failed:\n{r.stdout}\n{r.stderr}")
     os.replace(CEILING_LIB + ".tmp", CEILING_LIB)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":

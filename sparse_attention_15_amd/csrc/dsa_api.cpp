@@ -108,7 +108,8 @@ dsa_status dsa_debug_status(hipStream_t stream) {
               (f & 1u) ? " block_table entry outside [0, num_pages);" : "",
               (f & 2u) ? " seq_lens entry outside [T, max_seq_len];" : "",
               (f & 4u) ? " attention index neither -1 nor a visible position;" : "",
-              (f & 8u) ? " histogram-clear handshake timed out (workspace shared by overlapping calls?);" : "");
+              (f & 8u) ? " decode histogram-clear handshake timed out, the rows concerned were written as -1 "
+                         "(workspace shared by overlapping calls?);" : "");
 }
 
 size_t dsa_indexer_workspace_size(const dsa_paged_layout* layout, const dsa_indexer_shape* shape) {

@@ -137,6 +137,23 @@ constexpr uint32_t kFlagSync = 8u;         // a wait for another workgroup's his
 static __device__ uint32_t g_input_flags;
 __device__ __forceinline__ void flag_input(uint32_t bit) { atomicOr(&g_input_flags, bit); }
 
+// Timeline build (-DDSA_TIMELINE, libdsa_timeline.so, a measurement variant of the library):
+// thread 0 of each workgroup records the 100 MHz real-time counter at numbered points of the
+// decode score kernel and the attention kernel, one row of 8 points per workgroup (the first 8192
+// workgroups) in a per-translation-unit array; dsa_timeline_fetch_* copies it out.  In the normal
+// build the stamps compile to nothing.
+#ifdef DSA_TIMELINE
+constexpr int kTimelineWgs = 8192;
+static __device__ unsigned long long g_timeline[kTimelineWgs][8];
+#define DSA_STAMP(point)                                                                         \
+  do {                                                                                           \
+    if (threadIdx.x == 0 && blockIdx.x < kTimelineWgs)                                           \
+      g_timeline[blockIdx.x][point] = __builtin_amdgcn_s_memrealtime();                          \
+  } while (0)
+#else
+#define DSA_STAMP(point) do { } while (0)
+#endif
+
 // Length of query row (b, t): keys 0..pos are visible, pos = seq_len - T + t.  seq_len is clamped
 // to the block-table capacity so a bad length can never address past the table.
 __device__ __forceinline__ int row_visible(const int32_t* seq_lens, int b, int T, int t, int cap) {

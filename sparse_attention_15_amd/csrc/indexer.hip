@@ -23,6 +23,8 @@
 //                   row, finishes the threshold in LDS, keeps candidates above it plus the
 //                   lowest-position ties up to the quota, and merges both lists into idx_out.
 // A row with n <= K selects every visible position and skips the score scratch.
+#include <stdlib.h>
+
 #include <algorithm>
 #include <type_traits>
 
@@ -35,9 +37,11 @@ constexpr int kTileKeys = 128;    // keys staged in LDS per step (two pages)
 constexpr int kChunkKeys = 1024;  // keys per score workgroup
 constexpr int kBins = 2048;       // first radix digit: key bits 31..21
 // Control words per row, after the histograms: [0..2] the select's counters (segments done, list
-// cursors), [4..5] the 64-bit tag that marks the row's histogram cleared for this call (decode).
+// cursors), [4..5] the 64-bit tag that marks the row's histogram cleared for this call (decode),
+// [6..7] the poison words: the call's tag when a decode workgroup gave up waiting for that clear.
 constexpr int kCtl = 8;
 constexpr int kTagWord = 4;
+constexpr int kPoisonWord = 6;
 constexpr unsigned kSyncSpinCap = 1u << 20;   // waits for a tag end after ~50 ms at most
 constexpr int kThreads = 256;
 
@@ -81,6 +85,8 @@ struct ScoreArgs {
   uint32_t* hist;               // [rows, kBins]
   uint32_t* ctl;                // [rows, kCtl] control words
   unsigned long long tag;       // decode: this call's histogram-cleared tag (never 0)
+  unsigned spin_cap;            // decode: sleeps before a tag wait gives up
+  int withhold_tag;             // decode, test hook: the clearing workgroups publish no tag
   const unsigned char* q_e8;    // MXFP8: [B,T,HI,DI/32] E8M0 scale bytes of q
   const unsigned char* k_e8;    // MXFP8: [P,64,DI/32] E8M0 scale bytes of the K cache
   int B, T, max_pages, num_pages, K, n_chunks, n_qtiles, row_stride, max_seq_len;
@@ -675,7 +681,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   __shared__ float2 lds_rsc[FP8 && !MX ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
   __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? 4 : 1][MX ? NSLOT : 1][MX ? SB : 16];
   __shared__ int lds_starts[kDecodeMaxItems];      // sequences whose first tile is in this range
-  __shared__ int lds_nstarts;
+  __shared__ int lds_nstarts, lds_ok;
   __shared__ uint32_t sh[8];
   // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
   static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
@@ -686,6 +692,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 31, hh = lane >> 5;
   const int cap = a.max_seq_len;
+  DSA_STAMP(0);
 
   int carry = 0;
   for (int base = 0; base < a.B; base += kThreads) {
@@ -711,7 +718,10 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
   const int hi = (int)((long long)(blockIdx.x + 1) * total / gridDim.x);
   const int n_items = min(hi - lo, kDecodeMaxItems);   // the grid keeps hi - lo within the table
-  if (n_items <= 0) return;
+  if (n_items <= 0) {
+    DSA_STAMP(1); DSA_STAMP(2);
+    return;
+  }
 
   auto locate = [&](int f) -> int {
     int l = 0, h = a.B;
@@ -766,22 +776,34 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     }
   };
   // Adds the LDS histogram into sequence b's row once the workgroup that clears that row (the one
-  // holding its first tile) has published this call's tag.  The wait is bounded: past the cap the
-  // counts go in anyway and the debug flag records it.
+  // holding its first tile) has published this call's tag.  That workgroup has a lower index, so
+  // with workgroups dispatched in index order the wait always ends.  The wait is still bounded
+  // (a.spin_cap sleeps): past it this workgroup adds nothing, sets the debug flag and marks the row
+  // with this call's tag in its poison words, which li_select answers with a row of -1 (never a
+  // selection from a histogram that may not have been cleared or lacks these counts).
   auto flush = [&](int b) {
     if (tid == 0) {
       const unsigned long long* tagp =
           reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)b * kCtl + kTagWord);
       unsigned spins = 0;
+      int ok = 1;
       while (__hip_atomic_load(tagp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
-        if (++spins > kSyncSpinCap) { flag_input(kFlagSync); break; }
+        if (++spins > a.spin_cap) {
+          flag_input(kFlagSync);
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)b * kCtl + kPoisonWord), a.tag,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
         __builtin_amdgcn_s_sleep(2);
       }
+      lds_ok = ok;
     }
     __syncthreads();
+    const bool ok = lds_ok != 0;
     for (int i = tid; i < kBins; i += kThreads) {
       const uint32_t v = lds_hist[i];
-      if (v != 0u) atomicAdd(&a.hist[(size_t)b * kBins + i], v);
+      if (ok && v != 0u) atomicAdd(&a.hist[(size_t)b * kBins + i], v);
       lds_hist[i] = 0u;
     }
   };
@@ -809,25 +831,23 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   __syncthreads();
   // This workgroup clears the histogram and control words of every sequence it starts (no other
   // workgroup has flushed into them: they all wait for the tag), then publishes this call's tag
-  // for each.  The zeros and the tag travel through device-coherent (agent-scope) stores, which go
-  // past the per-XCD L2s, and the histogram adds are device-coherent atomics, so finishing the
-  // stores (vmcnt) before the tag is written is enough; a release/acquire fence pair would write
-  // back and invalidate whole L2s in every workgroup.
+  // for each.  Wave 0 does both: its clears go out before its first key blocks, and the wait for
+  // those blocks below (vmcnt 0, which counts stores too) also finishes the clears, so the tag
+  // follows without a wait of its own.  The zeros and the tag travel through device-coherent
+  // (agent-scope) stores, which go past the per-XCD L2s, and the histogram adds are
+  // device-coherent atomics, so finished stores are visible to every workgroup; a release/acquire
+  // fence pair would write back and invalidate whole L2s in every workgroup.
   const int n_starts = lds_nstarts;
-  for (int k = 0; k < n_starts; ++k) {
-    const int b = lds_starts[k];
-    for (int i = tid; i < kBins; i += kThreads)
-      __hip_atomic_store(&a.hist[(size_t)b * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (tid < kTagWord)
-      __hip_atomic_store(&a.ctl[(size_t)b * kCtl + tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (wave == 0) {
+    for (int k = 0; k < n_starts; ++k) {
+      const int b = lds_starts[k];
+      for (int i = lane; i < kBins; i += 64)
+        __hip_atomic_store(&a.hist[(size_t)b * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane < kTagWord)
+        __hip_atomic_store(&a.ctl[(size_t)b * kCtl + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  if (n_starts > 0) {
-    wait_vmcnt<0>();
-    __syncthreads();
-    for (int k = tid; k < n_starts; k += kThreads)
-      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * kCtl + kTagWord),
-                         a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  DSA_STAMP(1);
 
   // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i (page half wave / 2), into
   // ring slot i % NSLOT.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key %
@@ -856,8 +876,13 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   for (int u = 0; u < NSLOT; ++u)
     if (u < n_items) issue(u, u);
   // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
-  // so no wait for them lands in the main loop (it also covers the first blocks)
+  // so no wait for them lands in the main loop (it also covers the first blocks, and wave 0's
+  // clears)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (wave == 0 && !a.withhold_tag)
+    for (int k = lane; k < n_starts; k += 64)
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * kCtl + kTagWord),
+                         a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (FP8 && !MX) {
     static_assert(kDecodeMaxItems <= kThreads, "one record per thread");
     if (tid < n_items) lds_rsc[tid] = my_sc;
@@ -938,6 +963,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   }
   __syncthreads();
   flush(b_cur);
+  DSA_STAMP(2);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -952,6 +978,8 @@ struct SelectArgs {
   uint2* g_cand;            // [rows, kCandCap] (key, position) inside the threshold range
   const int32_t* seq_lens;
   int32_t* idx_out;         // [rows, K]
+  unsigned long long tag;   // decode: the score launch's tag (a row whose poison words hold it is
+                            // emitted as -1); 0 otherwise
   int T, K, row_stride, max_seq_len;
 };
 
@@ -1097,6 +1125,13 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   if (n <= a.K) {
     if (seg == 0)
       for (int j = tid; j < a.K; j += NT) out[j] = j < n ? j : -1;
+    return;
+  }
+  if (a.tag != 0ull &&
+      *reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)row * kCtl + kPoisonWord) == a.tag) {
+    // a score workgroup of this call gave up waiting for the row's histogram clear
+    if (seg == 0)
+      for (int j = tid; j < a.K; j += NT) out[j] = -1;
     return;
   }
   const int seg_len = seg_len_of(n);
@@ -1317,6 +1352,19 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
 // ------------------------------------------------------------------------------------------------
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+#ifdef DSA_TIMELINE
+extern "C" int dsa_timeline_reset_indexer(void) {
+  static unsigned long long zeros[kTimelineWgs][8];
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), zeros, sizeof zeros, 0, hipMemcpyHostToDevice) == hipSuccess ? 0 : 2;
+}
+
+extern "C" int dsa_timeline_fetch_indexer(unsigned long long* host, int wgs) {
+  if (wgs < 0 || wgs > kTimelineWgs) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), (size_t)wgs * 8 * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 2;
+}
+#endif
+
 hipError_t indexer_take_input_flags(uint32_t* flags) {
   uint32_t z = 0;
   hipError_t e = hipMemcpyFromSymbol(flags, HIP_SYMBOL(g_input_flags), sizeof(uint32_t), 0, hipMemcpyDeviceToHost);
@@ -1422,6 +1470,15 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.hist = hist;
   s.ctl = hist + (size_t)p.rows * kBins;
   s.tag = self_clear ? next_call_tag() : 0ull;
+  // Test hooks for the bounded tag wait (read per call; unset in normal use):
+  // DSA_TEST_SYNC_SPIN_CAP overrides the number of sleeps before a wait gives up, and
+  // DSA_TEST_WITHHOLD_TAG=1 makes the clearing workgroups publish no tag, so every wait times out.
+  s.spin_cap = kSyncSpinCap;
+  s.withhold_tag = 0;
+  if (self_clear) {
+    if (const char* e = getenv("DSA_TEST_SYNC_SPIN_CAP")) s.spin_cap = (unsigned)strtoul(e, nullptr, 10);
+    if (const char* e = getenv("DSA_TEST_WITHHOLD_TAG")) s.withhold_tag = atoi(e) != 0;
+  }
   s.B = a.B; s.T = a.T; s.max_pages = a.max_pages; s.num_pages = a.num_pages; s.K = a.top_k;
   s.n_chunks = p.n_chunks; s.n_qtiles = p.n_qtiles; s.row_stride = p.row_stride;
   s.max_seq_len = a.max_seq_len;
@@ -1457,6 +1514,7 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   sa.g_cand = reinterpret_cast<uint2*>(ws + p.off_cand);
   sa.seq_lens = a.seq_lens;
   sa.idx_out = a.idx_out;
+  sa.tag = s.tag;
   sa.T = a.T; sa.K = a.top_k; sa.row_stride = p.row_stride; sa.max_seq_len = a.max_seq_len;
   {
     LaunchScope ls("li_select", st);

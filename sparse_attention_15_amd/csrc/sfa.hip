@@ -276,23 +276,30 @@ __device__ __forceinline__ void sfa_combine_part(const SfaArgs& a, int row, int 
   const int tid = threadIdx.x, lane = tid & 63;
   const int S = a.n_splits, NGT = (a.H + 31) / 32;
   unsigned long long* flags = a.sync + (((size_t)row * NGT + g) * a.comb_parts + part) * S;
+  // The splits are lower-numbered workgroups of this launch, so with workgroups dispatched in index
+  // order the wait always ends; past its cap it gives up, the outputs this part writes become NaN
+  // and the debug flag is set.
+  __shared__ int timed_out;
   if (tid < 64) {
     // lane i watches the flags of splits i, i + 64, ...; polls back off (up to ~4000 cycles apart)
     unsigned spins = 0, nap = 1;
+    int late = 0;
     for (;;) {
       bool ready = true;
       for (int sp = lane; sp < S; sp += 64)
         ready &= __hip_atomic_load(&flags[sp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag;
       if (__builtin_amdgcn_readfirstlane(__ballot(!ready) == 0ull ? 1 : 0)) break;
-      if (++spins > kMergeSpinCap / 16) { if (lane == 0) flag_input(kFlagSync); break; }
+      if (++spins > kMergeSpinCap / 16) { if (lane == 0) flag_input(kFlagSync); late = 1; break; }
       for (unsigned k = 0; k < nap; ++k) __builtin_amdgcn_s_sleep(4);
       nap = nap < 16 ? 2 * nap : 16;
     }
     // only this part reads these flags: reset them for the next call
     for (int sp = lane; sp < S; sp += 64)
       __hip_atomic_store(&flags[sp], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) timed_out = late;
   }
   lds_barrier();
+  DSA_STAMP(5);
   // merge weights of every split and head of the group (wgt[S][32]), the row's lse from part 0
   for (int i = tid; i < S * 32; i += NT) {
     const int sp = i >> 5, h = g * 32 + (i & 31);
@@ -312,11 +319,11 @@ __device__ __forceinline__ void sfa_combine_part(const SfaArgs& a, int row, int 
       L += e * wgt[2 * (sp * 32 + tid) + 1];
       wgt[2 * (sp * 32 + tid)] = e;
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float inv = timed_out ? __builtin_nanf("") : (L > 0.f ? 1.f / L : 0.f);
     for (int sp = 0; sp < S; ++sp) wgt[2 * (sp * 32 + tid)] *= inv;
     const int h = g * 32 + tid;
     if (a.lse != nullptr && part == 0 && h < a.H)
-      a.lse[(size_t)row * a.H + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      a.lse[(size_t)row * a.H + h] = timed_out ? __builtin_nanf("") : (L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY);
   }
   lds_barrier();
   // units per thread: the group's 2048 units over comb_parts parts of NT threads
@@ -407,9 +414,12 @@ void sfa_pipe(SfaArgs a) {
 
   const SfaRole role = sfa_role(a);
   if (role.combine) {
+    DSA_STAMP(4);
     sfa_combine_part<NW>(a, role.row, role.g, role.part, reinterpret_cast<float*>(&lds_kv[0][0]));
+    DSA_STAMP(6);
     return;
   }
+  DSA_STAMP(0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: LDS DMA bases stay in SGPRs
   const int nl = lane & 31, hh = lane >> 5;
@@ -508,6 +518,7 @@ void sfa_pipe(SfaArgs a) {
       qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qh + 16 * ((2 * ks + hh) ^ ((nl >> 1) & 7))));
   }
   lds_barrier();                            // every wave holds its q: the ring is free
+  DSA_STAMP(1);
   // Tiles run from the first through the last tile holding a selected key (a causal row with
   // fewer visible positions than K leaves its trailing tiles empty).  Keys that are not selected
   // are gathered from the first selected row (finite data: their zero probabilities never meet a
@@ -784,7 +795,9 @@ void sfa_pipe(SfaArgs a) {
       for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
     lds_barrier();                          // all waves read the request before slot 0 is refilled
   }
+  DSA_STAMP(2);
   finish_split<NW>(a, o, m_run, l_run, row, split, gg, tid);
+  DSA_STAMP(3);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1127,6 +1140,19 @@ hipError_t attn_scratch(void** ptr) {
   *ptr = addr[dev];
   return hipSuccess;
 }
+
+#ifdef DSA_TIMELINE
+extern "C" int dsa_timeline_reset_attn(void) {
+  static unsigned long long zeros[kTimelineWgs][8];
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), zeros, sizeof zeros, 0, hipMemcpyHostToDevice) == hipSuccess ? 0 : 2;
+}
+
+extern "C" int dsa_timeline_fetch_attn(unsigned long long* host, int wgs) {
+  if (wgs < 0 || wgs > kTimelineWgs) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), (size_t)wgs * 8 * sizeof(unsigned long long), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? 0 : 2;
+}
+#endif
 
 hipError_t attn_take_input_flags(uint32_t* flags) {
   uint32_t z = 0;

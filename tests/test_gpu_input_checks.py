@@ -88,3 +88,31 @@ def test_latent_append_clamps_and_reports_bad_length_and_page():
     with pytest.raises(dsa.DsaError, match="block_table"):
         dsa.dsa_debug_status()
     dsa.dsa_debug_status()
+
+
+def test_decode_tag_wait_timeout_emits_minus_one_rows(monkeypatch):
+    """The decode score kernel's bounded wait for a row's histogram clear, forced from the host:
+    the clearing workgroups publish no tag and the waits give up after 64 sleeps.  Every kernel
+    still exits; rows with n > K come out all -1 (never a selection from an uncleared histogram),
+    rows with n <= K are unaffected, the handshake check is reported, and the next call without
+    the hooks is correct again."""
+    import numpy as np
+    import oracle
+    from tests._gpu import check_indices_band, oracle_args, to_np
+    spec = W.custom("tagwait", 3, 1, (1500, 2600, 4100), 64, 128, 2048, 16)
+    c = W.make_case(spec)
+    d = Dev(c)
+    _clear()
+    monkeypatch.setenv("DSA_TEST_WITHHOLD_TAG", "1")
+    monkeypatch.setenv("DSA_TEST_SYNC_SPIN_CAP", "64")
+    idx = to_np(d.indexer())
+    monkeypatch.delenv("DSA_TEST_WITHHOLD_TAG")
+    monkeypatch.delenv("DSA_TEST_SYNC_SPIN_CAP")
+    assert np.array_equal(idx[0, 0], np.r_[np.arange(1500), -np.ones(548)].astype(np.int32))
+    assert (idx[1:] == -1).all()
+    with pytest.raises(dsa.DsaError, match="handshake"):
+        dsa.dsa_debug_status()
+    idx = to_np(d.indexer())
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=2048, dtype="bf16", return_scores=True)
+    check_indices_band(idx, ref, extra, 2048, c.seq_lens, 1)
+    dsa.dsa_debug_status()
