@@ -644,26 +644,35 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Decode, one query row per sequence.  The persistent grid walks the same flattened
-// (sequence, 128-key tile) list as li_score_persist, but each wave streams only its own 32-key
-// block of every tile, through a private LDS ring (two 8 KiB slots for bf16 keys, four 4 KiB
-// slots for fp8) filled with direct-to-LDS loads (the
-// block lies in one page, so its address is a scalar base plus a per-lane offset).  Nothing in
-// the main loop waits for another wave: the waves meet only when the sequence changes, to publish
-// the shared row histogram and load the next query.
+// Decode (one query row per sequence) and verify (up to four).  The persistent grid walks the same
+// flattened (sequence, 128-key tile) list as li_score_persist, but each wave streams its own 32-key
+// blocks of every tile through a private LDS ring (two 8 KiB slots for bf16 keys, four 4 KiB slots
+// for fp8) filled with direct-to-LDS loads (a block lies in one page, so its address is a scalar
+// base plus a per-lane offset).  Nothing in the main loop waits for another wave: the waves meet
+// only when the sequence changes, to publish the shared row histograms and load the next queries.
+//   TQ = 1 (decode): 4 waves, wave w scores block w of each tile for the sequence's query row;
+//                    two workgroups per CU.
+//   TQ = 4 (verify): 8 waves, wave w scores query row w % 4 on blocks w / 4 and w / 4 + 2 of each
+//                    tile, so every query row sees every key while the keys cross HBM once per
+//                    workgroup; one workgroup per CU, histogram counters packed two per word.
 constexpr int kDecodeMaxItems = 256;   // tiles per decode workgroup (the grid is sized for it)
 
 // MX: MXFP8 operands (FP8 storage, one E8M0 scale per 32 elements, block-scaled MFMA).
-template <int HI, int DI, bool FP8, bool MX = false>
-__global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
+template <int HI, int DI, bool FP8, bool MX, int TQ>
+__global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score_decode(ScoreArgs a) {
   static_assert(!MX || FP8, "MXFP8 keeps E4M3 codes");
   static_assert(!FP8 || DI % 64 == 0, "E4M3 products run in 64-element MFMA chunks");
-  using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles, 4 waves x 32 keys
+  static_assert(TQ == 1 || TQ == 4, "decode or verify");
+  using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles of four 32-key blocks
   typedef typename AFrag<FP8>::T frag_t;
+  constexpr int NW = TQ == 1 ? 4 : 8;              // waves
+  constexpr int NT = 64 * NW;
+  constexpr int WPQ = NW / TQ;                     // waves per query row
+  constexpr int NBW = 4 / WPQ;                     // blocks per wave and tile
   // E4M3 operands (fp8 and MXFP8) run on the 32x32x64 block-scaled MFMA, fp8 with unit scales
   // (its per-head and per-page scales apply outside the product)
   constexpr int NC = FP8 ? DI / 64 : 1;            // 64-element chunks of the dot product
-  constexpr int BLK = 32 * C::ROWB;                // one wave's block (bytes)
+  constexpr int BLK = 32 * C::ROWB;                // one block (bytes)
   constexpr int NG = DI / 32;                      // MX: scale bytes per key row
   constexpr int SB = 32 * NG;                      // MX: scale bytes per block
   // wave-wide loads per block: the code rows, plus (MX) one for the block's scale bytes
@@ -671,40 +680,56 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   constexpr int KPL = 1024 / C::ROWB;              // keys per load
   static_assert(NLD >= 1 && KPL * C::CPK == 64 && C::KT / kPage == 2, "block shape");
   static_assert(SB % 16 == 0 && SB / 16 <= 64, "scale bytes of a block: one 16-byte load per lane");
-  // ring slots per wave: 64 KiB of ring per workgroup either way (two workgroups per CU)
+  // Decode: a private ring per wave, NSLOT slots of one block (16 KiB per wave either way).
+  // Verify: one ring of RS whole tiles shared by the waves; each wave loads its share of every
+  // tile, and a barrier per tile hands the tile to all of them (the four query rows read the same
+  // keys, which then cross the memory system once per workgroup).
+  constexpr bool SHARED = TQ != 1;
   constexpr int NSLOT = FP8 ? 4 : 2;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[4][NSLOT][BLK];
-  __shared__ uint32_t lds_hist[kBins];
+  constexpr int RS = 4;                            // shared ring: tiles
+  constexpr int LPW = 4 * (BLK / 1024) / NW;       // shared ring: code loads per wave and tile
+  constexpr int NLDT = LPW + (MX ? 1 : 0);         // shared ring: all loads per wave and tile
+  static_assert(!SHARED || (4 * (BLK / 1024)) % NW == 0, "tile loads split evenly over the waves");
+  static_assert(!SHARED || !MX || SB % 32 == 0, "tile scale bytes split over eight waves");
+  constexpr int RING = SHARED ? RS * 4 * BLK : NW * NSLOT * BLK;
+  // histogram words per query row: 32-bit counters (decode), or two 16-bit counters per word
+  // (verify: a workgroup holds at most kDecodeMaxItems * 128 = 32768 keys of a row)
+  constexpr int HW = TQ == 1 ? kBins : kBins / 2;
+  static_assert(kDecodeMaxItems * 128 < 65536, "16-bit counters");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[RING];
+  __shared__ uint32_t lds_hist[TQ][HW];
   // per tile of this workgroup: sequence | tile index << 9, the physical pages of its two halves
-  // (-1 past the sequence end), and the sequence's visible length
+  // (-1 past the sequence end), and the sequence's visible length (of its last query row)
   __shared__ int4 lds_rec[kDecodeMaxItems];
   __shared__ float2 lds_rsc[FP8 && !MX ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
-  __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? 4 : 1][MX ? NSLOT : 1][MX ? SB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? (SHARED ? RS * 4 : NW * NSLOT) : 1][MX ? SB : 16];
   __shared__ int lds_starts[kDecodeMaxItems];      // sequences whose first tile is in this range
   __shared__ int lds_nstarts, lds_ok;
   __shared__ uint32_t sh[8];
-  // the work list lives in the key ring until the first gather (two workgroups fit on a CU)
+  // the work list lives in the key ring until the first gather
   static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
-  int* const lds_tstart = reinterpret_cast<int*>(&lds_k[0][0][0]);
+  static_assert(kDecodeMaxItems <= NT, "one tile record per thread");
+  int* const lds_tstart = reinterpret_cast<int*>(&lds_k[0]);
   int* const lds_len = lds_tstart + kMaxSeqPersist + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 31, hh = lane >> 5;
+  const int qi = wave % TQ, sub = wave / TQ;       // this wave's query row and first block
   const int cap = a.max_seq_len;
   DSA_STAMP(0);
 
   int carry = 0;
-  for (int base = 0; base < a.B; base += kThreads) {
+  for (int base = 0; base < a.B; base += NT) {
     const int b = base + tid;
     int v = 0;
     if (b < a.B) {
-      const int nmax = row_visible(a.seq_lens, b, 1, 0, cap);
+      const int nmax = row_visible(a.seq_lens, b, a.T, a.T - 1, cap);
       lds_len[b] = nmax;
       v = nmax > a.K ? (nmax + C::KT - 1) / C::KT : 0;
     }
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<kThreads>((uint32_t)v, sh, tot);
+    const uint32_t ex = block_exclusive_scan<NT>((uint32_t)v, sh, tot);
     if (b < a.B) lds_tstart[b] = carry + (int)ex;
     carry += (int)tot;
   }
@@ -712,7 +737,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     lds_tstart[a.B] = carry;
     lds_nstarts = 0;
   }
-  for (int i = tid; i < kBins; i += kThreads) lds_hist[i] = 0u;
+  for (int i = tid; i < TQ * HW; i += NT) lds_hist[i / HW][i % HW] = 0u;
   __syncthreads();
   const int total = carry;
   const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
@@ -737,6 +762,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   int asc[FP8 ? C::MB : 1][NC];                  // their group scales (127 = 1 for fp8)
   float wreg[C::MB][16];
   auto load_q = [&](int b) {
+    const size_t row = (size_t)b * a.T + (qi < a.T ? qi : 0);
 #pragma unroll
     for (int m = 0; m < C::MB; ++m) {
       const int head = 32 * m + nl;
@@ -744,9 +770,9 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           if (head < HI) {
-            const unsigned char* src = a.q + ((size_t)b * HI + head) * DI + 64 * c + 16 * hh;
+            const unsigned char* src = a.q + (row * HI + head) * DI + 64 * c + 16 * hh;
             amx[m][c] = mx_join(*reinterpret_cast<const u32x4*>(src), *reinterpret_cast<const u32x4*>(src + 32));
-            asc[m][c] = MX ? (int)a.q_e8[((size_t)b * HI + head) * NG + 2 * c + hh] : 127;
+            asc[m][c] = MX ? (int)a.q_e8[(row * HI + head) * NG + 2 * c + hh] : 127;
           } else {
             amx[m][c] = mx_i32x8{0, 0, 0, 0, 0, 0, 0, 0};
             asc[m][c] = 127;
@@ -756,7 +782,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
 #pragma unroll
         for (int kk = 0; kk < C::KS; ++kk) {
           if (head < HI) {
-            const unsigned char* src = a.q + (((size_t)b * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
+            const unsigned char* src = a.q + ((row * HI + head) * DI + 16 * kk + 8 * hh) * C::ELT;
             afrag[m][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(src));
           } else {
             afrag[m][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -768,30 +794,32 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
         const int hd = 32 * m + 8 * (r >> 2) + 4 * hh + (r & 3);
         float wv = 0.f;
         if (hd < HI) {
-          wv = a.w[(size_t)b * HI + hd];
-          if constexpr (FP8 && !MX) wv *= a.q_scale[(size_t)b * HI + hd];
+          wv = a.w[row * HI + hd];
+          if constexpr (FP8 && !MX) wv *= a.q_scale[row * HI + hd];
         }
         wreg[m][r] = wv;
       }
     }
   };
-  // Adds the LDS histogram into sequence b's row once the workgroup that clears that row (the one
-  // holding its first tile) has published this call's tag.  That workgroup has a lower index, so
-  // with workgroups dispatched in index order the wait always ends.  The wait is still bounded
-  // (a.spin_cap sleeps): past it this workgroup adds nothing, sets the debug flag and marks the row
-  // with this call's tag in its poison words, which li_select answers with a row of -1 (never a
-  // selection from a histogram that may not have been cleared or lacks these counts).
+  // Adds the LDS histograms into sequence b's rows once the workgroup that clears them (the one
+  // holding the sequence's first tile) has published this call's tag in the control words of the
+  // sequence's first row.  That workgroup has a lower index, so with workgroups dispatched in
+  // index order the wait always ends.  The wait is still bounded (a.spin_cap sleeps): past it this
+  // workgroup adds nothing, sets the debug flag and marks the rows with this call's tag in their
+  // poison words, which li_select answers with rows of -1 (never a selection from a histogram that
+  // may not have been cleared or lacks these counts).
   auto flush = [&](int b) {
     if (tid == 0) {
       const unsigned long long* tagp =
-          reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)b * kCtl + kTagWord);
+          reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)b * a.T * kCtl + kTagWord);
       unsigned spins = 0;
       int ok = 1;
       while (__hip_atomic_load(tagp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
         if (++spins > a.spin_cap) {
           flag_input(kFlagSync);
-          __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)b * kCtl + kPoisonWord), a.tag,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int t = 0; t < a.T; ++t)
+            __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + ((size_t)b * a.T + t) * kCtl + kPoisonWord),
+                               a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
         }
@@ -801,18 +829,27 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     }
     __syncthreads();
     const bool ok = lds_ok != 0;
-    for (int i = tid; i < kBins; i += kThreads) {
-      const uint32_t v = lds_hist[i];
-      if (ok && v != 0u) atomicAdd(&a.hist[(size_t)b * kBins + i], v);
-      lds_hist[i] = 0u;
+    for (int i = tid; i < TQ * HW; i += NT) {
+      const int t = i / HW, w = i % HW;
+      const uint32_t v = lds_hist[t][w];
+      if (ok && v != 0u && t < a.T) {
+        uint32_t* row_hist = a.hist + ((size_t)b * a.T + t) * kBins;
+        if constexpr (TQ == 1) {
+          atomicAdd(&row_hist[w], v);
+        } else {
+          if (v & 0xFFFFu) atomicAdd(&row_hist[2 * w], v & 0xFFFFu);
+          if (v >> 16) atomicAdd(&row_hist[2 * w + 1], v >> 16);
+        }
+      }
+      lds_hist[t][w] = 0u;
     }
   };
 
-  // the first sequence's query loads while the tile records are built
+  // the first sequence's queries load while the tile records are built
   float2 my_sc = make_float2(0.f, 0.f);   // fp8: scales of this thread's record (n_items <= threads)
   int b_cur = locate(lo);
   load_q(b_cur);
-  for (int i = tid; i < n_items; i += kThreads) {
+  for (int i = tid; i < n_items; i += NT) {
     const int f = lo + i;
     const int b = locate(f);
     const int j = f - lds_tstart[b];
@@ -829,7 +866,7 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     if constexpr (FP8 && !MX) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
-  // This workgroup clears the histogram and control words of every sequence it starts (no other
+  // This workgroup clears the histograms and control words of every sequence it starts (no other
   // workgroup has flushed into them: they all wait for the tag), then publishes this call's tag
   // for each.  Wave 0 does both: its clears go out before its first key blocks, and the wait for
   // those blocks below (vmcnt 0, which counts stores too) also finishes the clears, so the tag
@@ -840,68 +877,119 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
   const int n_starts = lds_nstarts;
   if (wave == 0) {
     for (int k = 0; k < n_starts; ++k) {
-      const int b = lds_starts[k];
-      for (int i = lane; i < kBins; i += 64)
-        __hip_atomic_store(&a.hist[(size_t)b * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (lane < kTagWord)
-        __hip_atomic_store(&a.ctl[(size_t)b * kCtl + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const size_t r0 = (size_t)lds_starts[k] * a.T;
+      for (int i = lane; i < a.T * kBins; i += 64)
+        __hip_atomic_store(&a.hist[r0 * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = lane; i < a.T * kTagWord; i += 64)
+        __hip_atomic_store(&a.ctl[(r0 + i / kTagWord) * kCtl + i % kTagWord], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   DSA_STAMP(1);
 
-  // Block i of this wave = keys 32*wave .. 32*wave + 31 of tile lo + i (page half wave / 2), into
-  // ring slot i % NSLOT.  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key %
-  // CPK), so the slot holds key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block
-  // past the sequence end reads page 0; its keys are never stored.  The loop issues no other
-  // global load (the fp8 page scales come from the tile records), so the counter waits below see
-  // only these.
-  auto issue = [&](int i, int slot) {
-    const int4 r = lds_rec[i];
-    const int pg = __builtin_amdgcn_readfirstlane(wave < 2 ? r.y : r.z);
+  // Block blk of tile item i holds keys 32 * blk .. 32 * blk + 31 of the tile (page half
+  // blk / 2).  Lane l of load u fetches key KPL*u + l / CPK, chunk (l % CPK) ^ (key % CPK), so a
+  // block holds key rows of ROWB bytes with chunks XOR-swizzled by the key.  A block past the
+  // sequence end reads page 0; its keys are never stored.  The loop issues no other global load
+  // (the fp8 page scales come from the tile records), so the counter waits below see only these.
+  // Decode: block number k of this wave is block sub + WPQ * (k % NBW) of item k / NBW, in its
+  // private ring slot k % NSLOT.  Verify: item i sits in shared ring slot i % RS; this wave loads
+  // loads LPW * wave .. LPW * wave + LPW - 1 of the tile's 4 * BLK / 1024 (and, MXFP8, half a
+  // block's scale bytes).
+  auto block_ptr = [&](int slot, int blk) -> unsigned char* {
+    return SHARED ? &lds_k[(slot * 4 + blk) * BLK] : &lds_k[(wave * NSLOT + slot) * BLK];
+  };
+  auto block_sx = [&](int slot, int blk) -> unsigned char* {
+    return SHARED ? lds_kx[slot * 4 + blk] : lds_kx[wave * NSLOT + slot];
+  };
+  auto load_rows = [&](const int4& r, int blk, int u, unsigned char* dst) {
+    const int pg = __builtin_amdgcn_readfirstlane(blk < 2 ? r.y : r.z);
     const int phys = pg < 0 ? 0 : pg;
-    const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (wave & 1)) * C::ROWB;
+    const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (blk & 1)) * C::ROWB;
+    const int key = KPL * u + lane / C::CPK;
+    const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
+    lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
+  };
+  const int n_blocks = SHARED ? n_items : n_items * NBW;   // ring steps of this wave
+  auto issue = [&](int k) {
+    if constexpr (SHARED) {
+      const int4 r = lds_rec[k];
+      const int slot = k % RS;
 #pragma unroll
-    for (int u = 0; u < BLK / 1024; ++u) {
-      const int key = KPL * u + lane / C::CPK;
-      const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
-      lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), lds_k[wave][slot] + 1024 * u);
-    }
-    if constexpr (MX) {
-      // the block's scale bytes (key-major, NG per key) are contiguous in the scale pool
-      if (lane < SB / 16)
-        lds_dma16(a.k_e8 + ((size_t)phys * kPage + 32 * (wave & 1)) * NG + 16 * lane, lds_kx[wave][slot]);
+      for (int v = 0; v < LPW; ++v) {
+        const int g = LPW * wave + v, blk = g / (BLK / 1024), u = g % (BLK / 1024);
+        load_rows(r, blk, u, block_ptr(slot, blk));
+      }
+      if constexpr (MX) {
+        // wave w: bytes (w % 2) * SB / 2 .. of block w / 2's scales (key-major, NG per key)
+        const int blk = wave / 2;
+        const int pg = __builtin_amdgcn_readfirstlane(blk < 2 ? r.y : r.z);
+        const int phys = pg < 0 ? 0 : pg;
+        if (lane < SB / 32)
+          lds_dma16(a.k_e8 + ((size_t)phys * kPage + 32 * (blk & 1)) * NG + (wave % 2) * (SB / 2) + 16 * lane,
+                    block_sx(slot, blk) + (wave % 2) * (SB / 2));
+      }
+    } else {
+      const int4 r = lds_rec[k / NBW];
+      const int blk = sub + WPQ * (k % NBW);
+      const int slot = k % NSLOT;
+#pragma unroll
+      for (int u = 0; u < BLK / 1024; ++u) load_rows(r, blk, u, block_ptr(slot, 0));
+      if constexpr (MX) {
+        // the block's scale bytes (key-major, NG per key) are contiguous in the scale pool
+        const int pg = __builtin_amdgcn_readfirstlane(blk < 2 ? r.y : r.z);
+        const int phys = pg < 0 ? 0 : pg;
+        if (lane < SB / 16)
+          lds_dma16(a.k_e8 + ((size_t)phys * kPage + 32 * (blk & 1)) * NG + 16 * lane, block_sx(slot, 0));
+      }
     }
   };
+  constexpr int kAhead = SHARED ? RS - 1 : NSLOT;        // ring steps issued before the loop
 #pragma unroll
-  for (int u = 0; u < NSLOT; ++u)
-    if (u < n_items) issue(u, u);
+  for (int u = 0; u < kAhead; ++u)
+    if (u < n_blocks) issue(u);
   // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
   // so no wait for them lands in the main loop (it also covers the first blocks, and wave 0's
   // clears)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   if (wave == 0 && !a.withhold_tag)
     for (int k = lane; k < n_starts; k += 64)
-      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * kCtl + kTagWord),
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * a.T * kCtl + kTagWord),
                          a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (FP8 && !MX) {
-    static_assert(kDecodeMaxItems <= kThreads, "one record per thread");
     if (tid < n_items) lds_rsc[tid] = my_sc;
     lds_barrier();
   }
 
-  for (int i = 0; i < n_items; ++i) {
-    const int slot = i % NSLOT;
-    // this wave's block i has landed; up to NSLOT - 1 later blocks stay in flight
-    const int later = min(NSLOT - 1, n_items - 1 - i);
-    if (later >= 3) wait_vmcnt<3 * NLD>();
-    else if (later == 2) wait_vmcnt<2 * NLD>();
-    else if (later == 1) wait_vmcnt<NLD>();
-    else wait_vmcnt<0>();
+  for (int k = 0; k < n_blocks * (SHARED ? NBW : 1); ++k) {
+    // decode: ring step k is block k; verify: ring step i = k / NBW, its blocks k % NBW
+    const int i = k / NBW, blk = sub + WPQ * (k % NBW);
+    const int slot = SHARED ? i % RS : k % NSLOT;
+    if constexpr (SHARED) {
+      if (k % NBW == 0) {
+        // tile i has landed for this wave (up to RS - 2 later tiles stay in flight), then for all
+        // waves; every wave is past tile i - 1, whose slot takes tile i + RS - 1
+        const int later = min(RS - 2, n_items - 1 - i);
+        if (later >= 2) wait_vmcnt<2 * NLDT>();
+        else if (later == 1) wait_vmcnt<NLDT>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (i + RS - 1 < n_items) issue(i + RS - 1);
+      }
+    } else {
+      // this wave's block k has landed; up to NSLOT - 1 later blocks stay in flight
+      const int later = min(NSLOT - 1, n_blocks - 1 - k);
+      if (later >= 3) wait_vmcnt<3 * NLD>();
+      else if (later == 2) wait_vmcnt<2 * NLD>();
+      else if (later == 1) wait_vmcnt<NLD>();
+      else wait_vmcnt<0>();
+    }
     const int4 rec = lds_rec[i];
     const int b = __builtin_amdgcn_readfirstlane(rec.x & 511);
     const int j = __builtin_amdgcn_readfirstlane(rec.x >> 9);
-    const int n_me = __builtin_amdgcn_readfirstlane(rec.w);
-    if (b != b_cur) {                 // new sequence: publish the histogram, load the query
+    // visible keys of this wave's query row
+    const int n_me = __builtin_amdgcn_readfirstlane(rec.w) - (a.T - 1 - qi);
+    if (b != b_cur) {                 // new sequence: publish the histograms, load the queries
       __syncthreads();
       flush(b_cur);
       load_q(b);
@@ -912,9 +1000,10 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
     float kscale = 1.f;
     if constexpr (FP8 && !MX) {
       const float2 sc = lds_rsc[i];
-      kscale = wave < 2 ? sc.x : sc.y;
+      kscale = blk < 2 ? sc.x : sc.y;
     }
-    const unsigned char* blk = lds_k[wave][slot];
+    const unsigned char* blkp = block_ptr(slot, SHARED ? blk : 0);
+    const unsigned char* blkx = block_sx(slot, SHARED ? blk : 0);
     f32x16 acc[C::MB];
 #pragma unroll
     for (int m = 0; m < C::MB; ++m)
@@ -926,10 +1015,10 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       int bsc[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const unsigned char* row = blk + nl * C::ROWB;
+        const unsigned char* row = blkp + nl * C::ROWB;
         bmx[c] = mx_join(*reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + hh) ^ (nl & (C::CPK - 1)))),
                          *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 + hh) ^ (nl & (C::CPK - 1)))));
-        bsc[c] = MX ? (int)lds_kx[wave][slot][nl * NG + 2 * c + hh] : 127;
+        bsc[c] = MX ? (int)blkx[nl * NG + 2 * c + hh] : 127;
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -939,14 +1028,14 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       bf16x8 bfr[C::KS];
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
-        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blk + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
+        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blkp + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
 #pragma unroll
         for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
     }
-    // the slot's reads are complete (the MFMAs consumed them): refill it
-    if (i + NSLOT < n_items) issue(i + NSLOT, slot);
+    // decode: the slot's reads are complete (the MFMAs consumed them): refill it
+    if (!SHARED && k + NSLOT < n_blocks) issue(k + NSLOT);
     float part = 0.f;
 #pragma unroll
     for (int m = 0; m < C::MB; ++m)
@@ -954,11 +1043,13 @@ __global__ __launch_bounds__(256, 2) void li_score_decode(ScoreArgs a) {
       for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
     part = xor32_sum(part);
     if constexpr (FP8 && !MX) part *= kscale;
-    const int s = j * C::KT + 32 * wave + nl;
-    if (hh == 0 && s < n_me) {
+    const int s = j * C::KT + 32 * blk + nl;
+    // rows with n_me <= K select every visible key without scores (li_select)
+    if (hh == 0 && s < n_me && n_me > a.K && qi < a.T) {
       const uint32_t key = float_key(part);
-      a.keys[(size_t)b * a.row_stride + s] = key;
-      atomicAdd(&lds_hist[key >> 21], 1u);
+      a.keys[((size_t)b * a.T + qi) * a.row_stride + s] = key;
+      if constexpr (TQ == 1) atomicAdd(&lds_hist[0][key >> 21], 1u);
+      else atomicAdd(&lds_hist[qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
     }
   }
   __syncthreads();
@@ -1401,9 +1492,9 @@ template <int HI, int DI, bool FP8>
 static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, bool mx, hipStream_t st) {
   if constexpr (FP8) {
     if (mx) {   // MXFP8: decode, verify or the chunked (prefill) grid
-      if (persist && tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      if (persist && tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true, 1>), dim3(grid), dim3(256), 0, st, s);
       else if (persist && tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
-      else if (persist) hipLaunchKernelGGL((li_score_persist<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (persist) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true, 4>), dim3(grid), dim3(512), 0, st, s);
       else if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, true, 1, true>), dim3(grid), dim3(kThreads), 0, st, s);
       else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
       else hipLaunchKernelGGL((li_score<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
@@ -1411,9 +1502,9 @@ static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, boo
     }
   }
   if (persist) {
-    if (tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, FP8>), dim3(grid), dim3(kThreads), 0, st, s);
+    if (tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, false, 1>), dim3(grid), dim3(256), 0, st, s);
     else if (tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
-    else hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 4>), dim3(grid), dim3(kThreads), 0, st, s);
+    else hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, false, 4>), dim3(grid), dim3(512), 0, st, s);
     return;
   }
   if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, FP8, 1>), dim3(grid), dim3(kThreads), 0, st, s);
@@ -1448,8 +1539,9 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   const size_t hist_words = (size_t)p.rows * (kBins + kCtl);   // histograms + control words
   const bool persist = a.T <= 4 && a.B <= kMaxSeqPersist;
-  // the decode kernel clears each row's histogram itself (tag handshake); the others need it clear
-  const bool self_clear = persist && p.tq == 1;
+  // the decode / verify kernel (one or four query rows per sequence) clears each row's histogram
+  // itself (tag handshake); the others need it clear
+  const bool self_clear = persist && p.tq != 2;
   if (!self_clear) {
     const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
     LaunchScope ls("li_zero_hist", st);
@@ -1484,12 +1576,15 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.max_seq_len = a.max_seq_len;
   int grid = a.B * p.n_qtiles * p.n_chunks;
   if (persist) {
-    const int kt = p.tq == 1 ? 128 : 64;
+    // decode: two 4-wave workgroups per CU; verify (tq 4): one 8-wave workgroup per CU; tq 2
+    // (li_score_persist, 64-key tiles): two per CU
+    const int kt = p.tq == 2 ? 64 : 128;
     const long long max_tiles = (long long)a.B * ((a.max_seq_len + kt - 1) / kt);
-    grid = (int)std::max<long long>(1, std::min<long long>(2LL * device_cus(), (max_tiles + 1) / 2));
+    const long long per_cu = p.tq == 4 ? 1 : 2;
+    grid = (int)std::max<long long>(1, std::min<long long>(per_cu * device_cus(), (max_tiles + 1) / 2));
     // a workgroup's range (at most ceil(max_tiles / grid) tiles) must fit its tile table:
     // kDecodeMaxItems tiles in the decode kernel, kMaxPagesPersist pages in the others
-    if (p.tq == 1) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
+    if (p.tq != 2) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
     else grid = (int)std::max<long long>(grid, (max_tiles * (kt / kPage) + kMaxPagesPersist - 1) / kMaxPagesPersist);
   }
   if (grid > 0) {

@@ -90,7 +90,8 @@ def test_latent_append_clamps_and_reports_bad_length_and_page():
     dsa.dsa_debug_status()
 
 
-def test_decode_tag_wait_timeout_emits_minus_one_rows(monkeypatch):
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_tag_wait_timeout_emits_minus_one_rows(monkeypatch, T):
     """The decode score kernel's bounded wait for a row's histogram clear, forced from the host:
     the clearing workgroups publish no tag and the waits give up after 64 sleeps.  Every kernel
     still exits; rows with n > K come out all -1 (never a selection from an uncleared histogram),
@@ -99,7 +100,8 @@ def test_decode_tag_wait_timeout_emits_minus_one_rows(monkeypatch):
     import numpy as np
     import oracle
     from tests._gpu import check_indices_band, oracle_args, to_np
-    spec = W.custom("tagwait", 3, 1, (1500, 2600, 4100), 64, 128, 2048, 16)
+    # T = 4: the first sequence's rows see 1497..1500 keys (all n <= K), the others more than K
+    spec = W.custom("tagwait", 3, T, (1500, 2600, 4100), 64, 128, 2048, 16)
     c = W.make_case(spec)
     d = Dev(c)
     _clear()
@@ -108,11 +110,13 @@ def test_decode_tag_wait_timeout_emits_minus_one_rows(monkeypatch):
     idx = to_np(d.indexer())
     monkeypatch.delenv("DSA_TEST_WITHHOLD_TAG")
     monkeypatch.delenv("DSA_TEST_SYNC_SPIN_CAP")
-    assert np.array_equal(idx[0, 0], np.r_[np.arange(1500), -np.ones(548)].astype(np.int32))
+    for t in range(T):
+        n = 1500 - T + 1 + t
+        assert np.array_equal(idx[0, t], np.r_[np.arange(n), -np.ones(2048 - n)].astype(np.int32))
     assert (idx[1:] == -1).all()
     with pytest.raises(dsa.DsaError, match="handshake"):
         dsa.dsa_debug_status()
     idx = to_np(d.indexer())
-    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=2048, dtype="bf16", return_scores=True)
-    check_indices_band(idx, ref, extra, 2048, c.seq_lens, 1)
+    ref, extra = oracle.indexer_topk_ref(**oracle_args(c), T=T, K=2048, dtype="bf16", return_scores=True)
+    check_indices_band(idx, ref, extra, 2048, c.seq_lens, T)
     dsa.dsa_debug_status()

@@ -68,7 +68,8 @@ def test_mx_small_verify():
 
 
 # ---------------------------------------------------------------- exact-arithmetic variants
-@pytest.mark.parametrize("T,lens", [(1, (3000, 5000)), (4, (2600, 4500))])
+@pytest.mark.parametrize("T,lens", [(1, (3000, 5000)), (4, (2600, 4500)), (3, (2049, 2051, 3333)),
+                                    (4, (2050, 2051, 9000))])
 def test_wide_grid_exact(T, lens):
     spec = W.custom("grid8_wide", len(lens), T, lens, 64, 128, 2048, 128, values="grid8")
     _run(spec, exact=True)
