@@ -81,12 +81,18 @@ struct SfaArgs {
 //   B: the 64 rope columns, 128 bytes (8 chunks), row r at kRegionB + 128*r.
 // Chunk c of row r sits at slot c ^ swa(r) in A and c ^ swb(r) in B.  A region-A row is exactly
 // one wave-wide direct-to-LDS load (64 lanes x 16 bytes), so a gather is one scalar-addressed load
-// per row.  The XORs keep the reads free of bank conflicts (16-byte slots, 16 per 256-byte bank
-// cycle): the score product's 16 lanes read one chunk of 16 consecutive rows, and swa is a
-// permutation of the row's low four bits; the value product's transposed 8-byte reads take 2
-// chunks (c, c^1) of 4 consecutive rows, and swa >> 1 differs between those rows.
+// per row.  The XORs keep the reads free of bank conflicts whether the LDS serves 128 or 256 bytes
+// per cycle (16-byte slots, 8 or 16 per bank cycle).  The score product's 16-byte reads take one
+// chunk of 8 or 16 consecutive rows per cycle: swa permutes a row's low four bits, and its low
+// three bits alone permute the low three.  The value product's transposed 8-byte reads take
+// chunks 4m + {0, 1} (16 lanes) or 4m + {0..3} (32 lanes) of 4 consecutive rows 4p .. 4p + 3:
+// bits 1-2 and bits 2-3 of swa each take four different values over those rows.  With row bits
+// r0..r3: swa = r2 | r1 << 1 | r0 << 2 | (r0 ^ r1 ^ r3) << 3.
 constexpr int kRegionB = 32768;
-__device__ __forceinline__ int swa(int r) { return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3); }
+__device__ __forceinline__ int swa(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  return r2 | (r1 << 1) | (r0 << 2) | ((r0 ^ r1 ^ r3) << 3);
+}
 __device__ __forceinline__ int swb(int r) { return (r >> 1) & 7; }
 
 
