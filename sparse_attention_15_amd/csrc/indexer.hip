@@ -1207,6 +1207,9 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.x, seg = blockIdx.y;
   const int b = row / a.T, t = row % a.T;
+  // timeline points 3..7 of the row's first segment (the score kernel uses 0..2)
+#define SEL_STAMP(point) do { if (seg == 0) DSA_STAMP(point); } while (0)
+  SEL_STAMP(3);
   // the score kernel of this call is done with the row's histogram-cleared tag: reset it, so a
   // replay of the same launches (same tag) waits for its own clear again
   if (seg == 0 && tid == 0)
@@ -1265,6 +1268,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   if (tid == 0) S.cursor = 0u;
   uint32_t above, C;
   uint32_t prefix = sel_find_bin<kBins>(a.hist + (size_t)row * kBins, (uint32_t)a.K, S, phase, above, C);
+  SEL_STAMP(4);
   uint32_t need = (uint32_t)a.K - above;  // keys still to take from the current prefix range
   const uint32_t G = above;               // keys above the digit-0 range
   int resolved = 1;
@@ -1371,6 +1375,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       }
       lds_barrier();
     }
+    SEL_STAMP(5);
     const int ng = (int)min(G2, (uint32_t)DSA_MAX_TOP_K), nc = (int)C;
     // remaining digits over the candidates (each digit's histogram is used once)
     if (resolved == 1) {
@@ -1394,6 +1399,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       prefix = (prefix << 10) | d;
     }
     const uint32_t theta = prefix;       // the exact threshold key; `need` of its ties are kept
+    SEL_STAMP(6);
     for (int c0 = 0; c0 < n; c0 += kMapBits) {
       const int c1 = min(n, c0 + kMapBits);
       bm_sel[2 * tid] = 0u; bm_sel[2 * tid + 1] = 0u;
@@ -1438,6 +1444,8 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
     }
   }
   for (int j = (int)run_out + tid; j < a.K; j += NT) out[j] = -1;
+  SEL_STAMP(7);
+#undef SEL_STAMP
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -124,6 +124,14 @@ def main():
         lines += _table("li_score_decode", DECODE_POINTS, range(3), r)
         xcd = [f"{r[wi % 8 == x, 2].mean():.1f}" for x in range(8)]
         lines += ["", "Streaming done, mean per XCD 0..7: " + ", ".join(xcd) + " us", ""]
+        rows = spec.B * spec.T
+        sel = ti[:rows]
+        if (sel[:, 3] != 0).all():
+            rs = (sel[:, 3:8].astype(np.int64) - int(t0)) * TICK_US
+            lines += _table("li_select (first segment of each row)",
+                            ["start", "digit-0 bin found (row histogram read)", "candidates collected",
+                             "threshold resolved", "indices written"], range(5), rs)
+            lines += [""]
     ws = np.nonzero(ta[:, 0])[0]
     wc = np.nonzero(ta[:, 4])[0]
     if ws.size:
