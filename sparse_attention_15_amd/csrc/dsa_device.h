@@ -57,6 +57,18 @@ __device__ __forceinline__ void lds_dma16_rows(const void* sbase, uint32_t voff,
                : "memory", "m0");
 }
 
+// Same, with the nontemporal cache policy: for streams read once, so they do not displace other
+// lines from the caches.
+__device__ __forceinline__ void lds_dma16_rows_nt(const void* sbase, uint32_t voff, const void* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
+  const uint64_t sb = reinterpret_cast<uintptr_t>(sbase);
+  const uint64_t sbu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sb >> 32)) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(base), "v"(voff),
+               "s"(sbu)
+               : "memory", "m0");
+}
+
 // Waits until at most N of this wave's global loads (including direct-to-LDS loads) are pending.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -908,7 +908,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (blk & 1)) * C::ROWB;
     const int key = KPL * u + lane / C::CPK;
     const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
-    lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
+    lds_dma16_rows_nt(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
   };
   const int n_blocks = SHARED ? n_items : n_items * NBW;   // ring steps of this wave
   auto issue = [&](int k) {
