@@ -370,12 +370,19 @@ __device__ __forceinline__ SfaRole sfa_role(const SfaArgs& a) {
 // Direct-to-LDS load of 16 bytes per lane through a buffer resource: lane i's 16 bytes from
 // byte offset soff + voff (soff wave-uniform, voff per lane) land at LDS address lds_dst + 16 i.
 // Inline assembly for the reason given at lds_dma16; the resource's size bounds every access.
+// NT: the nontemporal cache policy, for rows no other workgroup of the launch reads.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t rsrc, uint32_t soff, uint32_t voff,
                                               const void* lds_dst) {
   const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_dst));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(base), "v"(voff),
-               "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds" ::"s"(base), "v"(voff),
+                 "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(base), "v"(voff),
+                 "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -404,7 +411,7 @@ __device__ __forceinline__ float prob(float s, float scale, float m) {
 // bf16 latent cache, software-pipelined (see the file comment).  BUF: the cache spans less than
 // 4 GiB, so the row table holds each selected row's 32-bit byte offset and the gathers address it
 // through a buffer resource (a scalar offset per value row, no 64-bit address arithmetic).
-template <int NW, bool BUF>
+template <int NW, bool BUF, bool NTG = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sfa_pipe(SfaArgs a) {
   constexpr int NT = NW * 64;               // one wave per 32-head group
@@ -553,7 +560,7 @@ void sfa_pipe(SfaArgs a) {
       int pr = __builtin_amdgcn_readfirstlane(id);
       pr = pr == -1 ? fill_row : pr;        // -1: not selected (a BUF offset may exceed 2^31)
       if constexpr (BUF)
-        lds_dma16_buf(kv_rsrc, (uint32_t)pr, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)), slot + 1024 * r);
+        lds_dma16_buf<NTG>(kv_rsrc, (uint32_t)pr, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)), slot + 1024 * r);
       else
         lds_dma16_rows(a.kv + (size_t)(uint32_t)pr * kRowBytes, (uint32_t)(16 * lane) ^ (uint32_t)(16 * swa(r)),
                        slot + 1024 * r);
@@ -562,7 +569,7 @@ void sfa_pipe(SfaArgs a) {
       const int r = 8 * k + (lane >> 3);
       const int pr = id == -1 ? fill_row : id;
       if constexpr (BUF)
-        lds_dma16_buf(kv_rsrc, 0u, (uint32_t)pr + 2 * kDimV + 16 * ((lane & 7) ^ swb(r)), slot + kRegionB + 1024 * k);
+        lds_dma16_buf<NTG>(kv_rsrc, 0u, (uint32_t)pr + 2 * kDimV + 16 * ((lane & 7) ^ swb(r)), slot + kRegionB + 1024 * k);
       else
         lds_dma16(a.kv + (size_t)(uint32_t)pr * kRowBytes + 2 * kDimV + 16 * ((lane & 7) ^ swb(r)),
                   slot + kRegionB + 1024 * k);
@@ -1237,6 +1244,9 @@ hipError_t launch_attn(const AttnArgs& a, const AttnPlan& p, hipStream_t st) {
   s.kv_bytes = buf ? (uint32_t)kv_bytes : 0u;
   if (p.groups_per_wg == 4) {
     if (kv8) hipLaunchKernelGGL(sfa_main_kv8<4>, grid, dim3(256), 0, st, s);
+    // one query row per sequence: no row shares its selected latent rows with another, so they
+    // stream past the caches; with several query rows per sequence the rows overlap and stay cached
+    else if (buf && a.T == 1) hipLaunchKernelGGL((sfa_pipe<4, true, true>), grid, dim3(256), 0, st, s);
     else if (buf) hipLaunchKernelGGL((sfa_pipe<4, true>), grid, dim3(256), 0, st, s);
     else hipLaunchKernelGGL((sfa_pipe<4, false>), grid, dim3(256), 0, st, s);
   } else if (p.groups_per_wg == 2) {
