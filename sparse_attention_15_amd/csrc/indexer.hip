@@ -656,9 +656,12 @@ __global__ __launch_bounds__(256, 2) void li_score_persist(ScoreArgs a) {
 //                    tile, so every query row sees every key while the keys cross HBM once per
 //                    workgroup; one workgroup per CU, histogram counters packed two per word.
 constexpr int kDecodeMaxItems = 256;   // tiles per decode workgroup (the grid is sized for it)
+constexpr int kMaxGroupsPersist = 4096; // query groups in a verify / prefill work list
+constexpr int kGroupBits = 13;          // tile records: group | tile index << kGroupBits
+static_assert(kMaxGroupsPersist <= (1 << kGroupBits) && kMaxSeqPersist <= (1 << kGroupBits), "group ids");
 
 // MX: MXFP8 operands (FP8 storage, one E8M0 scale per 32 elements, block-scaled MFMA).
-template <int HI, int DI, bool FP8, bool MX, int TQ>
+template <int HI, int DI, bool FP8, bool MX, int TQ, bool NTK = true>
 __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score_decode(ScoreArgs a) {
   static_assert(!MX || FP8, "MXFP8 keeps E4M3 codes");
   static_assert(!FP8 || DI % 64 == 0, "E4M3 products run in 64-element MFMA chunks");
@@ -696,21 +699,23 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   // (verify: a workgroup holds at most kDecodeMaxItems * 128 = 32768 keys of a row)
   constexpr int HW = TQ == 1 ? kBins : kBins / 2;
   static_assert(kDecodeMaxItems * 128 < 65536, "16-bit counters");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[RING];
+  // the work list lives in the key ring until the first gather
+  constexpr int MAXG = TQ == 1 ? kMaxSeqPersist : kMaxGroupsPersist;   // query groups in the work list
+  constexpr int WLB = ((2 * MAXG + 1) * 4 + 1023) / 1024 * 1024;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds_k[RING > WLB ? RING : WLB];
   __shared__ uint32_t lds_hist[TQ][HW];
-  // per tile of this workgroup: sequence | tile index << 9, the physical pages of its two halves
-  // (-1 past the sequence end), and the sequence's visible length (of its last query row)
+  // per tile of this workgroup: query group | tile index << kGroupBits, the physical pages of its
+  // two halves (-1 past the sequence end), and the visible length of the group's last query row
   __shared__ int4 lds_rec[kDecodeMaxItems];
   __shared__ float2 lds_rsc[FP8 && !MX ? kDecodeMaxItems : 1];   // fp8: the two pages' scales (0 past the end)
   __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? (SHARED ? RS * 4 : NW * NSLOT) : 1][MX ? SB : 16];
-  __shared__ int lds_starts[kDecodeMaxItems];      // sequences whose first tile is in this range
+  __shared__ int lds_starts[kDecodeMaxItems];      // query groups whose first tile is in this range
   __shared__ int lds_nstarts, lds_ok;
   __shared__ uint32_t sh[8];
-  // the work list lives in the key ring until the first gather
-  static_assert(sizeof(lds_k) >= (2 * kMaxSeqPersist + 1) * sizeof(int), "work list in the ring");
+  static_assert(sizeof(lds_k) >= (2 * MAXG + 1) * sizeof(int), "work list in the ring");
   static_assert(kDecodeMaxItems <= NT, "one tile record per thread");
   int* const lds_tstart = reinterpret_cast<int*>(&lds_k[0]);
-  int* const lds_len = lds_tstart + kMaxSeqPersist + 1;
+  int* const lds_len = lds_tstart + MAXG + 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -718,23 +723,32 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   const int qi = wave % TQ, sub = wave / TQ;       // this wave's query row and first block
   const int cap = a.max_seq_len;
   DSA_STAMP(0);
+  // Query group g = rows TQ*k .. TQ*k + TQ - 1 (those below T) of sequence g / GPS, k = g % GPS:
+  // the sequence's one row (decode), its T <= 4 rows (verify), or four consecutive rows of a causal
+  // prefill chunk.  The group's tiles cover the keys its last row sees; each row masks the rest.
+  const int GPS = (a.T + TQ - 1) / TQ;             // query groups per sequence
+  const int NGR = a.B * GPS;                       // query groups (the host keeps it <= MAXG)
+  auto seq_of = [&](int g) { return g / GPS; };
+  auto row0_of = [&](int g) { return (size_t)(g / GPS) * a.T + TQ * (g % GPS); };   // first row
+  auto rows_of = [&](int g) { return min(TQ, a.T - TQ * (g % GPS)); };              // rows < T
+  auto last_t_of = [&](int g) { return TQ * (g % GPS) + rows_of(g) - 1; };
 
   int carry = 0;
-  for (int base = 0; base < a.B; base += NT) {
-    const int b = base + tid;
+  for (int base = 0; base < NGR; base += NT) {
+    const int g = base + tid;
     int v = 0;
-    if (b < a.B) {
-      const int nmax = row_visible(a.seq_lens, b, a.T, a.T - 1, cap);
-      lds_len[b] = nmax;
+    if (g < NGR) {
+      const int nmax = row_visible(a.seq_lens, seq_of(g), a.T, last_t_of(g), cap);
+      lds_len[g] = nmax;
       v = nmax > a.K ? (nmax + C::KT - 1) / C::KT : 0;
     }
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan<NT>((uint32_t)v, sh, tot);
-    if (b < a.B) lds_tstart[b] = carry + (int)ex;
+    if (g < NGR) lds_tstart[g] = carry + (int)ex;
     carry += (int)tot;
   }
   if (tid == 0) {
-    lds_tstart[a.B] = carry;
+    lds_tstart[NGR] = carry;
     lds_nstarts = 0;
   }
   for (int i = tid; i < TQ * HW; i += NT) lds_hist[i / HW][i % HW] = 0u;
@@ -749,7 +763,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   }
 
   auto locate = [&](int f) -> int {
-    int l = 0, h = a.B;
+    int l = 0, h = NGR;
     while (h - l > 1) {
       const int m = (l + h) >> 1;
       if (lds_tstart[m] <= f) l = m; else h = m;
@@ -761,8 +775,8 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   mx_i32x8 amx[FP8 ? C::MB : 1][NC];             // E4M3: q codes of lane (head, h) per chunk
   int asc[FP8 ? C::MB : 1][NC];                  // their group scales (127 = 1 for fp8)
   float wreg[C::MB][16];
-  auto load_q = [&](int b) {
-    const size_t row = (size_t)b * a.T + (qi < a.T ? qi : 0);
+  auto load_q = [&](int g) {
+    const size_t row = row0_of(g) + (qi < rows_of(g) ? qi : 0);
 #pragma unroll
     for (int m = 0; m < C::MB; ++m) {
       const int head = 32 * m + nl;
@@ -801,24 +815,26 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
       }
     }
   };
-  // Adds the LDS histograms into sequence b's rows once the workgroup that clears them (the one
-  // holding the sequence's first tile) has published this call's tag in the control words of the
-  // sequence's first row.  That workgroup has a lower index, so with workgroups dispatched in
+  // Adds the LDS histograms into group g's rows once the workgroup that clears them (the one
+  // holding the group's first tile) has published this call's tag in the control words of the
+  // group's first row.  That workgroup has a lower index, so with workgroups dispatched in
   // index order the wait always ends.  The wait is still bounded (a.spin_cap sleeps): past it this
   // workgroup adds nothing, sets the debug flag and marks the rows with this call's tag in their
   // poison words, which li_select answers with rows of -1 (never a selection from a histogram that
   // may not have been cleared or lacks these counts).
-  auto flush = [&](int b) {
+  auto flush = [&](int g) {
+    const size_t r0 = row0_of(g);
+    const int nrows = rows_of(g);
     if (tid == 0) {
       const unsigned long long* tagp =
-          reinterpret_cast<const unsigned long long*>(a.ctl + (size_t)b * a.T * kCtl + kTagWord);
+          reinterpret_cast<const unsigned long long*>(a.ctl + r0 * kCtl + kTagWord);
       unsigned spins = 0;
       int ok = 1;
       while (__hip_atomic_load(tagp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
         if (++spins > a.spin_cap) {
           flag_input(kFlagSync);
-          for (int t = 0; t < a.T; ++t)
-            __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + ((size_t)b * a.T + t) * kCtl + kPoisonWord),
+          for (int t = 0; t < nrows; ++t)
+            __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (r0 + t) * kCtl + kPoisonWord),
                                a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
@@ -832,8 +848,8 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     for (int i = tid; i < TQ * HW; i += NT) {
       const int t = i / HW, w = i % HW;
       const uint32_t v = lds_hist[t][w];
-      if (ok && v != 0u && t < a.T) {
-        uint32_t* row_hist = a.hist + ((size_t)b * a.T + t) * kBins;
+      if (ok && v != 0u && t < nrows) {
+        uint32_t* row_hist = a.hist + (r0 + t) * kBins;
         if constexpr (TQ == 1) {
           atomicAdd(&row_hist[w], v);
         } else {
@@ -845,28 +861,31 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     }
   };
 
-  // the first sequence's queries load while the tile records are built
+  // the first group's queries load while the tile records are built
   float2 my_sc = make_float2(0.f, 0.f);   // fp8: scales of this thread's record (n_items <= threads)
-  int b_cur = locate(lo);
-  load_q(b_cur);
+  int g_cur = locate(lo);
+  size_t cur_row0 = row0_of(g_cur);          // the current group's first row and row count
+  int cur_rows = rows_of(g_cur);
+  load_q(g_cur);
   for (int i = tid; i < n_items; i += NT) {
     const int f = lo + i;
-    const int b = locate(f);
-    const int j = f - lds_tstart[b];
-    const int n = lds_len[b];
+    const int g = locate(f);
+    const int j = f - lds_tstart[g];
+    const int n = lds_len[g];
+    const int b = seq_of(g);
     int pg[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int lp = 2 * j + h;
       pg[h] = lp * kPage < n ? clamp_page(a.block_table[(size_t)b * a.max_pages + lp], a.num_pages) : -1;
     }
-    lds_rec[i] = make_int4(b | (j << 9), pg[0], pg[1], n);
-    if (j == 0) lds_starts[atomicAdd(&lds_nstarts, 1)] = b;
+    lds_rec[i] = make_int4(g | (j << kGroupBits), pg[0], pg[1], n);
+    if (j == 0) lds_starts[atomicAdd(&lds_nstarts, 1)] = g;
     // fp8 page scales: loaded now, stored to LDS once the first gathers are in flight
     if constexpr (FP8 && !MX) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
-  // This workgroup clears the histograms and control words of every sequence it starts (no other
+  // This workgroup clears the histograms and control words of every group it starts (no other
   // workgroup has flushed into them: they all wait for the tag), then publishes this call's tag
   // for each.  Wave 0 does both: its clears go out before its first key blocks, and the wait for
   // those blocks below (vmcnt 0, which counts stores too) also finishes the clears, so the tag
@@ -877,10 +896,11 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   const int n_starts = lds_nstarts;
   if (wave == 0) {
     for (int k = 0; k < n_starts; ++k) {
-      const size_t r0 = (size_t)lds_starts[k] * a.T;
-      for (int i = lane; i < a.T * kBins; i += 64)
+      const size_t r0 = row0_of(lds_starts[k]);
+      const int nrows = rows_of(lds_starts[k]);
+      for (int i = lane; i < nrows * kBins; i += 64)
         __hip_atomic_store(&a.hist[r0 * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int i = lane; i < a.T * kTagWord; i += 64)
+      for (int i = lane; i < nrows * kTagWord; i += 64)
         __hip_atomic_store(&a.ctl[(r0 + i / kTagWord) * kCtl + i % kTagWord], 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -908,7 +928,8 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     const unsigned char* base = a.kc + ((size_t)phys * kPage + 32 * (blk & 1)) * C::ROWB;
     const int key = KPL * u + lane / C::CPK;
     const int c = (lane % C::CPK) ^ (key & (C::CPK - 1));
-    lds_dma16_rows_nt(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
+    if constexpr (NTK) lds_dma16_rows_nt(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
+    else lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
   };
   const int n_blocks = SHARED ? n_items : n_items * NBW;   // ring steps of this wave
   auto issue = [&](int k) {
@@ -954,7 +975,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   __builtin_amdgcn_s_waitcnt(0x0F70);
   if (wave == 0 && !a.withhold_tag)
     for (int k = lane; k < n_starts; k += 64)
-      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + (size_t)lds_starts[k] * a.T * kCtl + kTagWord),
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + row0_of(lds_starts[k]) * kCtl + kTagWord),
                          a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if constexpr (FP8 && !MX) {
     if (tid < n_items) lds_rsc[tid] = my_sc;
@@ -985,18 +1006,21 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
       else wait_vmcnt<0>();
     }
     const int4 rec = lds_rec[i];
-    const int b = __builtin_amdgcn_readfirstlane(rec.x & 511);
-    const int j = __builtin_amdgcn_readfirstlane(rec.x >> 9);
-    // visible keys of this wave's query row
-    const int n_me = __builtin_amdgcn_readfirstlane(rec.w) - (a.T - 1 - qi);
-    if (b != b_cur) {                 // new sequence: publish the histograms, load the queries
+    const int g = __builtin_amdgcn_readfirstlane(rec.x & ((1 << kGroupBits) - 1));
+    const int j = __builtin_amdgcn_readfirstlane(rec.x >> kGroupBits);
+    if (g != g_cur) {                 // new group: publish the histograms, load the queries
       __syncthreads();
-      flush(b_cur);
-      load_q(b);
+      flush(g_cur);
+      load_q(g);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
-      b_cur = b;
+      g_cur = g;
+      cur_row0 = row0_of(g);
+      cur_rows = rows_of(g);
     }
+    // this wave's query row (valid below T) and its visible keys (rec.w is the group's last row's)
+    const bool row_ok = qi < cur_rows;
+    const int n_me = __builtin_amdgcn_readfirstlane(rec.w) - (cur_rows - 1 - qi);
     float kscale = 1.f;
     if constexpr (FP8 && !MX) {
       const float2 sc = lds_rsc[i];
@@ -1045,15 +1069,15 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     if constexpr (FP8 && !MX) part *= kscale;
     const int s = j * C::KT + 32 * blk + nl;
     // rows with n_me <= K select every visible key without scores (li_select)
-    if (hh == 0 && s < n_me && n_me > a.K && qi < a.T) {
+    if (hh == 0 && s < n_me && n_me > a.K && row_ok) {
       const uint32_t key = float_key(part);
-      a.keys[((size_t)b * a.T + qi) * a.row_stride + s] = key;
+      a.keys[(cur_row0 + qi) * a.row_stride + s] = key;
       if constexpr (TQ == 1) atomicAdd(&lds_hist[0][key >> 21], 1u);
       else atomicAdd(&lds_hist[qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
     }
   }
   __syncthreads();
-  flush(b_cur);
+  flush(g_cur);
   DSA_STAMP(2);
 }
 
@@ -1496,34 +1520,32 @@ bool indexer_supported(int heads, int dim) {
   return (heads == 8 || heads == 16 || heads == 32 || heads == 64) && (dim == 64 || dim == 128);
 }
 
-template <int HI, int DI, bool FP8>
-static void launch_score(const ScoreArgs& s, int tq, int grid, bool persist, bool mx, hipStream_t st) {
-  if constexpr (FP8) {
-    if (mx) {   // MXFP8: decode, verify or the chunked (prefill) grid
-      if (persist && tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true, 1>), dim3(grid), dim3(256), 0, st, s);
-      else if (persist && tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
-      else if (persist) hipLaunchKernelGGL((li_score_decode<HI, DI, true, true, 4>), dim3(grid), dim3(512), 0, st, s);
-      else if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, true, 1, true>), dim3(grid), dim3(kThreads), 0, st, s);
-      else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, true, 2, true>), dim3(grid), dim3(kThreads), 0, st, s);
-      else hipLaunchKernelGGL((li_score<HI, DI, true, 4, true>), dim3(grid), dim3(kThreads), 0, st, s);
+// Score kernel per call: the decode kernel (T = 1), the grouped kernel (query groups of up to four
+// rows: verify, with the keys streamed past the caches, and causal prefill chunks, whose query
+// groups reread the same keys and keep them cached), the two-row persistent kernel (T = 2), or the
+// chunked grid when the work list would not fit a workgroup's LDS.
+enum class ScoreMode { kChunked, kDecode, kVerify, kPrefill, kPersist2 };
+
+template <int HI, int DI, bool FP8, bool MX>
+static void launch_score_mode(const ScoreArgs& s, ScoreMode mode, int tq, int grid, hipStream_t st) {
+  switch (mode) {
+    case ScoreMode::kDecode: hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, MX, 1>), dim3(grid), dim3(256), 0, st, s); return;
+    case ScoreMode::kVerify: hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, MX, 4, true>), dim3(grid), dim3(512), 0, st, s); return;
+    case ScoreMode::kPrefill: hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, MX, 4, false>), dim3(grid), dim3(512), 0, st, s); return;
+    case ScoreMode::kPersist2: hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2, MX>), dim3(grid), dim3(kThreads), 0, st, s); return;
+    case ScoreMode::kChunked:
+      if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, FP8, 1, MX>), dim3(grid), dim3(kThreads), 0, st, s);
+      else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, FP8, 2, MX>), dim3(grid), dim3(kThreads), 0, st, s);
+      else hipLaunchKernelGGL((li_score<HI, DI, FP8, 4, MX>), dim3(grid), dim3(kThreads), 0, st, s);
       return;
-    }
   }
-  if (persist) {
-    if (tq == 1) hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, false, 1>), dim3(grid), dim3(256), 0, st, s);
-    else if (tq == 2) hipLaunchKernelGGL((li_score_persist<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
-    else hipLaunchKernelGGL((li_score_decode<HI, DI, FP8, false, 4>), dim3(grid), dim3(512), 0, st, s);
-    return;
-  }
-  if (tq == 1) hipLaunchKernelGGL((li_score<HI, DI, FP8, 1>), dim3(grid), dim3(kThreads), 0, st, s);
-  else if (tq == 2) hipLaunchKernelGGL((li_score<HI, DI, FP8, 2>), dim3(grid), dim3(kThreads), 0, st, s);
-  else hipLaunchKernelGGL((li_score<HI, DI, FP8, 4>), dim3(grid), dim3(kThreads), 0, st, s);
 }
 
 template <int HI, int DI>
-static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, int tq, int grid, bool persist, hipStream_t st) {
-  if (fp8 || mx) launch_score<HI, DI, true>(s, tq, grid, persist, mx, st);
-  else launch_score<HI, DI, false>(s, tq, grid, persist, false, st);
+static void launch_score_dt(const ScoreArgs& s, bool fp8, bool mx, ScoreMode mode, int tq, int grid, hipStream_t st) {
+  if (mx) launch_score_mode<HI, DI, true, true>(s, mode, tq, grid, st);
+  else if (fp8) launch_score_mode<HI, DI, true, false>(s, mode, tq, grid, st);
+  else launch_score_mode<HI, DI, false, false>(s, mode, tq, grid, st);
 }
 
 // MXFP8 runs on every score path (decode, verify, chunked prefill).
@@ -1546,10 +1568,14 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
   const size_t hist_words = (size_t)p.rows * (kBins + kCtl);   // histograms + control words
-  const bool persist = a.T <= 4 && a.B <= kMaxSeqPersist;
-  // the decode / verify kernel (one or four query rows per sequence) clears each row's histogram
-  // itself (tag handshake); the others need it clear
-  const bool self_clear = persist && p.tq != 2;
+  const long long groups4 = (long long)a.B * ((a.T + 3) / 4);
+  const ScoreMode mode = a.T == 1 ? (a.B <= kMaxSeqPersist ? ScoreMode::kDecode : ScoreMode::kChunked)
+                       : a.T == 2 ? (a.B <= kMaxSeqPersist ? ScoreMode::kPersist2 : ScoreMode::kChunked)
+                       : groups4 <= kMaxGroupsPersist ? (a.T <= 4 ? ScoreMode::kVerify : ScoreMode::kPrefill)
+                       : ScoreMode::kChunked;
+  // the decode and grouped kernels clear their rows' histograms themselves (tag handshake); the
+  // others need them clear
+  const bool self_clear = mode == ScoreMode::kDecode || mode == ScoreMode::kVerify || mode == ScoreMode::kPrefill;
   if (!self_clear) {
     const int zgrid = (int)std::min<size_t>((hist_words / 4 + 255) / 256, 2048);
     LaunchScope ls("li_zero_hist", st);
@@ -1583,29 +1609,31 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   s.n_chunks = p.n_chunks; s.n_qtiles = p.n_qtiles; s.row_stride = p.row_stride;
   s.max_seq_len = a.max_seq_len;
   int grid = a.B * p.n_qtiles * p.n_chunks;
-  if (persist) {
-    // decode: two 4-wave workgroups per CU; verify (tq 4): one 8-wave workgroup per CU; tq 2
-    // (li_score_persist, 64-key tiles): two per CU
-    const int kt = p.tq == 2 ? 64 : 128;
-    const long long max_tiles = (long long)a.B * ((a.max_seq_len + kt - 1) / kt);
-    const long long per_cu = p.tq == 4 ? 1 : 2;
+  if (mode != ScoreMode::kChunked) {
+    // decode: two 4-wave workgroups per CU over (sequence, 128-key tile); grouped: one 8-wave
+    // workgroup per CU over (query group, 128-key tile); two rows: two per CU over 64-key tiles
+    const bool two = mode == ScoreMode::kPersist2;
+    const int kt = two ? 64 : 128;
+    const long long units = mode == ScoreMode::kDecode || two ? a.B : groups4;
+    const long long max_tiles = units * ((a.max_seq_len + kt - 1) / kt);
+    const long long per_cu = mode == ScoreMode::kDecode || two ? 2 : 1;
     grid = (int)std::max<long long>(1, std::min<long long>(per_cu * device_cus(), (max_tiles + 1) / 2));
     // a workgroup's range (at most ceil(max_tiles / grid) tiles) must fit its tile table:
-    // kDecodeMaxItems tiles in the decode kernel, kMaxPagesPersist pages in the others
-    if (p.tq != 2) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
+    // kDecodeMaxItems tiles in the decode and grouped kernels, kMaxPagesPersist pages in the other
+    if (!two) grid = (int)std::max<long long>(grid, (max_tiles + kDecodeMaxItems - 1) / kDecodeMaxItems);
     else grid = (int)std::max<long long>(grid, (max_tiles * (kt / kPage) + kMaxPagesPersist - 1) / kMaxPagesPersist);
   }
   if (grid > 0) {
     LaunchScope ls("li_score", st);
     switch (a.heads * 1000 + a.dim) {
-      case 8064: launch_score_dt<8, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 8128: launch_score_dt<8, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 16064: launch_score_dt<16, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 16128: launch_score_dt<16, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 32064: launch_score_dt<32, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 32128: launch_score_dt<32, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 64064: launch_score_dt<64, 64>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
-      case 64128: launch_score_dt<64, 128>(s, a.fp8, a.mx, p.tq, grid, persist, st); break;
+      case 8064: launch_score_dt<8, 64>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 8128: launch_score_dt<8, 128>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 16064: launch_score_dt<16, 64>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 16128: launch_score_dt<16, 128>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 32064: launch_score_dt<32, 64>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 32128: launch_score_dt<32, 128>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 64064: launch_score_dt<64, 64>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
+      case 64128: launch_score_dt<64, 128>(s, a.fp8, a.mx, mode, p.tq, grid, st); break;
       default: return hipErrorInvalidValue;
     }
   }
