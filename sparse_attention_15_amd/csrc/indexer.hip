@@ -931,7 +931,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     if constexpr (NTK) lds_dma16_rows_nt(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
     else lds_dma16_rows(base, (uint32_t)(key * C::ROWB + 16 * c), dst + 1024 * u);
   };
-  const int n_blocks = SHARED ? n_items : n_items * NBW;   // ring steps of this wave
+  const int n_blocks = n_items;                            // ring steps (decode: NBW = 1)
   auto issue = [&](int k) {
     if constexpr (SHARED) {
       const int4 r = lds_rec[k];
@@ -982,21 +982,22 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     lds_barrier();
   }
 
-  for (int k = 0; k < n_blocks * (SHARED ? NBW : 1); ++k) {
-    // decode: ring step k is block k; verify: ring step i = k / NBW, its blocks k % NBW
-    const int i = k / NBW, blk = sub + WPQ * (k % NBW);
+  // A ring step is one block of this wave (decode) or one shared tile (verify, prefill), whose
+  // NB blocks of this wave are scored together: their MFMA chains interleave, and one block's
+  // reduction overlaps the other's products.
+  constexpr int NB = SHARED ? NBW : 1;
+  for (int k = 0; k < n_blocks; ++k) {
+    const int i = k;                                  // tile record (decode: NBW = 1)
     const int slot = SHARED ? i % RS : k % NSLOT;
     if constexpr (SHARED) {
-      if (k % NBW == 0) {
-        // tile i has landed for this wave (up to RS - 2 later tiles stay in flight), then for all
-        // waves; every wave is past tile i - 1, whose slot takes tile i + RS - 1
-        const int later = min(RS - 2, n_items - 1 - i);
-        if (later >= 2) wait_vmcnt<2 * NLDT>();
-        else if (later == 1) wait_vmcnt<NLDT>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (i + RS - 1 < n_items) issue(i + RS - 1);
-      }
+      // tile i has landed for this wave (up to RS - 2 later tiles stay in flight), then for all
+      // waves; every wave is past tile i - 1, whose slot takes tile i + RS - 1
+      const int later = min(RS - 2, n_items - 1 - i);
+      if (later >= 2) wait_vmcnt<2 * NLDT>();
+      else if (later == 1) wait_vmcnt<NLDT>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (i + RS - 1 < n_items) issue(i + RS - 1);
     } else {
       // this wave's block k has landed; up to NSLOT - 1 later blocks stay in flight
       const int later = min(NSLOT - 1, n_blocks - 1 - k);
@@ -1021,59 +1022,74 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     // this wave's query row (valid below T) and its visible keys (rec.w is the group's last row's)
     const bool row_ok = qi < cur_rows;
     const int n_me = __builtin_amdgcn_readfirstlane(rec.w) - (cur_rows - 1 - qi);
-    float kscale = 1.f;
-    if constexpr (FP8 && !MX) {
-      const float2 sc = lds_rsc[i];
-      kscale = blk < 2 ? sc.x : sc.y;
-    }
-    const unsigned char* blkp = block_ptr(slot, SHARED ? blk : 0);
-    const unsigned char* blkx = block_sx(slot, SHARED ? blk : 0);
-    f32x16 acc[C::MB];
+    f32x16 acc[NB][C::MB];
 #pragma unroll
-    for (int m = 0; m < C::MB; ++m)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[m][r] = 0.f;
+      for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[nb][m][r] = 0.f;
     if constexpr (FP8) {
       // key nl: chunks 4c + h and 4c + 2 + h of its row (16 bytes each, XOR-swizzled by the key)
-      mx_i32x8 bmx[NC];
-      int bsc[NC];
+      mx_i32x8 bmx[NB][NC];
+      int bsc[NB][NC];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const unsigned char* row = blkp + nl * C::ROWB;
-        bmx[c] = mx_join(*reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + hh) ^ (nl & (C::CPK - 1)))),
-                         *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 + hh) ^ (nl & (C::CPK - 1)))));
-        bsc[c] = MX ? (int)blkx[nl * NG + 2 * c + hh] : 127;
+      for (int nb = 0; nb < NB; ++nb) {
+        const int blk = sub + WPQ * nb;
+        const unsigned char* row = block_ptr(slot, SHARED ? blk : 0) + nl * C::ROWB;
+        const unsigned char* blkx = block_sx(slot, SHARED ? blk : 0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          bmx[nb][c] = mx_join(*reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + hh) ^ (nl & (C::CPK - 1)))),
+                               *reinterpret_cast<const u32x4*>(row + 16 * ((4 * c + 2 + hh) ^ (nl & (C::CPK - 1)))));
+          bsc[nb][c] = MX ? (int)blkx[nl * NG + 2 * c + hh] : 127;
+        }
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int m = 0; m < C::MB; ++m) acc[m] = mfma_mx(amx[m][c], bmx[c], acc[m], asc[m][c], bsc[c]);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int m = 0; m < C::MB; ++m) acc[nb][m] = mfma_mx(amx[m][c], bmx[nb][c], acc[nb][m], asc[m][c], bsc[nb][c]);
     } else {
-      bf16x8 bfr[C::KS];
+      bf16x8 bfr[NB][C::KS];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const unsigned char* row = block_ptr(slot, SHARED ? sub + WPQ * nb : 0) + nl * C::ROWB;
+#pragma unroll
+        for (int kk = 0; kk < C::KS; ++kk)
+          bfr[nb][kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
+      }
 #pragma unroll
       for (int kk = 0; kk < C::KS; ++kk)
-        bfr[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(blkp + nl * C::ROWB + 16 * ((2 * kk + hh) ^ (nl & (C::CPK - 1)))));
 #pragma unroll
-      for (int kk = 0; kk < C::KS; ++kk)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int m = 0; m < C::MB; ++m) acc[m] = mfma_bf16(afrag[m][kk], bfr[kk], acc[m]);
+          for (int m = 0; m < C::MB; ++m) acc[nb][m] = mfma_bf16(afrag[m][kk], bfr[nb][kk], acc[nb][m]);
     }
     // decode: the slot's reads are complete (the MFMAs consumed them): refill it
     if (!SHARED && k + NSLOT < n_blocks) issue(k + NSLOT);
-    float part = 0.f;
 #pragma unroll
-    for (int m = 0; m < C::MB; ++m)
+    for (int nb = 0; nb < NB; ++nb) {
+      const int blk = sub + WPQ * nb;
+      float part = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[m][r]), part);
-    part = xor32_sum(part);
-    if constexpr (FP8 && !MX) part *= kscale;
-    const int s = j * C::KT + 32 * blk + nl;
-    // rows with n_me <= K select every visible key without scores (li_select)
-    if (hh == 0 && s < n_me && n_me > a.K && row_ok) {
-      const uint32_t key = float_key(part);
-      a.keys[(cur_row0 + qi) * a.row_stride + s] = key;
-      if constexpr (TQ == 1) atomicAdd(&lds_hist[0][key >> 21], 1u);
-      else atomicAdd(&lds_hist[qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
+      for (int m = 0; m < C::MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) part = fmaf(wreg[m][r], relu(acc[nb][m][r]), part);
+      part = xor32_sum(part);
+      if constexpr (FP8 && !MX) {
+        const float2 sc = lds_rsc[i];
+        part *= blk < 2 ? sc.x : sc.y;
+      }
+      const int s = j * C::KT + 32 * blk + nl;
+      // rows with n_me <= K select every visible key without scores (li_select)
+      if (hh == 0 && s < n_me && n_me > a.K && row_ok) {
+        const uint32_t key = float_key(part);
+        a.keys[(cur_row0 + qi) * a.row_stride + s] = key;
+        if constexpr (TQ == 1) atomicAdd(&lds_hist[0][key >> 21], 1u);
+        else atomicAdd(&lds_hist[qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
+      }
     }
   }
   __syncthreads();
