@@ -666,6 +666,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   static_assert(!MX || FP8, "MXFP8 keeps E4M3 codes");
   static_assert(!FP8 || DI % 64 == 0, "E4M3 products run in 64-element MFMA chunks");
   static_assert(TQ == 1 || TQ == 4, "decode or verify");
+  static_assert(HI % 4 == 0, "weights load four heads at a time");
   using C = PCfg<HI, DI, FP8, 1>;                  // 128-key tiles of four 32-key blocks
   typedef typename AFrag<FP8>::T frag_t;
   constexpr int NW = TQ == 1 ? 4 : 8;              // waves
@@ -803,15 +804,27 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
           }
         }
       }
+      // weights of heads 32m + 8j + 4hh .. + 3 (register r = 4j + i): one 16-byte load per j
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int hd = 32 * m + 8 * (r >> 2) + 4 * hh + (r & 3);
-        float wv = 0.f;
-        if (hd < HI) {
-          wv = a.w[row * HI + hd];
-          if constexpr (FP8 && !MX) wv *= a.q_scale[row * HI + hd];
+      for (int j = 0; j < 4; ++j) {
+        const int hd0 = 32 * m + 8 * j + 4 * hh;
+        float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hd0 + 4 <= HI) {
+          wv = *reinterpret_cast<const float4*>(a.w + row * HI + hd0);
+          if constexpr (FP8 && !MX) {
+            const float4 qs = *reinterpret_cast<const float4*>(a.q_scale + row * HI + hd0);
+            wv.x *= qs.x; wv.y *= qs.y; wv.z *= qs.z; wv.w *= qs.w;
+          }
+        } else {
+          float* wp = &wv.x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (hd0 + i < HI) wp[i] = FP8 && !MX ? a.w[row * HI + hd0 + i] * a.q_scale[row * HI + hd0 + i] : a.w[row * HI + hd0 + i];
         }
-        wreg[m][r] = wv;
+        wreg[m][4 * j] = wv.x;
+        wreg[m][4 * j + 1] = wv.y;
+        wreg[m][4 * j + 2] = wv.z;
+        wreg[m][4 * j + 3] = wv.w;
       }
     }
   };
@@ -861,12 +874,12 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     }
   };
 
-  // the first group's queries load while the tile records are built
+  // The first group's queries load after the first key blocks are requested: the block-table loads
+  // of the tile records, and then those blocks, are the longer dependent chain.
   float2 my_sc = make_float2(0.f, 0.f);   // fp8: scales of this thread's record (n_items <= threads)
   int g_cur = locate(lo);
   size_t cur_row0 = row0_of(g_cur);          // the current group's first row and row count
   int cur_rows = rows_of(g_cur);
-  load_q(g_cur);
   for (int i = tid; i < n_items; i += NT) {
     const int f = lo + i;
     const int g = locate(f);
@@ -969,6 +982,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
 #pragma unroll
   for (int u = 0; u < kAhead; ++u)
     if (u < n_blocks) issue(u);
+  load_q(g_cur);
   // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
   // so no wait for them lands in the main loop (it also covers the first blocks, and wave 0's
   // clears)
