@@ -696,15 +696,19 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   static_assert(!SHARED || (4 * (BLK / 1024)) % NW == 0, "tile loads split evenly over the waves");
   static_assert(!SHARED || !MX || SB % 32 == 0, "tile scale bytes split over eight waves");
   constexpr int RING = SHARED ? RS * 4 * BLK : NW * NSLOT * BLK;
-  // histogram words per query row: 32-bit counters (decode), or two 16-bit counters per word
-  // (verify: a workgroup holds at most kDecodeMaxItems * 128 = 32768 keys of a row)
-  constexpr int HW = TQ == 1 ? kBins : kBins / 2;
+  // histogram words per query row: two 16-bit counters per word (a workgroup holds at most
+  // kDecodeMaxItems * 128 = 32768 keys of a row).  Decode keeps two histograms: at a sequence
+  // change the finished sequence's counts stay in LDS and go out at the end, so no device atomics
+  // are in flight when the wave next waits for its loads (their acknowledgements are slow while
+  // the key streams load the memory system, and the counter waits are in order).
+  constexpr int HW = kBins / 2;
+  constexpr int HB = TQ == 1 ? 2 : 1;
   static_assert(kDecodeMaxItems * 128 < 65536, "16-bit counters");
   // the work list lives in the key ring until the first gather
   constexpr int MAXG = TQ == 1 ? kMaxSeqPersist : kMaxGroupsPersist;   // query groups in the work list
   constexpr int WLB = ((2 * MAXG + 1) * 4 + 1023) / 1024 * 1024;
   __shared__ __attribute__((aligned(1024))) unsigned char lds_k[RING > WLB ? RING : WLB];
-  __shared__ uint32_t lds_hist[TQ][HW];
+  __shared__ uint32_t lds_hist[HB][TQ][HW];
   // per tile of this workgroup: query group | tile index << kGroupBits, the physical pages of its
   // two halves (-1 past the sequence end), and the visible length of the group's last query row
   __shared__ int4 lds_rec[kDecodeMaxItems];
@@ -712,6 +716,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   __shared__ __attribute__((aligned(16))) unsigned char lds_kx[MX ? (SHARED ? RS * 4 : NW * NSLOT) : 1][MX ? SB : 16];
   __shared__ int lds_starts[kDecodeMaxItems];      // query groups whose first tile is in this range
   __shared__ int lds_nstarts, lds_ok;
+  __shared__ int lds_dirty[2];              // started groups whose rows need a clear
   __shared__ uint32_t sh[8];
   static_assert(sizeof(lds_k) >= (2 * MAXG + 1) * sizeof(int), "work list in the ring");
   static_assert(kDecodeMaxItems <= NT, "one tile record per thread");
@@ -752,7 +757,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     lds_tstart[NGR] = carry;
     lds_nstarts = 0;
   }
-  for (int i = tid; i < TQ * HW; i += NT) lds_hist[i / HW][i % HW] = 0u;
+  for (int i = tid; i < HB * TQ * HW; i += NT) (&lds_hist[0][0][0])[i] = 0u;
   __syncthreads();
   const int total = carry;
   const int lo = (int)((long long)blockIdx.x * total / gridDim.x);
@@ -835,7 +840,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   // workgroup adds nothing, sets the debug flag and marks the rows with this call's tag in their
   // poison words, which li_select answers with rows of -1 (never a selection from a histogram that
   // may not have been cleared or lacks these counts).
-  auto flush = [&](int g) {
+  auto flush = [&](int g, int hb) {
     const size_t r0 = row0_of(g);
     const int nrows = rows_of(g);
     if (tid == 0) {
@@ -860,17 +865,13 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     const bool ok = lds_ok != 0;
     for (int i = tid; i < TQ * HW; i += NT) {
       const int t = i / HW, w = i % HW;
-      const uint32_t v = lds_hist[t][w];
+      const uint32_t v = lds_hist[hb][t][w];
       if (ok && v != 0u && t < nrows) {
         uint32_t* row_hist = a.hist + (r0 + t) * kBins;
-        if constexpr (TQ == 1) {
-          atomicAdd(&row_hist[w], v);
-        } else {
-          if (v & 0xFFFFu) atomicAdd(&row_hist[2 * w], v & 0xFFFFu);
-          if (v >> 16) atomicAdd(&row_hist[2 * w + 1], v >> 16);
-        }
+        if (v & 0xFFFFu) atomicAdd(&row_hist[2 * w], v & 0xFFFFu);
+        if (v >> 16) atomicAdd(&row_hist[2 * w + 1], v >> 16);
       }
-      lds_hist[t][w] = 0u;
+      lds_hist[hb][t][w] = 0u;
     }
   };
 
@@ -880,6 +881,8 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   int g_cur = locate(lo);
   size_t cur_row0 = row0_of(g_cur);          // the current group's first row and row count
   int cur_rows = rows_of(g_cur);
+  int hb = 0;                                // histogram the current group counts into
+  int pend = -1;                             // decode: group parked in the other histogram
   for (int i = tid; i < n_items; i += NT) {
     const int f = lo + i;
     const int g = locate(f);
@@ -898,24 +901,42 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     if constexpr (FP8 && !MX) my_sc = make_float2(pg[0] < 0 ? 0.f : a.k_scale[pg[0]], pg[1] < 0 ? 0.f : a.k_scale[pg[1]]);
   }
   __syncthreads();
-  // This workgroup clears the histograms and control words of every group it starts (no other
-  // workgroup has flushed into them: they all wait for the tag), then publishes this call's tag
-  // for each.  Wave 0 does both: its clears go out before its first key blocks, and the wait for
-  // those blocks below (vmcnt 0, which counts stores too) also finishes the clears, so the tag
-  // follows without a wait of its own.  The zeros and the tag travel through device-coherent
-  // (agent-scope) stores, which go past the per-XCD L2s, and the histogram adds are
-  // device-coherent atomics, so finished stores are visible to every workgroup; a release/acquire
-  // fence pair would write back and invalidate whole L2s in every workgroup.
+  // This workgroup makes sure the histograms and control words of every group it starts are clear
+  // (no other workgroup has flushed into them: they all wait for the tag), then publishes this
+  // call's tag for each.  The select of the previous call leaves the rows it read clear, so the
+  // rows are first read (every wave its share, up to kCheckStarts groups) and cleared only if any
+  // word is not zero: the first call on a workspace, or one after a call that left them dirty.
+  // The reads go out before the first key blocks and the wait for those blocks below covers them.
+  // A clear (wave 0) goes through device-coherent (agent-scope) stores, which go past the per-XCD
+  // L2s, as the histogram adds are device-coherent atomics, so finished stores are visible to every
+  // workgroup; wave 0 waits for them (vmcnt 0) before the tag, which only a dirty row costs: the
+  // acknowledgements of such stores take microseconds while the key streams load the memory
+  // system.  A release/acquire fence pair would write back and invalidate whole L2s instead.
   const int n_starts = lds_nstarts;
-  if (wave == 0) {
-    for (int k = 0; k < n_starts; ++k) {
-      const size_t r0 = row0_of(lds_starts[k]);
-      const int nrows = rows_of(lds_starts[k]);
-      for (int i = lane; i < nrows * kBins; i += 64)
-        __hip_atomic_store(&a.hist[r0 * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int i = lane; i < nrows * kTagWord; i += 64)
-        __hip_atomic_store(&a.ctl[(r0 + i / kTagWord) * kCtl + i % kTagWord], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  constexpr int kCheckStarts = 2;
+  constexpr int kChkWords = TQ * kBins / NT;               // histogram words per thread and group
+  static_assert(kChkWords % 4 == 0 && kChkWords >= 4, "16-byte check loads");
+  const bool check = n_starts <= kCheckStarts;
+  u32x4 chk[kCheckStarts][kChkWords / 4 + 1];
+  if (check) {
+#pragma unroll
+    for (int k = 0; k < kCheckStarts; ++k) {
+      if (k < n_starts) {
+        const size_t r0 = row0_of(lds_starts[k]);
+        const int nrows = rows_of(lds_starts[k]);
+#pragma unroll
+        for (int v = 0; v < kChkWords / 4; ++v) {
+          const int w0 = 4 * (tid + NT * v);               // word of the group's rows
+          chk[k][v] = w0 < nrows * kBins ? *reinterpret_cast<const u32x4*>(a.hist + r0 * kBins + w0)
+                                         : u32x4{0u, 0u, 0u, 0u};
+        }
+        // control words 0..3 (the select's counters) of row tid
+        chk[k][kChkWords / 4] = tid < nrows ? *reinterpret_cast<const u32x4*>(a.ctl + (r0 + tid) * kCtl)
+                                            : u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int v = 0; v <= kChkWords / 4; ++v) chk[k][v] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   DSA_STAMP(1);
@@ -983,14 +1004,42 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   for (int u = 0; u < kAhead; ++u)
     if (u < n_blocks) issue(u);
   load_q(g_cur);
-  // compiler-visible wait (vmcnt 0) for q, w and the tile records' block-table and scale loads,
-  // so no wait for them lands in the main loop (it also covers the first blocks, and wave 0's
-  // clears)
+  // compiler-visible wait (vmcnt 0) for q, w, the tile records' block-table and scale loads and
+  // the check reads, so no wait for them lands in the main loop (it also covers the first blocks)
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  if (wave == 0 && !a.withhold_tag)
-    for (int k = lane; k < n_starts; k += 64)
-      __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + row0_of(lds_starts[k]) * kCtl + kTagWord),
-                         a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n_starts > 0) {                        // workgroup-uniform
+    if (tid < kCheckStarts) lds_dirty[tid] = check ? 0 : 1;
+    __syncthreads();
+    if (check) {
+#pragma unroll
+      for (int k = 0; k < kCheckStarts; ++k) {
+        uint32_t any = 0u;
+#pragma unroll
+        for (int v = 0; v <= kChkWords / 4; ++v) any |= chk[k][v][0] | chk[k][v][1] | chk[k][v][2] | chk[k][v][3];
+        if (k < n_starts && __ballot(any != 0u) != 0ull && lane == 0) lds_dirty[k] = 1;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      bool cleared = false;
+      for (int k = 0; k < n_starts; ++k) {
+        if (check && lds_dirty[k] == 0) continue;
+        const size_t r0 = row0_of(lds_starts[k]);
+        const int nrows = rows_of(lds_starts[k]);
+        for (int i = lane; i < nrows * kBins; i += 64)
+          __hip_atomic_store(&a.hist[r0 * kBins + i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = lane; i < nrows * kTagWord; i += 64)
+          __hip_atomic_store(&a.ctl[(r0 + i / kTagWord) * kCtl + i % kTagWord], 0u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        cleared = true;
+      }
+      if (cleared) __builtin_amdgcn_s_waitcnt(0x0F70);
+      if (!a.withhold_tag)
+        for (int k = lane; k < n_starts; k += 64)
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(a.ctl + row0_of(lds_starts[k]) * kCtl + kTagWord),
+                             a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
   if constexpr (FP8 && !MX) {
     if (tid < n_items) lds_rsc[tid] = my_sc;
     lds_barrier();
@@ -1023,12 +1072,24 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
     const int4 rec = lds_rec[i];
     const int g = __builtin_amdgcn_readfirstlane(rec.x & ((1 << kGroupBits) - 1));
     const int j = __builtin_amdgcn_readfirstlane(rec.x >> kGroupBits);
-    if (g != g_cur) {                 // new group: publish the histograms, load the queries
-      __syncthreads();
-      flush(g_cur);
-      load_q(g);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
+    if (g != g_cur) {                 // new group: publish or park the histograms, load the queries
+      if constexpr (HB == 2) {
+        if (pend >= 0) {              // both histograms hold groups: publish the older one
+          __syncthreads();
+          flush(pend, hb ^ 1);
+          __syncthreads();            // cleared before the new group counts into it
+        }
+        pend = g_cur;
+        hb ^= 1;
+        load_q(g);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      } else {
+        __syncthreads();
+        flush(g_cur, 0);
+        load_q(g);
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      }
       g_cur = g;
       cur_row0 = row0_of(g);
       cur_rows = rows_of(g);
@@ -1101,13 +1162,13 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
       if (hh == 0 && s < n_me && n_me > a.K && row_ok) {
         const uint32_t key = float_key(part);
         a.keys[(cur_row0 + qi) * a.row_stride + s] = key;
-        if constexpr (TQ == 1) atomicAdd(&lds_hist[0][key >> 21], 1u);
-        else atomicAdd(&lds_hist[qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
+        atomicAdd(&lds_hist[hb][qi][key >> 22], 1u << (16 * ((key >> 21) & 1u)));
       }
     }
   }
   __syncthreads();
-  flush(g_cur);
+  flush(g_cur, hb);
+  if (HB == 2 && pend >= 0) flush(pend, hb ^ 1);
   DSA_STAMP(2);
 }
 
@@ -1116,7 +1177,7 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
 // seg_len(n) keys, one workgroup each.
 struct SelectArgs {
   const uint32_t* keys;     // [rows, row_stride] order-preserving score keys
-  const uint32_t* hist;     // [rows, kBins] histogram of key bits 31..21
+  uint32_t* hist;           // [rows, kBins] histogram of key bits 31..21 (left zero once read)
   uint32_t* ctl;            // [rows, kCtl]: segments done, gt cursor, candidate cursor (zeroed per
                             // call), then the histogram-cleared tag, which the select resets
   int32_t* g_gt;            // [rows, DSA_MAX_TOP_K] positions above the threshold range
@@ -1249,6 +1310,16 @@ __device__ __forceinline__ void emit_words(const uint32_t (&sel)[2], const uint3
 // through per-chunk bitmaps.  A prefix range too big for LDS falls back to one workgroup for the
 // row, which resolves more digits with histogram passes over the row, and, if even the exact key
 // theta has too many ties, emits straight from the keys.
+// Leaves a row's histogram and the select's counters (control words 0..3) zero for the next call,
+// whose score kernel then finds them clear and skips its own clearing stores.  Called once every
+// reader of this call is done with them.  Plain stores: the next call's kernels run after this
+// launch has ended, when they are visible to every workgroup.
+__device__ __forceinline__ void sel_leave_clear(const SelectArgs& a, int row) {
+  u32x4* h = reinterpret_cast<u32x4*>(a.hist + (size_t)row * kBins);
+  for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) h[i] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(a.ctl + (size_t)row * kCtl) = u32x4{0u, 0u, 0u, 0u};
+}
+
 __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   constexpr int NT = kSelThreads;
   __shared__ uint32_t h1[kBins];           // digit-1 histogram
@@ -1323,6 +1394,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   uint32_t above, C;
   uint32_t prefix = sel_find_bin<kBins>(a.hist + (size_t)row * kBins, (uint32_t)a.K, S, phase, above, C);
   SEL_STAMP(4);
+  if (nseg == 1) sel_leave_clear(a, row);   // the only reader has read it (the scan's barrier)
   uint32_t need = (uint32_t)a.K - above;  // keys still to take from the current prefix range
   const uint32_t G = above;               // keys above the digit-0 range
   int resolved = 1;
@@ -1419,6 +1491,8 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       if (tid == 0) S.pub[2] = atomicAdd(&ctl[0], 1u);
       lds_barrier();
       if (S.pub[2] != (uint32_t)(nseg - 1)) return;
+      // every segment has read the histogram and updated the counters
+      sel_leave_clear(a, row);
       for (uint32_t i = tid; i < G; i += NT)
         gt_list[i] = __hip_atomic_load(&g_gt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (uint32_t i = tid; i < C; i += NT) {
