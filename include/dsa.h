@@ -23,8 +23,9 @@
  *     non-OK status, launches nothing and leaves outputs untouched.  A launch failure returns
  *     DSA_ERR_HIP.  dsa_last_error() gives a thread-local description of the last failure.
  *   - Workgroups of one launch meet through device memory in two places: a decode indexer
- *     workgroup waits for the workgroup that clears its row's histogram, and an attention combine
- *     workgroup waits for the split workgroups of its row.  The workgroup waited for always has a
+ *     workgroup waits for the workgroup that makes sure its row's histogram is clear, and an
+ *     attention combine workgroup waits for the split workgroups of its row.  The workgroup waited
+ *     for always has a
  *     lower index than the waiting one, so the waits end as long as the GPU dispatches the
  *     workgroups of a launch in index order (which AMD GPUs do).  Each wait is bounded (about 50 ms
  *     of polling): if it ever gives up, the affected outputs are not computed from partial data --
@@ -137,7 +138,9 @@ size_t dsa_indexer_workspace_size(const dsa_paged_layout *layout, const dsa_inde
  *            aligned; bf16: must be NULL
  *   idx_out  [batch, T, top_k] int32 logical positions, ascending, -1 padded; 4-byte aligned
  *   workspace / workspace_bytes: device scratch, 256-byte aligned, at least
- *            dsa_indexer_workspace_size() bytes; contents on entry are ignored.
+ *            dsa_indexer_workspace_size() bytes; contents on entry are ignored (a call leaves
+ *            the rows' histograms it read zero, so the next call on the same workspace skips
+ *            clearing them; any other contents are cleared first).
  */
 dsa_status dsa_indexer_topk(const void *q, const void *q_scale, const float *w,
                             const void *k_cache, const void *k_scale,
