@@ -25,15 +25,14 @@
  *   - Workgroups of one launch meet through device memory in two places: a decode indexer
  *     workgroup waits for the workgroup that makes sure its row's histogram is clear, and an
  *     attention combine workgroup waits for the split workgroups of its row.  The workgroup waited
- *     for always has a
- *     lower index than the waiting one, so the waits end as long as the GPU dispatches the
- *     workgroups of a launch in index order (which AMD GPUs do).  Each wait is bounded (about 50 ms
- *     of polling): if it ever gives up, the affected outputs are not computed from partial data --
- *     the indexer row is written as all -1, the attention outputs of the row (out and lse) as NaN --
- *     and dsa_debug_status() reports the timeout.  Test hooks, read at each indexer call and unset
- *     in normal use: DSA_TEST_SYNC_SPIN_CAP=<n> bounds the indexer wait at n polls, and
- *     DSA_TEST_WITHHOLD_TAG=1 makes the clearing workgroups skip their signal, so every indexer
- *     row with more than top_k visible keys takes the timeout path.
+ *     for always has a lower index than the waiting one, so the waits end as long as the GPU
+ *     dispatches the workgroups of a launch in index order (which AMD GPUs do).  Each wait is
+ *     bounded (about 50 ms of polling): if it ever gives up, the affected outputs are not computed
+ *     from partial data -- the indexer row is written as all -1, the attention outputs of the row
+ *     (out and lse) as NaN -- and dsa_debug_status() reports the timeout.  Test hooks, read at
+ *     each indexer call and unset in normal use: DSA_TEST_SYNC_SPIN_CAP=<n> bounds the indexer
+ *     wait at n polls, and DSA_TEST_WITHHOLD_TAG=1 makes the clearing workgroups skip their
+ *     signal, so every indexer row with more than top_k visible keys takes the timeout path.
  *   - Device-side preconditions (not checked on the host because the data lives on the device):
  *     T <= seq_lens[b] <= max_seq_len <= max_pages * page_size, block_table entries used by a
  *     sequence lie in [0, num_pages), fp8 scales are finite and > 0.  The kernels clamp page ids
