@@ -1237,15 +1237,17 @@ __device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch& S, uint32_t
 // Bin holding the need-th largest element of a histogram of NB bins (higher bin = larger keys);
 // returns it with the count in higher bins (`above`) and in the bin itself (`count`).  1 <= need
 // <= total is required.  Thread 0 owns the highest bins.
+// sel_find_bin_pre takes this thread's PER bins already loaded (h[i] = bin hi - 1 - i).
 template <int NB>
-__device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t need, SelScratch& S,
-                                                 uint32_t& phase, uint32_t& above, uint32_t& count) {
+__device__ __forceinline__ uint32_t sel_find_bin_pre(const uint32_t (&h)[NB / kSelThreads], uint32_t need,
+                                                     SelScratch& S, uint32_t& phase, uint32_t& above,
+                                                     uint32_t& count) {
   constexpr int PER = NB / kSelThreads;
   static_assert(PER >= 1 && NB % kSelThreads == 0, "bins per thread");
   const int hi = NB - PER * (int)threadIdx.x;
-  uint32_t h[PER], mine = 0;
+  uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) { h[i] = hist[hi - 1 - i]; mine += h[i]; }
+  for (int i = 0; i < PER; ++i) mine += h[i];
   uint32_t tot;
   const uint32_t pre = sel_scan(mine, S, phase, tot);
   if (pre < need && pre + mine >= need) {
@@ -1260,6 +1262,16 @@ __device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t 
   above = S.res[1];
   count = S.res[2];
   return S.res[0];
+}
+template <int NB>
+__device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t need, SelScratch& S,
+                                                 uint32_t& phase, uint32_t& above, uint32_t& count) {
+  constexpr int PER = NB / kSelThreads;
+  const int hi = NB - PER * (int)threadIdx.x;
+  uint32_t h[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) h[i] = hist[hi - 1 - i];
+  return sel_find_bin_pre<NB>(h, need, S, phase, above, count);
 }
 
 // Radix digits of a key: digit 0 = bits 31..21 (histogrammed by the score kernel), digit 1 =
@@ -1335,6 +1347,13 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   // timeline points 3..7 of the row's first segment (the score kernel uses 0..2)
 #define SEL_STAMP(point) do { if (seg == 0) DSA_STAMP(point); } while (0)
   SEL_STAMP(3);
+  // The row histogram's bins of this thread go out first, beside the sequence length and poison
+  // loads they would otherwise wait behind.
+  constexpr int kHistPer = kBins / kSelThreads;
+  uint32_t hist0[kHistPer];
+#pragma unroll
+  for (int i = 0; i < kHistPer; ++i)
+    hist0[i] = a.hist[(size_t)row * kBins + kBins - kHistPer * tid - 1 - i];
   // the score kernel of this call is done with the row's histogram-cleared tag: reset it, so a
   // replay of the same launches (same tag) waits for its own clear again
   if (seg == 0 && tid == 0)
@@ -1392,7 +1411,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   h2[tid] = 0u;
   if (tid == 0) S.cursor = 0u;
   uint32_t above, C;
-  uint32_t prefix = sel_find_bin<kBins>(a.hist + (size_t)row * kBins, (uint32_t)a.K, S, phase, above, C);
+  uint32_t prefix = sel_find_bin_pre<kBins>(hist0, (uint32_t)a.K, S, phase, above, C);
   SEL_STAMP(4);
   if (nseg == 1) sel_leave_clear(a, row);   // the only reader has read it (the scan's barrier)
   uint32_t need = (uint32_t)a.K - above;  // keys still to take from the current prefix range
