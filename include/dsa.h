@@ -194,9 +194,9 @@ size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_
  * result is exact for any logits, and the extra cost is at most one more pass over the split per
  * raise: a split of t 32-key tiles whose largest logit climbs by more than 164 log2 units (about
  * 114 in natural units, after sm_scale) from each tile to the next restarts up to t - 1 times,
- * about t^2 / 2 tile passes in all; real attention logits stay within one reference.  An entry outside [0, pos], pos = seq_lens[b] - T + t (the positions
- * query t may attend to), is skipped like -1 and sets the attention-index check that
- * dsa_debug_status() reports.
+ * about t^2 / 2 tile passes in all; real attention logits stay within one reference.  An entry
+ * outside [0, pos], pos = seq_lens[b] - T + t (the positions query t may attend to), is skipped
+ * like -1 and sets the attention-index check that dsa_debug_status() reports.
  *
  *   q         [batch, T, heads, 576] bf16 (MLA-absorbed query), 16-byte aligned
  *   kv_cache  [num_pages, page_size, 576] bf16 latent rows, 16-byte aligned
