@@ -48,3 +48,21 @@ def test_workspace_dirty_clean_scribbled_relaid(T):
     assert np.array_equal(to_np(d.indexer(workspace=ws)), first)
     assert np.array_equal(to_np(d2.indexer(workspace=ws)), other)
     dsa.dsa_debug_status()
+
+
+def test_workspace_across_modes():
+    """One workspace through decode (T = 1), two query rows (T = 2: cleared by its own launch),
+    verify (T = 4) and decode again, each on its own layout of the same memory; every result
+    matches the oracle and the repeated decode call its first result."""
+    lens = (2600, 9000, 40000)
+    cases = [W.make_case(W.custom(f"wsmode{T}", 3, T, lens, 64, 128, 2048, 16)) for T in (1, 2, 4)]
+    devs = [Dev(c) for c in cases]
+    ws = torch.full((max(_need(d) for d in devs),), 0xA5, dtype=torch.uint8, device="cuda:0")
+    refs = [_ref(c, c.spec.T) for c in cases]
+    got = []
+    for d, c, (ref, extra) in zip(devs, cases, refs):
+        idx = to_np(d.indexer(workspace=ws))
+        check_indices_band(idx, ref, extra, 2048, c.seq_lens, c.spec.T)
+        got.append(idx)
+    assert np.array_equal(to_np(devs[0].indexer(workspace=ws)), got[0])
+    dsa.dsa_debug_status()
