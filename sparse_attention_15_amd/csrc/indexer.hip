@@ -947,9 +947,9 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
   // sequence end reads page 0; its keys are never stored.  The loop issues no other global load
   // (the fp8 page scales come from the tile records), so the counter waits below see only these.
   // Decode: block number k of this wave is block sub + WPQ * (k % NBW) of item k / NBW, in its
-  // private ring slot k % NSLOT.  Verify: item i sits in shared ring slot i % RS; this wave loads
-  // loads LPW * wave .. LPW * wave + LPW - 1 of the tile's 4 * BLK / 1024 (and, MXFP8, half a
-  // block's scale bytes).
+  // private ring slot k % NSLOT.  Verify and prefill: item i sits in shared ring slot i % RS; this
+  // wave issues loads LPW * wave .. LPW * wave + LPW - 1 of the tile's 4 * BLK / 1024 (and, MXFP8,
+  // half a block's scale bytes).
   auto block_ptr = [&](int slot, int blk) -> unsigned char* {
     return SHARED ? &lds_k[(slot * 4 + blk) * BLK] : &lds_k[(wave * NSLOT + slot) * BLK];
   };
@@ -1313,15 +1313,6 @@ __device__ __forceinline__ void emit_words(const uint32_t (&sel)[2], const uint3
   run_tie += tot >> 12;
 }
 
-// The threshold key theta (the K-th largest of the row's n > K keys) is resolved digit by digit,
-// digit 0 from the row histogram.  When the keys sharing the resolved prefix (the "candidates")
-// fit in LDS, each segment's workgroup collects, from its keys, the positions above the prefix
-// range and the (key, position) candidates; with several segments the lists go to global memory
-// and the workgroup that finishes last gathers them.  It resolves the remaining digits over the
-// candidates, then emits every key > theta plus the first `need` keys == theta in position order
-// through per-chunk bitmaps.  A prefix range too big for LDS falls back to one workgroup for the
-// row, which resolves more digits with histogram passes over the row, and, if even the exact key
-// theta has too many ties, emits straight from the keys.
 // Leaves a row's histogram and the select's counters (control words 0..3) zero for the next call,
 // whose score kernel then finds them clear and skips its own clearing stores.  Called once every
 // reader of this call is done with them.  Plain stores: the next call's kernels run after this
@@ -1332,6 +1323,15 @@ __device__ __forceinline__ void sel_leave_clear(const SelectArgs& a, int row) {
   if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(a.ctl + (size_t)row * kCtl) = u32x4{0u, 0u, 0u, 0u};
 }
 
+// The threshold key theta (the K-th largest of the row's n > K keys) is resolved digit by digit,
+// digit 0 from the row histogram.  When the keys sharing the resolved prefix (the "candidates")
+// fit in LDS, each segment's workgroup collects, from its keys, the positions above the prefix
+// range and the (key, position) candidates; with several segments the lists go to global memory
+// and the workgroup that finishes last gathers them.  It resolves the remaining digits over the
+// candidates, then emits every key > theta plus the first `need` keys == theta in position order
+// through per-chunk bitmaps.  A prefix range too big for LDS falls back to one workgroup for the
+// row, which resolves more digits with histogram passes over the row, and, if even the exact key
+// theta has too many ties, emits straight from the keys.
 __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   constexpr int NT = kSelThreads;
   __shared__ uint32_t h1[kBins];           // digit-1 histogram
