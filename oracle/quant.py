@@ -19,6 +19,19 @@ operations, rounded to nearest even.
 Per-head fp8 queries ([P1] §3: the prolog quantises the indexer q and folds the head weights in;
 reading): per query row and head, sq = amax / 448 in float32 (1 for an all-zero head), code = E4M3
 of float32(q / sq); the indexer then weights head h by w[t, h] * sq[t, h].
+
+Per-page fp8 indexer-K cache append ([P1] §3: the prolog writes the new keys into the cache; the
+fp8 indexer keeps one float32 scale per 64-token page; reading).  The pages fix no rule for a page
+that fills over several steps; the reading taken: a page's scale only grows, and equals the
+largest |key| the page has received, divided by 448.  For every page that receives new keys:
+  * m = max |new key element| landing in the page; candidate = float32(m / 448);
+  * s_old = the stored scale if the page already holds keys of this sequence (positions before
+    seq_len - T), else 0; s = max(s_old, candidate), and 1 if that is 0 (a page of zeros);
+  * if the page holds keys and s > s_old, each held code c is re-encoded:
+    E4M3(float32(float32(e4m3(c) * s_old) / s)) (a second rounding of those keys);
+  * new codes are E4M3(float32(x / s)); the page's scale becomes s.
+A page filled by one call gets exactly the one-shot rule of the fp8 workloads (scale = amax / 448
+of the page's keys).  E4M3 rounding is nearest even, clamped to +-448, throughout.
 """
 import numpy as np
 
@@ -113,3 +126,32 @@ def fp8_quantize_heads(x):
     sq = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
     y = (x / sq[..., None]).astype(np.float32)
     return _e4m3_rne(y.astype(np.float64)), sq
+
+
+def indexer_cache_append_fp8_ref(k_new, k_cache, k_scale, block_table, seq_lens, T):
+    """The per-page fp8 indexer-K cache after appending k_new [B, T, D] (bf16 values as float):
+    k_cache [P, 64, D] E4M3 codes, k_scale [P] float32, one scale per page.  Token t of sequence b
+    is logical position seq_lens[b] - T + t (page block_table[b, pos // 64], slot pos % 64).
+    Returns new (k_cache, k_scale) copies; codes of held keys must be finite."""
+    kc, ks = k_cache.copy(), np.asarray(k_scale, np.float32).copy()
+    x = np.asarray(k_new, np.float32)
+    f32 = np.float32
+    for b in range(x.shape[0]):
+        L = int(seq_lens[b])
+        first = L - T                                    # position of the first new key
+        for j in range(first // 64, (L - 1) // 64 + 1):
+            page = int(block_table[b, j])
+            lo, hi = max(first, 64 * j), min(L, 64 * j + 64)
+            held = lo - 64 * j                           # slots 0..held-1 already hold keys
+            new = x[b, lo - first:hi - first]
+            cand = f32(f32(np.abs(new).max()) / f32(E4M3_MAX))
+            s_old = ks[page] if held > 0 else f32(0.0)
+            s = max(s_old, cand)
+            if s == 0:
+                s = f32(1.0)
+            if held > 0 and s > s_old:
+                dec = (e4m3_table()[kc[page, :held]].astype(f32) * s_old).astype(f32)
+                kc[page, :held] = _e4m3_rne((dec / s).astype(f32).astype(np.float64))
+            kc[page, held:held + hi - lo] = _e4m3_rne((new / s).astype(f32).astype(np.float64))
+            ks[page] = s
+    return kc, ks
