@@ -179,6 +179,10 @@ def main():
     ap.add_argument("--append", action="store_true",
                     help="time dsa_indexer_cache_append instead: a prefill chunk of MXFP8 keys "
                          "(8 sequences x 65536 tokens x 128 dims) into the paged cache")
+    ap.add_argument("--append-fp8", action="store_true",
+                    help="time dsa_indexer_cache_append_fp8 instead: a prefill chunk of keys "
+                         "(8 sequences x 65536 tokens x 128 dims) into the per-page fp8 cache, "
+                         "and a decode step (32 sequences x 1 key into partly filled pages)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -207,6 +211,8 @@ def main():
         return bench_append(args, dev, dsa)
     if args.append_kv8:
         return bench_append_kv8(args, dev, dsa)
+    if args.append_fp8:
+        return bench_append_fp8(args, dev, dsa)
 
     r = run_workload(args.workload, args, dev, torch, dsa, W, None, cpu=not args.no_cpu_baseline)
     res = r["line"]
@@ -554,6 +560,92 @@ def bench_append(args, dev, dsa):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "mx_quant_rows (paged)", "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": cpu}), flush=True)
+
+
+def bench_append_fp8(args, dev, dsa):
+    """dsa_indexer_cache_append_fp8 of a prefill chunk: B sequences x T new keys x 128 dims, bf16
+    in, E4M3 codes out with one fp32 scale per 64-key page, into fresh permuted pages.
+    Algorithmic bytes per call: 2 B read + 1 B written per element, plus 4 B of scale written and
+    4 B of table read per page.  Also times a decode step: 32 sequences appending one key each to
+    pages that already hold keys (launch-bound; reported as us per call)."""
+    import torch
+    import oracle.quant as oq
+    B, T, D = 8, 65536, 128
+    P = B * T // 64 + 1
+    gen = torch.Generator(device=dev).manual_seed(17)
+    perm = torch.randperm(P, device=dev, generator=gen).to(torch.int32)
+    bt = perm[:B * T // 64].view(B, T // 64).contiguous()
+    sl = torch.full((B,), T, dtype=torch.int32, device=dev)
+    nbytes = B * T * D * 2 + B * T * D + bt.numel() * (4 + 4)
+    R = max(1, math.ceil(args.rotate_gib * 2 ** 30 / nbytes))
+    srcs = [(torch.randn(B, T, D, device=dev, generator=gen) / math.sqrt(D)).to(torch.bfloat16) for _ in range(R)]
+    kcs = [torch.empty(P, 64, D, dtype=torch.uint8, device=dev) for _ in range(R)]
+    kss = [torch.empty(P, dtype=torch.float32, device=dev) for _ in range(R)]
+    log(f"fp8 page append: B={B} T={T} D={D}, {nbytes / 1e6:.1f} MB per call, {R} rotation copies")
+
+    def step(i):
+        j = i % R
+        dsa.dsa_indexer_cache_append_fp8(srcs[j], kcs[j], kss[j], bt, sl, max_seq_len=T, num_pages=P)
+
+    def timed(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms = timed(step, args.steps)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"timed {args.steps} calls: {ms * 1e3:.1f} us/call, {gbs:.1f} GB/s")
+
+    # decode step: sequence b of 32 holds lens[b] - 1 keys (in pages the prefill chunk filled) and
+    # appends one; lengths are spread over the slot offsets of a page.  After the first call the
+    # key fits the page's scale, so the timed calls re-encode nothing
+    Bd = 32
+    lens_d = torch.tensor([1000 + 197 * b for b in range(Bd)], dtype=torch.int32, device=dev)
+    bt_d = perm[:Bd * 112].view(Bd, 112).contiguous()      # 112 pages = 7168 positions per sequence
+    new_d = (torch.randn(Bd, 1, D, device=dev, generator=gen) / math.sqrt(D)).to(torch.bfloat16)
+
+    def dstep(i):
+        dsa.dsa_indexer_cache_append_fp8(new_d, kcs[0], kss[0], bt_d, lens_d, max_seq_len=112 * 64,
+                                         num_pages=P)
+
+    for i in range(args.warmup):
+        dstep(i)
+    torch.cuda.synchronize()
+    ms_d = timed(dstep, args.steps)
+    log(f"decode step B={Bd}: {ms_d * 1e3:.2f} us/call")
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's append over the first sequences of one call (NumPy float32 / float64)
+        x = srcs[0].float().cpu().numpy()
+        btn, ksn = bt.cpu().numpy(), np.zeros(P, np.float32)
+        kcn = np.zeros((P, 64, D), np.uint8)
+        keys, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            n = 4096
+            oq.indexer_cache_append_fp8_ref(x[:1, :n], kcn, ksn, btn[:1], np.array([n]), n)
+            keys += n
+        el = time.perf_counter() - t0
+        cpu = {"value": round(keys / el * D * 2 / 1e9, 4), "unit": "GB/s (bf16 read)", "cores": 1,
+               "kind": "oracle", "sample": f"{keys} keys of one call in {el:.1f} s"}
+    print(json.dumps({
+        "metric": "fp8 per-page indexer-K cache append throughput", "value": round(gbs, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16->e4m3",
+        "data": "synthetic",
+        "config": {"workload": f"cache append B={B} T={T} dim={D}, page 64, permuted fresh pages",
+                   "rotation_copies": R},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fp8_page_append", "algorithmic_bytes_per_launch": nbytes},
+        "decode_step": {"batch": Bd, "T": 1, "us_per_call": round(ms_d * 1e3, 2)},
         "cpu_baseline": cpu}), flush=True)
 
 

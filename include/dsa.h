@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define DSA_VERSION 3             /* 3: FP8 latent cache (attention, append), per-head fp8 q quantiser */
+#define DSA_VERSION 4             /* 4: per-page fp8 indexer-K append; 3: FP8 latent cache, per-head fp8 q */
 #define DSA_PAGE_SIZE 64          /* tokens per cache page */
 #define DSA_DIM_QK 576            /* MLA latent row: 512 "nope" + 64 rope columns */
 #define DSA_DIM_V 512             /* V = the first 512 columns of the latent row */
@@ -175,6 +175,33 @@ dsa_status dsa_mxfp8_quantize(const void *x, int64_t rows, int32_t dim, void *co
  * dsa_indexer_topk. */
 dsa_status dsa_indexer_cache_append(const void *k_new, const dsa_paged_layout *layout, int32_t T,
                                     int32_t dim, void *k_cache, void *k_scale, hipStream_t stream);
+
+/* Appends the T newest keys of every sequence to the per-page fp8 indexer-K cache that
+ * dsa_indexer_topk reads with DSA_FP8_E4M3 ([P1] §3: the prolog writes each step's new keys into
+ * the cache; the fp8 indexer keys carry one fp32 scale per page).  Key t of sequence b is logical
+ * position seq_lens[b] - T + t, stored at page block_table[b, pos / 64], slot pos % 64.
+ *
+ * A page's scale only grows: it is the largest |key| the page has received / 448 (fp32 division),
+ * 1 while it has received only zeros.  For each page that receives new keys, with m = the largest
+ * |element| of those keys and s_old = the page's stored scale if it already holds keys of the
+ * sequence (positions before seq_lens[b] - T; otherwise the stored value is ignored):
+ *     s = max(s_old, m / 448)  (1 if that is 0)
+ *     if s > s_old, every held code c becomes E4M3((e4m3(c) * s_old) / s)   (a second rounding)
+ *     new codes are E4M3(x / s);  k_scale[page] = s
+ * with every product and quotient rounded to nearest even in fp32 and every E4M3 conversion
+ * nearest even, clamped to +-448.  A page written by one call holds exactly the one-shot
+ * quantisation (scale = amax / 448 of its keys).  Nothing else in the cache changes.
+ *
+ *   k_new    [batch, T, dim] bf16, finite, 16-byte aligned; dim 64 or 128
+ *   k_cache  [num_pages, page_size, dim] E4M3FN codes, 16-byte aligned; held codes finite
+ *   k_scale  [num_pages] fp32, 4-byte aligned; held pages' scales positive and finite
+ * The pages of different sequences must be distinct (each page is rewritten whole by one
+ * workgroup).  A sequence whose length lies outside [T, max_seq_len] is left untouched and sets
+ * the length check that dsa_debug_status() reports; block_table entries are device-side
+ * preconditions as for dsa_indexer_topk.  DSA_ERR_UNSUPPORTED for another dim, DSA_ERR_SHAPE for
+ * T < 1 or batch * T beyond 2^31 - 1, DSA_ERR_NULL / DSA_ERR_ALIGN as named. */
+dsa_status dsa_indexer_cache_append_fp8(const void *k_new, const dsa_paged_layout *layout, int32_t T,
+                                        int32_t dim, void *k_cache, float *k_scale, hipStream_t stream);
 
 /* Bytes of workspace dsa_sparse_attn needs for this layout and shape (0 on invalid input). */
 size_t dsa_sparse_attn_workspace_size(const dsa_paged_layout *layout, const dsa_attn_shape *shape);

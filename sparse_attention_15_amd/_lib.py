@@ -56,7 +56,7 @@ class DsaError(RuntimeError):
 _lib = None
 
 EXPORTS = ["dsa_indexer_workspace_size", "dsa_indexer_topk", "dsa_sparse_attn_workspace_size",
-           "dsa_sparse_attn", "dsa_sparse_attn_noalloc", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_latent_cache_append_fp8", "dsa_fp8_quantize_heads", "dsa_profile_start",
+           "dsa_sparse_attn", "dsa_sparse_attn_noalloc", "dsa_sparse_attn_fp8kv", "dsa_mxfp8_quantize", "dsa_indexer_cache_append", "dsa_indexer_cache_append_fp8", "dsa_latent_cache_append_fp8", "dsa_fp8_quantize_heads", "dsa_profile_start",
            "dsa_profile_stop", "dsa_last_error", "dsa_version", "dsa_debug_status"]
 
 
@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
     L.dsa_indexer_cache_append.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
                                            vp, vp, vp]
     L.dsa_indexer_cache_append.restype = ctypes.c_int
+    L.dsa_indexer_cache_append_fp8.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, ctypes.c_int32,
+                                               vp, vp, vp]
+    L.dsa_indexer_cache_append_fp8.restype = ctypes.c_int
     L.dsa_latent_cache_append_fp8.argtypes = [vp, ctypes.POINTER(Layout), ctypes.c_int32, vp, vp, vp]
     L.dsa_latent_cache_append_fp8.restype = ctypes.c_int
     L.dsa_fp8_quantize_heads.argtypes = [vp, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
@@ -192,6 +195,21 @@ def dsa_indexer_cache_append(k_new, k_cache, k_scale, block_table, seq_lens, *, 
     layout = make_layout(block_table, seq_lens, P, max_seq_len)
     _check(lib().dsa_indexer_cache_append(_ptr(k_new), ctypes.byref(layout), T, dim, _ptr(k_cache),
                                           _ptr(k_scale), _stream(stream)))
+    return k_cache, k_scale
+
+
+def dsa_indexer_cache_append_fp8(k_new, k_cache, k_scale, block_table, seq_lens, *, max_seq_len: int,
+                                 num_pages: int | None = None, stream=None):
+    """Appends k_new [B, T, dim] bf16 (the T newest keys of each sequence) to the per-page fp8
+    cache k_cache [P, 64, dim] uint8 / k_scale [P] fp32, in place (a page's scale grows with the
+    keys it receives; its held codes are re-encoded when it does)."""
+    assert k_new.dtype == torch.bfloat16 and k_new.is_contiguous()
+    assert k_scale.dtype == torch.float32
+    B, T, dim = k_new.shape
+    P = k_cache.shape[0] if num_pages is None else num_pages
+    layout = make_layout(block_table, seq_lens, P, max_seq_len)
+    _check(lib().dsa_indexer_cache_append_fp8(_ptr(k_new), ctypes.byref(layout), T, dim, _ptr(k_cache),
+                                              _ptr(k_scale), _stream(stream)))
     return k_cache, k_scale
 
 

@@ -197,6 +197,29 @@ dsa_status dsa_indexer_cache_append(const void* k_new, const dsa_paged_layout* l
   return DSA_OK;
 }
 
+dsa_status dsa_indexer_cache_append_fp8(const void* k_new, const dsa_paged_layout* layout, int32_t T,
+                                        int32_t dim, void* k_cache, float* k_scale, hipStream_t stream) {
+  if (T < 1) return fail(DSA_ERR_SHAPE, "T %d < 1", T);
+  dsa_status st = check_layout(layout, T);
+  if (st != DSA_OK) return st;
+  if (k_new == nullptr || k_cache == nullptr || k_scale == nullptr)
+    return fail(DSA_ERR_NULL, "k_new / k_cache / k_scale is NULL");
+  if (dim != 64 && dim != 128) return fail(DSA_ERR_UNSUPPORTED, "dim %d unsupported (64 or 128)", dim);
+  if (!aligned(k_new, 16) || !aligned(k_cache, 16) || !aligned(k_scale, 4))
+    return fail(DSA_ERR_ALIGN, "k_new / k_cache need 16-byte alignment, k_scale 4-byte");
+  const long long span = (T + 62) / 64 + 1;           // pages one sequence's T keys can reach
+  if ((long long)layout->batch * T > 0x7FFFFFFFLL || (long long)layout->batch * span > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_SHAPE, "batch * T exceeds 2^31 - 1");
+  dsa::Fp8PageLaunch q;
+  q.src = k_new; q.codes = k_cache; q.scales = k_scale;
+  q.block_table = layout->block_table; q.seq_lens = layout->seq_lens;
+  q.batch = layout->batch; q.T = T; q.dim = dim;
+  q.max_pages = layout->max_pages; q.num_pages = layout->num_pages; q.max_seq_len = layout->max_seq_len;
+  const hipError_t e = dsa::launch_fp8_page_append(q, stream);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "fp8 cache append launch: %s", hipGetErrorString(e));
+  return DSA_OK;
+}
+
 dsa_status dsa_fp8_quantize_heads(const void* x, int64_t rows, int32_t dim, void* codes, float* scales,
                                   hipStream_t stream) {
   if (rows < 0) return fail(DSA_ERR_SHAPE, "rows %lld < 0", (long long)rows);

@@ -69,6 +69,15 @@ struct Kv8Launch {
   int T, max_pages, num_pages, max_seq_len;
 };
 hipError_t launch_kv8_append(const Kv8Launch& q, hipStream_t stream);
+struct Fp8PageLaunch {
+  const void* src;          // [B, T, dim] bf16
+  void* codes;              // [P, 64, dim] E4M3
+  float* scales;            // [P] fp32
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int batch, T, dim, max_pages, num_pages, max_seq_len;
+};
+hipError_t launch_fp8_page_append(const Fp8PageLaunch& q, hipStream_t stream);
 hipError_t launch_fp8_heads(const void* src, long long rows, int dim, void* codes, float* scales,
                             hipStream_t stream);
 

@@ -1,6 +1,7 @@
 // quant.hip -- quantisation kernels of the prolog for gfx950: MXFP8 indexer rows (the step that
 // writes the new keys of a decode or prefill step into the paged MXFP8 indexer-K cache, and the
-// same quantiser for the indexer queries), and the FP8 latent-row append for the SFA cache.
+// same quantiser for the indexer queries), the per-page fp8 indexer-K append, the per-head fp8
+// query quantiser, and the FP8 latent-row append for the SFA cache.
 //
 // Pages: "Inference Optimization for Kimi K3.1 Pro: Decoding Architecture Evolution and Systems
 // Engineering Practices" §3 (the indexer prolog produces the indexer q and k and writes k into the
@@ -250,6 +251,129 @@ __global__ __launch_bounds__(256) void fp8_quant_heads(HeadArgs a) {
     *reinterpret_cast<uint2*>(a.codes + rr * D + 8 * c) = e4m3x8_scaled(x, sq);
     if (c == 0) a.scales[rr] = sq;
   }
+}
+
+// Per-page fp8 indexer-K append ("Inference Optimization for Kimi K3.1 Pro" §3: the prolog writes
+// each step's new keys into the cache; the fp8 indexer keeps one fp32 scale per 64-token page).
+// A page's scale only grows: it is the largest |key| the page has received / 448 (fp32 division),
+// 1 while the page has received only zeros.  For a page that receives new keys:
+//   s = max(s_old, m / 448), m = max |new key element| in the page, s_old = the stored scale if
+//   the page already holds keys of the sequence (else 0); s = 1 if that is 0;
+//   if s > s_old the held codes are re-encoded as E4M3((e4m3(c) * s_old) / s), each operation
+//   rounded to nearest even in fp32; new codes are E4M3(x / s); the page's scale becomes s.
+// One 256-thread workgroup per page the append reaches (the span of T keys touches at most
+// (T + 62) / 64 + 1 pages of a sequence): a page row of D bf16 is D / 8 16-byte chunks, so thread i
+// handles chunks i, i + 256, ... of the page (2 for D = 64, 4 for D = 128), all loads issued
+// before the block maximum is taken.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+struct Fp8PageArgs {
+  const uint16_t* src;        // [B, T, D] bf16
+  unsigned char* codes;       // [P, 64, D] E4M3
+  float* scales;              // [P]
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int T, span, max_pages, num_pages, max_seq_len;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void fp8_page_append(Fp8PageArgs a) {
+  constexpr int CPR = D / 8;                   // 16-byte chunks per key row
+  constexpr int PER = kPage * CPR / 256;       // chunks per thread
+  static_assert(PER * 256 == kPage * CPR, "D = 64 or 128");
+  __shared__ float red[4];
+  const int b = blockIdx.x / a.span, jj = blockIdx.x % a.span;
+  const int L = a.seq_lens[b];
+  if (L < a.T || L > a.max_seq_len) {          // no position is certain: write nothing
+    if (jj == 0 && threadIdx.x == 0) flag_input(kFlagLen);
+    return;
+  }
+  const int first = L - a.T;                   // logical position of the first new key
+  const int j = first / kPage + jj;            // the sequence's page this workgroup writes
+  if (j * kPage >= L) return;                  // whole workgroup: the span ends before this page
+  const int page = clamp_page(a.block_table[(size_t)b * a.max_pages + j], a.num_pages);
+  const int held = max(first - j * kPage, 0);  // slots 0 .. held-1 hold earlier keys
+  const int end = min(L - j * kPage, kPage);   // new keys fill slots held .. end-1
+  const long long src_row0 = (long long)b * a.T + (j * kPage - first);   // row of slot 0
+
+  u32x4 v[PER];
+  float am = 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = threadIdx.x + 256 * k, slot = c / CPR, col = c % CPR;
+    if (slot >= held && slot < end)
+      v[k] = *reinterpret_cast<const u32x4*>(a.src + (size_t)(src_row0 + slot) * D + 8 * col);
+  }
+  const float s_old = held > 0 ? a.scales[page] : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int slot = (threadIdx.x + 256 * k) / CPR;
+    if (slot >= held && slot < end) {
+      float x[8];
+      bf16x8_to_f32(v[k], x);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = fmaxf(s_old, __fdiv_rn(m, 448.f));
+  if (s == 0.f) s = 1.f;
+
+  unsigned char* pg = a.codes + (size_t)page * kPage * D;
+  if (held > 0 && s > s_old) {                 // workgroup-uniform
+    // each chunk of a held slot is read and written by the same thread
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int c = threadIdx.x + 256 * k, slot = c / CPR, col = c % CPR;
+      if (slot < held) {
+        uint2* q = reinterpret_cast<uint2*>(pg + (size_t)slot * D + 8 * col);
+        const uint2 w = *q;
+        float x[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t word = h ? w.y : w.x;
+          const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+          const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+          x[4 * h] = __fmul_rn(lo[0], s_old);
+          x[4 * h + 1] = __fmul_rn(lo[1], s_old);
+          x[4 * h + 2] = __fmul_rn(hi[0], s_old);
+          x[4 * h + 3] = __fmul_rn(hi[1], s_old);
+        }
+        *q = e4m3x8_scaled(x, s);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int c = threadIdx.x + 256 * k, slot = c / CPR, col = c % CPR;
+    if (slot >= held && slot < end) {
+      float x[8];
+      bf16x8_to_f32(v[k], x);
+      *reinterpret_cast<uint2*>(pg + (size_t)slot * D + 8 * col) = e4m3x8_scaled(x, s);
+    }
+  }
+  if (threadIdx.x == 0) a.scales[page] = s;
+}
+
+hipError_t launch_fp8_page_append(const Fp8PageLaunch& q, hipStream_t st) {
+  if (q.batch == 0) return hipSuccess;
+  Fp8PageArgs a;
+  a.src = static_cast<const uint16_t*>(q.src);
+  a.codes = static_cast<unsigned char*>(q.codes);
+  a.scales = q.scales;
+  a.block_table = q.block_table;
+  a.seq_lens = q.seq_lens;
+  a.T = q.T; a.max_pages = q.max_pages; a.num_pages = q.num_pages; a.max_seq_len = q.max_seq_len;
+  a.span = (q.T + kPage - 2) / kPage + 1;
+  const long long blocks = (long long)q.batch * a.span;
+  LaunchScope ls("fp8_page_append", st);
+  if (q.dim == 128) hipLaunchKernelGGL(fp8_page_append<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(fp8_page_append<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_heads(const void* src, long long rows, int dim, void* codes, float* scales,

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
-    assert dsa.lib().dsa_version() == 3
+    assert dsa.lib().dsa_version() == 4
 
 
 def _layout(B=2, max_pages=4, max_len=256, num_pages=9, page=64):
@@ -210,3 +210,17 @@ def test_cache_append_rejects(kw, status):
     a.update(kw)
     assert dsa.lib().dsa_indexer_cache_append(a["k_new"], ctypes.byref(a["layout"]), a["T"], a["dim"],
                                               a["k_cache"], a["k_scale"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_new=None), 1), (dict(k_cache=None), 1), (dict(k_scale=None), 1),
+    (dict(T=0), 2), (dict(dim=96), 4), (dict(dim=256), 4), (dict(k_new=FAKE + 2), 3),
+    (dict(k_cache=FAKE + 8), 3), (dict(k_scale=FAKE + 2), 3),
+    (dict(layout=_layout(page=32)), 4), (dict(layout=_layout(max_len=0)), 2),
+    (dict(layout=L.Layout(FAKE, FAKE + 256, 1 << 30, 1 << 14, 64, 9, 1 << 20), T=1 << 10), 2),
+])
+def test_fp8_cache_append_rejects(kw, status):
+    a = dict(k_new=FAKE, layout=_layout(), T=1, dim=128, k_cache=FAKE, k_scale=FAKE)
+    a.update(kw)
+    assert dsa.lib().dsa_indexer_cache_append_fp8(a["k_new"], ctypes.byref(a["layout"]), a["T"], a["dim"],
+                                                  a["k_cache"], a["k_scale"], None) == status
