@@ -195,8 +195,8 @@ dsa_status dsa_indexer_cache_append(const void *k_new, const dsa_paged_layout *l
  *   k_new    [batch, T, dim] bf16, finite, 16-byte aligned; dim 64 or 128
  *   k_cache  [num_pages, page_size, dim] E4M3FN codes, 16-byte aligned; held codes finite
  *   k_scale  [num_pages] fp32, 4-byte aligned; held pages' scales positive and finite
- * The pages of different sequences must be distinct (each page is rewritten whole by one
- * workgroup).  A sequence whose length lies outside [T, max_seq_len] is left untouched and sets
+ * The block-table entries a call reaches must name distinct pages, within a sequence and across
+ * sequences (each page is rewritten by one workgroup).  A sequence whose length lies outside [T, max_seq_len] is left untouched and sets
  * the length check that dsa_debug_status() reports; block_table entries are device-side
  * preconditions as for dsa_indexer_topk.  DSA_ERR_UNSUPPORTED for another dim, DSA_ERR_SHAPE for
  * T < 1 or batch * T beyond 2^31 - 1, DSA_ERR_NULL / DSA_ERR_ALIGN as named. */
