@@ -154,3 +154,65 @@ def test_indexer_and_attention_step_graph_replays(cfg):
         assert torch.equal(idx, i_ref), f"replay {r}: indices"
         assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}: out"
         assert torch.equal(lse, l_ref), f"replay {r}: lse"
+
+
+def test_fp8_cache_append_and_indexer_graph_replays():
+    """The per-page fp8 cache append followed by the fp8 indexer, captured once and replayed on new
+    keys and queries from the same starting cache (the eager calls and synchronisations in between);
+    codes, page scales and indices of every replay equal the eager calls' bit for bit.  The new
+    keys grow from replay to replay, so page scales rise and held keys are re-encoded."""
+    spec = W.custom("fp8page_graph", 2, 1, (2600, 4100), 64, 128, 256, 16, idx_dtype="fp8")
+    print(f"[case] graph {spec.name}", flush=True)
+    c = W.make_case(spec, poison=False)
+    d = Dev(c)
+    T = 40
+    dev = d.q_idx.device
+    k0, s0 = d.k.clone(), d.k_scale.clone()
+    new = torch.empty((2, T, spec.DI), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((2, 1, spec.K), dtype=torch.int32, device=dev)
+    layout = dsa.make_layout(d.bt, d.sl, c.num_pages, spec.max_len)
+    shape = dsa.IndexerShape(1, spec.HI, spec.DI, spec.K, dsa.DSA_FP8_E4M3)
+    ws = torch.empty(max(256, dsa.dsa_indexer_workspace_size(layout, shape)), dtype=torch.uint8, device=dev)
+
+    def calls(o):
+        dsa.dsa_indexer_cache_append_fp8(new, d.k, d.k_scale, d.bt, d.sl, max_seq_len=spec.max_len,
+                                         num_pages=c.num_pages)
+        d.indexer(idx_out=o, workspace=ws)
+
+    gen = torch.Generator(device="cpu").manual_seed(10)
+
+    def fresh(r):
+        return (torch.randn((2, T, spec.DI), generator=gen) * (0.1 * 4.0 ** r)).to(torch.bfloat16)
+
+    new.copy_(fresh(0))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls(out)                                        # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(out)
+    torch.cuda.synchronize()
+    q0 = d.q_idx.clone()
+    raised = False
+    for r in range(4):
+        new.copy_(fresh(r))
+        d.q_idx.copy_(q0[:, :, torch.randperm(spec.HI, generator=gen)])
+        d.k.copy_(k0)
+        d.k_scale.copy_(s0)
+        ref = torch.empty_like(out)
+        calls(ref)                                        # eager, from the starting cache
+        torch.cuda.synchronize()
+        ref_k, ref_s = d.k.clone(), d.k_scale.clone()
+        d.k.copy_(k0)
+        d.k_scale.copy_(s0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.k, ref_k), f"replay {r}: codes"
+        assert torch.equal(d.k_scale.view(torch.int32), ref_s.view(torch.int32)), f"replay {r}: scales"
+        assert torch.equal(out, ref), f"replay {r}: indices"
+        raised |= bool((ref_s != s0).any())
+    assert raised
