@@ -184,3 +184,37 @@ def test_length_below_T_writes_nothing_and_is_reported():
             p = c.bt[b, j]
             np.testing.assert_array_equal(got_c[p], ref_c[p])
             assert got_s[p].view(np.uint32) == ref_s[p].view(np.uint32)
+
+
+def test_append_at_bench_size_every_page():
+    """The append at the benchmark's size (8 sequences x 65536 new keys x 128 dims into 8193
+    permuted pages, the launch bench.py times), then a decode step of 32 sequences appending one
+    key each to pages that hold keys: every page's codes and scale bit-exact against the oracle."""
+    B, T, D = 8, 65536, 128
+    P = B * T // 64 + 1
+    gen = torch.Generator(device=DEV).manual_seed(17)
+    perm = torch.randperm(P, device=DEV, generator=gen).to(torch.int32)
+    bt = perm[:B * T // 64].view(B, T // 64).contiguous()
+    sl = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    src = (torch.randn(B, T, D, device=DEV, generator=gen) / np.sqrt(D)).to(torch.bfloat16)
+    kc = torch.full((P, 64, D), 0x7F, dtype=torch.uint8, device=DEV)
+    ks = torch.full((P,), 3.0, dtype=torch.float32, device=DEV)
+    kc0, ks0 = to_np(kc).copy(), to_np(ks).copy()
+    print("[case] fp8 page append bench size", flush=True)
+    dsa.dsa_indexer_cache_append_fp8(src, kc, ks, bt, sl, max_seq_len=T, num_pages=P)
+    torch.cuda.synchronize()
+    btn = bt.cpu().numpy()
+    ref_c, ref_s = indexer_cache_append_fp8_ref(src.float().cpu().numpy(), kc0, ks0, btn, np.full(B, T), T)
+    np.testing.assert_array_equal(to_np(ks).view(np.uint32), ref_s.view(np.uint32))
+    np.testing.assert_array_equal(to_np(kc), ref_c)
+    # decode step: sequence b holds lens[b] - 1 keys and appends one (the bench's decode leg)
+    Bd = 32
+    lens = np.array([1000 + 197 * b for b in range(Bd)], np.int32)
+    bt_d = perm[:Bd * 112].view(Bd, 112).contiguous()
+    new = (torch.randn(Bd, 1, D, device=DEV, generator=gen) / np.sqrt(D) * 3).to(torch.bfloat16)
+    print("[case] fp8 page append bench decode step", flush=True)
+    dsa.dsa_indexer_cache_append_fp8(new, kc, ks, bt_d, up(lens), max_seq_len=112 * 64, num_pages=P)
+    torch.cuda.synchronize()
+    ref_c, ref_s = indexer_cache_append_fp8_ref(new.float().cpu().numpy(), ref_c, ref_s, bt_d.cpu().numpy(), lens, 1)
+    np.testing.assert_array_equal(to_np(ks).view(np.uint32), ref_s.view(np.uint32))
+    np.testing.assert_array_equal(to_np(kc), ref_c)
