@@ -1344,8 +1344,9 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.x, seg = blockIdx.y;
   const int b = row / a.T, t = row % a.T;
-  // timeline points 3..7 of the row's first segment (the score kernel uses 0..2)
-#define SEL_STAMP(point) do { if (seg == 0) DSA_STAMP(point); } while (0)
+  // timeline points 3 and 4 from the row's first segment, 5..7 from the segment that finishes the
+  // row (the score kernel uses 0..2)
+#define SEL_STAMP(point) do { if (seg == 0 || (point) >= 5) DSA_STAMP(point); } while (0)
   SEL_STAMP(3);
   // The row histogram's bins of this thread go out first, beside the sequence length and poison
   // loads they would otherwise wait behind.

@@ -37,11 +37,18 @@ def _pcts(x):
     return [np.percentile(x, p) for p in (0, 10, 50, 90, 100)]
 
 
-def _table(title, names, cols, rows_us):
-    out = [f"**{title}** ({rows_us.shape[0]} workgroups), us from the first workgroup start:", "",
-           "| point | min | p10 | p50 | p90 | max |", "|---|---|---|---|---|---|"]
-    for name, c in zip(names, cols):
-        out.append(f"| {name} | " + " | ".join(f"{v:.1f}" for v in _pcts(rows_us[:, c])) + " |")
+def _table(title, names, raw, t0):
+    """raw: [workgroups, points] counter stamps (0 = the workgroup did not reach that point)."""
+    n = raw.shape[0]
+    out = [f"**{title}** ({n} workgroups), us from the first workgroup start:", "",
+           "| point | workgroups | min | p10 | p50 | p90 | max |", "|---|---|---|---|---|---|---|"]
+    for name, c in zip(names, range(raw.shape[1])):
+        hit = raw[:, c] != 0
+        if not hit.any():
+            out.append(f"| {name} | 0 | - | - | - | - | - |")
+            continue
+        us = (raw[hit, c].astype(np.int64) - int(t0)) * TICK_US
+        out.append(f"| {name} | {int(hit.sum())} | " + " | ".join(f"{v:.1f}" for v in _pcts(us)) + " |")
     return out
 
 
@@ -120,27 +127,25 @@ def main():
     wi = np.nonzero(ti[:, 0])[0]
     if wi.size:
         t0 = ti[wi, 0].min()
+        lines += _table("li_score_decode", DECODE_POINTS, ti[wi, :3], t0)
         r = (ti[wi, :3].astype(np.int64) - int(t0)) * TICK_US
-        lines += _table("li_score_decode", DECODE_POINTS, range(3), r)
         xcd = [f"{r[wi % 8 == x, 2].mean():.1f}" for x in range(8)]
         lines += ["", "Streaming done, mean per XCD 0..7: " + ", ".join(xcd) + " us", ""]
         rows = spec.B * spec.T
         sel = ti[:rows]
         if (sel[:, 3] != 0).all():
-            rs = (sel[:, 3:8].astype(np.int64) - int(t0)) * TICK_US
-            lines += _table("li_select (first segment of each row)",
-                            ["start", "digit-0 bin found (row histogram read)", "candidates collected",
-                             "threshold resolved", "indices written"], range(5), rs)
+            lines += _table("li_select (one row per line of stamps)",
+                            ["start (first segment)", "digit-0 bin found (first segment)",
+                             "candidates collected (segment finishing the row)",
+                             "threshold resolved", "indices written"], sel[:, 3:8], t0)
             lines += [""]
     ws = np.nonzero(ta[:, 0])[0]
     wc = np.nonzero(ta[:, 4])[0]
     if ws.size:
         t0 = min(ta[ws, 0].min(), ta[wc, 4].min() if wc.size else ta[ws, 0].min())
-        r = (ta[ws, :4].astype(np.int64) - int(t0)) * TICK_US
-        lines += _table("sfa_pipe split workgroups", SPLIT_POINTS, range(4), r)
+        lines += _table("sfa_pipe split workgroups", SPLIT_POINTS, ta[ws, :4], t0)
         if wc.size:
-            rc = (ta[wc, 4:7].astype(np.int64) - int(t0)) * TICK_US
-            lines += [""] + _table("sfa_pipe combine workgroups", COMBINE_POINTS, range(3), rc)
+            lines += [""] + _table("sfa_pipe combine workgroups", COMBINE_POINTS, ta[wc, 4:7], t0)
         lines += [""]
     print("\n".join(lines))
 
