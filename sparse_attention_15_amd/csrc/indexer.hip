@@ -1190,41 +1190,57 @@ struct SelectArgs {
 };
 
 constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kCandCap = 8192;                       // candidates staged in LDS
+constexpr int kSelThreadsShort = 256;                // launches whose rows are all <= kShortRow keys
+constexpr int kCandCap = 8192;                       // candidates per row in the global lists
 constexpr int kSelVec = 4;                           // 16-byte loads per thread per scan step
 constexpr int kSelPer = 4 * kSelVec;                 // consecutive keys per thread per step (16)
-constexpr int kSelChunk = kSelThreads * kSelPer;     // keys per scan step (16384)
 constexpr int kMaxSeg = 32;                          // workgroups per row at most
-constexpr int kMapWords = 2 * kSelThreads;           // bitmap words per emit chunk
-constexpr int kMapBits = 32 * kMapWords;             // positions per emit chunk (65536)
+
+// Workgroup shape of the select: NT threads, kCand candidates staged in LDS, scan steps of 16 NT
+// keys, bitmap chunks of 64 NT positions.  1024 threads for long rows (steps of 16384 keys,
+// chunks of 65536 positions); 256 threads when every row of the launch has at most kShortRow
+// keys: 40 KiB of LDS, so four rows share a CU.
+template <int NT>
+struct SelShape {
+  static constexpr int kWaves = NT / 64;
+  // 2040 (not 2048) candidates keep the short shape's LDS within a quarter of the CU's 160 KiB
+  static constexpr int kCand = NT == kSelThreads ? 8192 : 2040;
+  static constexpr int kChunk = NT * kSelPer;        // keys per scan step
+  static constexpr int kMapW = 2 * NT;               // bitmap words per emit chunk
+  static constexpr int kMapB = 32 * kMapW;           // positions per emit chunk
+};
+constexpr int kShortRow = 2 * SelShape<kSelThreadsShort>::kChunk;   // 8192 keys: two steps, one segment
 
 // Keys per segment: whole scan steps, at most kMaxSeg segments.  A row of up to two steps stays in
 // one workgroup (its second, prefetched step costs less than the publish-and-reload round trip
 // between the workgroups of a split row); longer rows take one step per segment.
+template <int NT = kSelThreads>
 __host__ __device__ __forceinline__ int seg_len_of(int n) {
-  const int steps = (n + kSelChunk - 1) / kSelChunk;
-  if (steps <= 2) return 2 * kSelChunk;
-  return kSelChunk * ((steps + kMaxSeg - 1) / kMaxSeg);
+  constexpr int kChunk = SelShape<NT>::kChunk;
+  const int steps = (n + kChunk - 1) / kChunk;
+  if (steps <= 2) return 2 * kChunk;
+  return kChunk * ((steps + kMaxSeg - 1) / kMaxSeg);
 }
 
+template <int NT>
 struct SelScratch {
-  uint32_t wave_tot[2][kSelWaves];   // per-wave totals, alternating halves between scans
+  uint32_t wave_tot[2][NT / 64];     // per-wave totals, alternating halves between scans
   uint32_t res[3];                   // bin search result: bin, count above it, count in it
   uint32_t cursor;                   // LDS list fill: gt count | candidate count << 16
   uint32_t pub[3];                   // global list offsets of this segment, segments done before
 };
 
-// Exclusive prefix sum over the 1024-thread workgroup with a single barrier: wave totals go to
-// alternating halves of `wave_tot`, so the next scan never overwrites totals still being read.
-__device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch& S, uint32_t& phase, uint32_t& total) {
+// Exclusive prefix sum over the workgroup with a single barrier: wave totals go to alternating
+// halves of `wave_tot`, so the next scan never overwrites totals still being read.
+template <int NT>
+__device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch<NT>& S, uint32_t& phase, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) S.wave_tot[phase][wid] = x;
   lds_barrier();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     const uint32_t t = S.wave_tot[phase][i];
     pre += i < wid ? t : 0u;
     tot += t;
@@ -1238,18 +1254,18 @@ __device__ __forceinline__ uint32_t sel_scan(uint32_t v, SelScratch& S, uint32_t
 // returns it with the count in higher bins (`above`) and in the bin itself (`count`).  1 <= need
 // <= total is required.  Thread 0 owns the highest bins.
 // sel_find_bin_pre takes this thread's PER bins already loaded (h[i] = bin hi - 1 - i).
-template <int NB>
-__device__ __forceinline__ uint32_t sel_find_bin_pre(const uint32_t (&h)[NB / kSelThreads], uint32_t need,
-                                                     SelScratch& S, uint32_t& phase, uint32_t& above,
+template <int NB, int NT>
+__device__ __forceinline__ uint32_t sel_find_bin_pre(const uint32_t (&h)[NB / NT], uint32_t need,
+                                                     SelScratch<NT>& S, uint32_t& phase, uint32_t& above,
                                                      uint32_t& count) {
-  constexpr int PER = NB / kSelThreads;
-  static_assert(PER >= 1 && NB % kSelThreads == 0, "bins per thread");
+  constexpr int PER = NB / NT;
+  static_assert(PER >= 1 && NB % NT == 0, "bins per thread");
   const int hi = NB - PER * (int)threadIdx.x;
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) mine += h[i];
   uint32_t tot;
-  const uint32_t pre = sel_scan(mine, S, phase, tot);
+  const uint32_t pre = sel_scan<NT>(mine, S, phase, tot);
   if (pre < need && pre + mine >= need) {
     uint32_t run = pre;
 #pragma unroll
@@ -1263,15 +1279,15 @@ __device__ __forceinline__ uint32_t sel_find_bin_pre(const uint32_t (&h)[NB / kS
   count = S.res[2];
   return S.res[0];
 }
-template <int NB>
-__device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t need, SelScratch& S,
+template <int NB, int NT>
+__device__ __forceinline__ uint32_t sel_find_bin(const uint32_t* hist, uint32_t need, SelScratch<NT>& S,
                                                  uint32_t& phase, uint32_t& above, uint32_t& count) {
-  constexpr int PER = NB / kSelThreads;
+  constexpr int PER = NB / NT;
   const int hi = NB - PER * (int)threadIdx.x;
   uint32_t h[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) h[i] = hist[hi - 1 - i];
-  return sel_find_bin_pre<NB>(h, need, S, phase, above, count);
+  return sel_find_bin_pre<NB, NT>(h, need, S, phase, above, count);
 }
 
 // Radix digits of a key: digit 0 = bits 31..21 (histogrammed by the score kernel), digit 1 =
@@ -1284,14 +1300,15 @@ __device__ __forceinline__ int unresolved_bits(int resolved) {
 // `tie` (taken while fewer than `need` ties of the row were seen before).  Thread t holds the two
 // bitmap words of positions base + 64t .. base + 64t + 63.  run_out / run_tie carry the row's
 // emitted count and tie count across chunks.
+template <int NT>
 __device__ __forceinline__ void emit_words(const uint32_t (&sel)[2], const uint32_t (&tie)[2], int base,
-                                           uint32_t need, int K, int32_t* out, SelScratch& S,
+                                           uint32_t need, int K, int32_t* out, SelScratch<NT>& S,
                                            uint32_t& phase, uint32_t& run_out, uint32_t& run_tie) {
   const uint32_t cs = __popc(sel[0]) + __popc(sel[1]);
   const uint32_t ct = __popc(tie[0]) + __popc(tie[1]);
   uint32_t tot;
   // taken positions per chunk < K <= 2048 fit 12 bits; ties per chunk <= 65536 fit the other 20
-  const uint32_t pre = sel_scan(cs | (ct << 12), S, phase, tot);
+  const uint32_t pre = sel_scan<NT>(cs | (ct << 12), S, phase, tot);
   uint32_t rank = run_tie + (pre >> 12);
   uint32_t o = run_out + (pre & 0xFFFu) + (min(rank, need) - min(run_tie, need));
   const int p0 = base + 64 * (int)threadIdx.x;
@@ -1317,9 +1334,10 @@ __device__ __forceinline__ void emit_words(const uint32_t (&sel)[2], const uint3
 // whose score kernel then finds them clear and skips its own clearing stores.  Called once every
 // reader of this call is done with them.  Plain stores: the next call's kernels run after this
 // launch has ended, when they are visible to every workgroup.
+template <int NT>
 __device__ __forceinline__ void sel_leave_clear(const SelectArgs& a, int row) {
   u32x4* h = reinterpret_cast<u32x4*>(a.hist + (size_t)row * kBins);
-  for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) h[i] = u32x4{0u, 0u, 0u, 0u};
+  for (int i = threadIdx.x; i < kBins / 4; i += NT) h[i] = u32x4{0u, 0u, 0u, 0u};
   if (threadIdx.x == 0) *reinterpret_cast<u32x4*>(a.ctl + (size_t)row * kCtl) = u32x4{0u, 0u, 0u, 0u};
 }
 
@@ -1332,15 +1350,17 @@ __device__ __forceinline__ void sel_leave_clear(const SelectArgs& a, int row) {
 // through per-chunk bitmaps.  A prefix range too big for LDS falls back to one workgroup for the
 // row, which resolves more digits with histogram passes over the row, and, if even the exact key
 // theta has too many ties, emits straight from the keys.
-__global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
-  constexpr int NT = kSelThreads;
+template <int NT>
+__global__ __launch_bounds__(NT) void li_select(SelectArgs a) {
+  using Sh = SelShape<NT>;
+  constexpr int kCand = Sh::kCand, kChunk = Sh::kChunk, kMapW = Sh::kMapW, kMapB = Sh::kMapB;
   __shared__ uint32_t h1[kBins];           // digit-1 histogram
   __shared__ uint32_t h2[1024];            // digit-2 histogram
   __shared__ int32_t gt_list[DSA_MAX_TOP_K];
-  __shared__ uint32_t c_key[kCandCap];
-  __shared__ int32_t c_pos[kCandCap];
-  __shared__ uint32_t bm_sel[kMapWords], bm_tie[kMapWords];
-  __shared__ SelScratch S;
+  __shared__ uint32_t c_key[kCand];
+  __shared__ int32_t c_pos[kCand];
+  __shared__ uint32_t bm_sel[kMapW], bm_tie[kMapW];
+  __shared__ SelScratch<NT> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int row = blockIdx.x, seg = blockIdx.y;
   const int b = row / a.T, t = row % a.T;
@@ -1350,7 +1370,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   SEL_STAMP(3);
   // The row histogram's bins of this thread go out first, beside the sequence length and poison
   // loads they would otherwise wait behind.
-  constexpr int kHistPer = kBins / kSelThreads;
+  constexpr int kHistPer = kBins / NT;
   uint32_t hist0[kHistPer];
 #pragma unroll
   for (int i = 0; i < kHistPer; ++i)
@@ -1373,14 +1393,14 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       for (int j = tid; j < a.K; j += NT) out[j] = -1;
     return;
   }
-  const int seg_len = seg_len_of(n);
+  const int seg_len = seg_len_of<NT>(n);
   int nseg = (n + seg_len - 1) / seg_len;
   if (seg >= nseg) return;
   int lo = seg * seg_len, hi = min(n, lo + seg_len);
   const uint32_t* keys = a.keys + (size_t)row * a.row_stride;
   uint32_t phase = 0;
 
-  // Pass over [lo, hi) in steps of kSelChunk keys: per_step(v, s0) gets this thread's kSelPer
+  // Pass over [lo, hi) in steps of kChunk keys: per_step(v, s0) gets this thread's kSelPer
   // consecutive keys from position s0 on (entries at positions >= hi are zero or stale and must
   // be masked).  The next step loads while the current one is processed.  A 16-byte load is
   // issued only if it starts below hi <= n; the row stride is a multiple of 4, so none leaves the
@@ -1398,9 +1418,9 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
     u32x4 nxt[kSelVec];
 #pragma unroll
     for (int u = 0; u < kSelVec; ++u) nxt[u] = u32x4{0u, 0u, 0u, 0u};
-    for (int base = lo; base < hi; base += kSelChunk) {
+    for (int base = lo; base < hi; base += kChunk) {
       const int s0 = base + tid * kSelPer;
-      if (base + kSelChunk < hi) load_step(nxt, s0 + kSelChunk);
+      if (base + kChunk < hi) load_step(nxt, s0 + kChunk);
       per_step(cur, s0);
 #pragma unroll
       for (int u = 0; u < kSelVec; ++u) cur[u] = nxt[u];
@@ -1409,22 +1429,22 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   auto key_of = [](const u32x4 (&v)[kSelVec], int j) -> uint32_t { return v[j >> 2][j & 3]; };
 
   for (int i = tid; i < kBins; i += NT) h1[i] = 0u;
-  h2[tid] = 0u;
+  for (int i = tid; i < 1024; i += NT) h2[i] = 0u;
   if (tid == 0) S.cursor = 0u;
   uint32_t above, C;
-  uint32_t prefix = sel_find_bin_pre<kBins>(hist0, (uint32_t)a.K, S, phase, above, C);
+  uint32_t prefix = sel_find_bin_pre<kBins, NT>(hist0, (uint32_t)a.K, S, phase, above, C);
   SEL_STAMP(4);
-  if (nseg == 1) sel_leave_clear(a, row);   // the only reader has read it (the scan's barrier)
+  if (nseg == 1) sel_leave_clear<NT>(a, row);   // the only reader has read it (the scan's barrier)
   uint32_t need = (uint32_t)a.K - above;  // keys still to take from the current prefix range
   const uint32_t G = above;               // keys above the digit-0 range
   int resolved = 1;
   uint32_t G2 = G;                        // keys above the final prefix range (fallback only)
 
-  if (C > (uint32_t)kCandCap) {
+  if (C > (uint32_t)kCand) {
     // one workgroup takes the whole row; more digits from histogram passes over it
     if (seg != 0) return;
     nseg = 1; lo = 0; hi = n;
-    while (C > (uint32_t)kCandCap && resolved < 3) {
+    while (C > (uint32_t)kCand && resolved < 3) {
       const int sh = unresolved_bits(resolved);
       uint32_t* hh = resolved == 1 ? h1 : h2;
       for (int s = tid * 4; s < n; s += NT * 4) {
@@ -1435,8 +1455,8 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
             atomicAdd(&hh[resolved == 1 ? ((v[j] >> 10) & 2047u) : (v[j] & 1023u)], 1u);
       }
       lds_barrier();
-      const uint32_t d = resolved == 1 ? sel_find_bin<kBins>(hh, need, S, phase, above, C)
-                                       : sel_find_bin<1024>(hh, need, S, phase, above, C);
+      const uint32_t d = resolved == 1 ? sel_find_bin<kBins, NT>(hh, need, S, phase, above, C)
+                                       : sel_find_bin<1024, NT>(hh, need, S, phase, above, C);
       need -= above;
       G2 += above;
       prefix = (prefix << (resolved == 1 ? 11 : 10)) | d;
@@ -1445,7 +1465,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
   }
 
   uint32_t run_out = 0, run_tie = 0;
-  if (C <= (uint32_t)kCandCap) {
+  if (C <= (uint32_t)kCand) {
     const int shift = unresolved_bits(resolved);
     const uint32_t hi_key = shift ? ((prefix << shift) | ((1u << shift) - 1u)) : prefix;
     // collect positions above the prefix range and candidates inside it (any order); each wave
@@ -1475,7 +1495,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
 #pragma unroll
       for (int j = 0; j < kSelPer; ++j)
         if ((cm >> j) & 1u) {
-          if (oc < (uint32_t)kCandCap) { c_key[oc] = key_of(v, j); c_pos[oc] = s0 + j; }
+          if (oc < (uint32_t)kCand) { c_key[oc] = key_of(v, j); c_pos[oc] = s0 + j; }
           ++oc;
         }
     });
@@ -1483,7 +1503,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
     if (nseg > 1) {
       // publish this segment's lists; the last segment to finish carries on with the row
       const uint32_t cnt = S.cursor;
-      const uint32_t ng = min(cnt & 0xFFFFu, (uint32_t)DSA_MAX_TOP_K), nc = min(cnt >> 16, (uint32_t)kCandCap);
+      const uint32_t ng = min(cnt & 0xFFFFu, (uint32_t)DSA_MAX_TOP_K), nc = min(cnt >> 16, (uint32_t)kCand);
       uint32_t* ctl = a.ctl + (size_t)row * kCtl;
       if (tid == 0) {
         S.pub[0] = atomicAdd(&ctl[1], ng);
@@ -1512,7 +1532,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       lds_barrier();
       if (S.pub[2] != (uint32_t)(nseg - 1)) return;
       // every segment has read the histogram and updated the counters
-      sel_leave_clear(a, row);
+      sel_leave_clear<NT>(a, row);
       for (uint32_t i = tid; i < G; i += NT)
         gt_list[i] = __hip_atomic_load(&g_gt[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (uint32_t i = tid; i < C; i += NT) {
@@ -1530,7 +1550,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       for (int i = tid; i < nc; i += NT) atomicAdd(&h1[(c_key[i] >> 10) & 2047u], 1u);
       lds_barrier();
       uint32_t cnt;
-      const uint32_t d = sel_find_bin<kBins>(h1, need, S, phase, above, cnt);
+      const uint32_t d = sel_find_bin<kBins, NT>(h1, need, S, phase, above, cnt);
       need -= above;
       prefix = (prefix << 11) | d;
       resolved = 2;
@@ -1542,14 +1562,14 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       }
       lds_barrier();
       uint32_t cnt;
-      const uint32_t d = sel_find_bin<1024>(h2, need, S, phase, above, cnt);
+      const uint32_t d = sel_find_bin<1024, NT>(h2, need, S, phase, above, cnt);
       need -= above;
       prefix = (prefix << 10) | d;
     }
     const uint32_t theta = prefix;       // the exact threshold key; `need` of its ties are kept
     SEL_STAMP(6);
-    for (int c0 = 0; c0 < n; c0 += kMapBits) {
-      const int c1 = min(n, c0 + kMapBits);
+    for (int c0 = 0; c0 < n; c0 += kMapB) {
+      const int c1 = min(n, c0 + kMapB);
       bm_sel[2 * tid] = 0u; bm_sel[2 * tid + 1] = 0u;
       bm_tie[2 * tid] = 0u; bm_tie[2 * tid + 1] = 0u;
       lds_barrier();
@@ -1566,13 +1586,13 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
       lds_barrier();
       const uint32_t sw[2] = {bm_sel[2 * tid], bm_sel[2 * tid + 1]};
       const uint32_t tw[2] = {bm_tie[2 * tid], bm_tie[2 * tid + 1]};
-      emit_words(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
+      emit_words<NT>(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
     }
   } else {
     // theta is exact (all digits resolved) and its ties exceed the staging space: the bitmap
     // words come straight from the keys
     const uint32_t theta = prefix;
-    for (int c0 = 0; c0 < n; c0 += kMapBits) {
+    for (int c0 = 0; c0 < n; c0 += kMapB) {
       uint32_t sw[2] = {0u, 0u}, tw[2] = {0u, 0u};
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
@@ -1588,7 +1608,7 @@ __global__ __launch_bounds__(1024) void li_select(SelectArgs a) {
           }
         }
       }
-      emit_words(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
+      emit_words<NT>(sw, tw, c0, need, a.K, out, S, phase, run_out, run_tie);
     }
   }
   for (int j = (int)run_out + tid; j < a.K; j += NT) out[j] = -1;
@@ -1773,7 +1793,11 @@ hipError_t launch_indexer(const IndexerArgs& a, const IndexerPlan& p, hipStream_
   sa.T = a.T; sa.K = a.top_k; sa.row_stride = p.row_stride; sa.max_seq_len = a.max_seq_len;
   {
     LaunchScope ls("li_select", st);
-    hipLaunchKernelGGL(li_select, dim3(p.rows, p.n_seg), dim3(kSelThreads), 0, st, sa);
+    // rows of at most kShortRow keys (one segment each): the 256-thread shape, four rows per CU
+    if (a.max_seq_len <= kShortRow)
+      hipLaunchKernelGGL(li_select<kSelThreadsShort>, dim3(p.rows, 1), dim3(kSelThreadsShort), 0, st, sa);
+    else
+      hipLaunchKernelGGL(li_select<kSelThreads>, dim3(p.rows, p.n_seg), dim3(kSelThreads), 0, st, sa);
   }
   return hipGetLastError();
 }
