@@ -10,8 +10,9 @@ import pytest
 import torch
 
 import oracle
+import sparse_attention_15_amd as dsa
 import workloads as W
-from tests._gpu import Dev, check_attn, check_indices_band, oracle_args, to_np
+from tests._gpu import Dev, check_attn, check_indices_band, oracle_args, to_np, up
 
 pytestmark = pytest.mark.gpu
 
@@ -128,6 +129,35 @@ def test_select_crowded_threshold_exact(values, lens, expect):
     pops = _threshold_populations(extra, [(b, 0) for b in range(len(lens))])
     assert all(f(p) for f, p in zip(expect, pops)), pops
     assert np.array_equal(idx, ref)
+
+
+# The same floods in launches whose rows all have at most 8192 keys, which run the 256-thread
+# select (2040 candidates staged in LDS): narrow and ties take one extra histogram pass, ties2
+# keeps more than 2040 exact ties and is emitted straight from the keys.
+@pytest.mark.parametrize("values,lens,expect", [
+    ("narrow", (8192, 5000), [lambda p: p[0] > 2040 and p[1] <= 2040] * 2),
+    ("ties", (8192, 7000), [lambda p: p[0] > 2040 and p[1] <= 2040] * 2),
+    ("ties2", (8192, 6000), [lambda p: p[2] > 2040] * 2),
+])
+def test_select_crowded_threshold_short_rows_exact(values, lens, expect):
+    test_select_crowded_threshold_exact(values, lens, expect)
+
+
+def test_select_shapes_agree_at_the_boundary():
+    """Rows of up to 8192 keys give the same indices whether the launch runs the 256-thread select
+    (max_seq_len 8192) or the 1024-thread one (the same rows with a block table one page wider and
+    max_seq_len 8256), and both equal the oracle's."""
+    spec = W.custom("grid8_boundary", 3, 1, (8192, 5000, 8191), 64, 128, 2048, 16, values="grid8")
+    print(f"[case] {spec.name}", flush=True)
+    c = W.make_case(spec)
+    d = Dev(c)
+    short = to_np(d.indexer())
+    wide = np.concatenate([c.block_table, c.block_table[:, :1]], axis=1)
+    long_ = to_np(dsa.dsa_indexer_topk(d.q_idx, None, d.w, d.k, None, up(wide), d.sl, T=1, top_k=spec.K,
+                                       max_seq_len=8256, num_pages=c.num_pages))
+    ref = oracle.indexer_topk_ref(**oracle_args(c), T=1, K=spec.K, dtype="bf16")
+    assert np.array_equal(short, ref)
+    assert np.array_equal(long_, ref)
 
 
 # Rows longer than one select segment (two scan steps of 16384 keys for rows up to 32768 keys, one
