@@ -89,7 +89,8 @@ def prefill(spec):
 MFMA_PEAK = {"bf16": 2500.0, "fp8": 5000.0}
 
 
-KERNEL_SOURCE = {"li_score": "indexer.hip", "sfa_main": "sfa.hip"}
+KERNEL_SOURCE = {"li_score": "indexer.hip", "sfa_main": "sfa.hip", "fp8_page_append": "quant.hip",
+                 "mx_quant_rows (paged)": "quant.hip"}
 
 
 def recorded_traffic(kernel, workload):
@@ -558,7 +559,8 @@ def bench_append(args, dev, dsa):
         "config": {"workload": f"cache append B={B} T={T} dim={D}, page 64, permuted pages",
                    "rotation_copies": R},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("mx_quant_rows (paged)", "append"),
                      "kernel": "mx_quant_rows (paged)", "algorithmic_bytes_per_launch": nbytes},
         "cpu_baseline": cpu}), flush=True)
 
@@ -643,7 +645,8 @@ def bench_append_fp8(args, dev, dsa):
         "config": {"workload": f"cache append B={B} T={T} dim={D}, page 64, permuted fresh pages",
                    "rotation_copies": R},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("fp8_page_append", "append-fp8"),
                      "kernel": "fp8_page_append", "algorithmic_bytes_per_launch": nbytes},
         "decode_step": {"batch": Bd, "T": 1, "us_per_call": round(ms_d * 1e3, 2)},
         "cpu_baseline": cpu}), flush=True)
