@@ -218,3 +218,26 @@ def test_latent_fp8_append_bench_size_sampled():
         p, slot = btn[b, t // 64], t % 64
         np.testing.assert_array_equal(kcn[p, slot], c_ref, err_msg=f"row {(b, t)}")
         np.testing.assert_array_equal(ksn[p, slot].view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_cache_append_bench_size_every_row():
+    """The MXFP8 append at the benchmark's size (8 sequences x 65536 new keys x 128 dims into 8193
+    permuted pages, the launch bench.py times): every code and scale byte against the oracle."""
+    B, T, D = 8, 65536, 128
+    P = B * T // 64 + 1
+    gen = torch.Generator(device=DEV).manual_seed(15)
+    perm = torch.randperm(P, device=DEV, generator=gen).to(torch.int32)
+    bt = perm[:B * T // 64].view(B, T // 64).contiguous()
+    sl = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    src = torch.randn(B, T, D, device=DEV, generator=gen).to(torch.bfloat16)
+    kc = torch.zeros(P, 64, D, dtype=torch.uint8, device=DEV)
+    ks = torch.zeros(P, 64, D // 32, dtype=torch.uint8, device=DEV)
+    print("[case] mxfp8 append bench size", flush=True)
+    dsa.dsa_indexer_cache_append(src, kc, ks, bt, sl, max_seq_len=T, num_pages=P)
+    torch.cuda.synchronize()
+    ref_c, ref_s = mxfp8_quantize_rows(src.float().cpu().numpy().astype(np.float64))
+    pages = bt.cpu().numpy()                       # [B, T / 64]: sequence b's token t at page t // 64
+    got_c = to_np(kc)[pages].reshape(B, T, D)
+    got_s = to_np(ks)[pages].reshape(B, T, D // 32)
+    np.testing.assert_array_equal(got_s, ref_s)
+    np.testing.assert_array_equal(got_c, ref_c)
