@@ -176,6 +176,15 @@ def test_fp8_grid_exact(T):
     _run(spec, exact=True)
 
 
+@pytest.mark.parametrize("HI,DI,T", [(8, 64, 1), (16, 128, 4), (32, 64, 2), (64, 64, 4), (8, 128, 3)])
+def test_fp8_grid_other_shapes_exact(HI, DI, T):
+    """The per-page fp8 indexer at other head counts and dims (decode, two rows, verify), on the
+    exact fp8 grid: the indices equal the oracle's bit for bit."""
+    spec = W.custom(f"fp8grid_{HI}x{DI}", 3, T, (2500, 777, 4100), HI, DI, 300, 16, idx_dtype="fp8",
+                    values="fp8grid")
+    _run(spec, exact=True, check_sfa=False)
+
+
 @pytest.mark.parametrize("HI,DI,K", [(8, 64, 256), (16, 128, 100), (32, 64, 512), (64, 64, 1)])
 def test_other_indexer_shapes_exact(HI, DI, K):
     spec = W.custom(f"grid_{HI}x{DI}", 2, 2, (1500, 777), HI, DI, K, 16, values="grid8")
