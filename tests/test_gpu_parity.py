@@ -292,3 +292,24 @@ def test_attn_random_index_sets_sharp(B, K):
     o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx,
                                           1 / 24, rows=rows)
     check_attn(to_np(out), to_np(lse), o_ref, l_ref, rows=rows)
+
+
+@pytest.mark.parametrize("H", [32, 48, 64, 96])
+def test_attn_head_counts(H):
+    """Head counts that give one wave per workgroup (32), two (48: the second group half full; 64)
+    and two head chunks of two groups with the last one empty (96), on random index sets with
+    several splits per row."""
+    rng = np.random.default_rng(H)
+    B, K = 3, 700
+    lens = (K + 10, 2500, 4100)
+    c = W.make_case(W.custom(f"attn_h{H}", B, 1, lens, 8, 64, K, H, values="sharp", sharp_c=1.0))
+    idx = np.full((B, 1, K), -1, np.int32)
+    for b in range(B):
+        m = int(rng.integers(1, K + 1))
+        idx[b, 0, :m] = np.sort(rng.choice(lens[b], m, replace=False))
+    print(f"[case] attention heads {H}", flush=True)
+    d = Dev(c)
+    out, lse = d.attn(idx)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.sparse_attn_ref(c.q_attn, c.kv_cache, c.block_table, c.seq_lens, idx, 1 / 24)
+    check_attn(to_np(out), to_np(lse), o_ref, l_ref)
