@@ -169,6 +169,14 @@ def test_multi_segment_rows_exact(T, lens):
     _run(spec, exact=True, check_sfa=False)
 
 
+def test_maximum_length_rows_exact():
+    """A row at the library's maximum length (2^20 keys: the select's 32 segments of two scan steps
+    each, 16 bitmap chunks) beside a 300001-key row, on the exact integer grid: the indices equal
+    the oracle's, and the attention over them matches."""
+    spec = W.custom("maxlen", 2, 1, (1 << 20, 300001), 8, 64, 2048, 16, values="grid8")
+    _run(spec, exact=True)
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_fp8_grid_exact(T):
     spec = W.custom("fp8grid", 2, T, (2500, 4100), 64, 128, 2048, 128, idx_dtype="fp8",
