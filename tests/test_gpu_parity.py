@@ -169,11 +169,12 @@ def test_multi_segment_rows_exact(T, lens):
     _run(spec, exact=True, check_sfa=False)
 
 
-def test_maximum_length_rows_exact():
-    """A row at the library's maximum length (2^20 keys: the select's 32 segments of two scan steps
-    each, 16 bitmap chunks) beside a 300001-key row, on the exact integer grid: the indices equal
-    the oracle's, and the attention over them matches."""
-    spec = W.custom("maxlen", 2, 1, (1 << 20, 300001), 8, 64, 2048, 16, values="grid8")
+@pytest.mark.parametrize("T", [1, 4])
+def test_maximum_length_rows_exact(T):
+    """A sequence at the library's maximum length (2^20 keys: the select's 32 segments of two scan
+    steps each, 16 bitmap chunks) beside a 300001-key one, decode and verify, on the exact integer
+    grid: the indices equal the oracle's, and the attention over them matches."""
+    spec = W.custom("maxlen", 2, T, (1 << 20, 300001), 8, 64, 2048, 16, values="grid8")
     _run(spec, exact=True)
 
 
