@@ -169,12 +169,13 @@ def test_multi_segment_rows_exact(T, lens):
     _run(spec, exact=True, check_sfa=False)
 
 
-@pytest.mark.parametrize("T", [1, 4])
-def test_maximum_length_rows_exact(T):
+@pytest.mark.parametrize("T,fmt", [(1, "bf16"), (4, "bf16"), (1, "fp8"), (1, "mxfp8")])
+def test_maximum_length_rows_exact(T, fmt):
     """A sequence at the library's maximum length (2^20 keys: the select's 32 segments of two scan
-    steps each, 16 bitmap chunks) beside a 300001-key one, decode and verify, on the exact integer
-    grid: the indices equal the oracle's, and the attention over them matches."""
-    spec = W.custom("maxlen", 2, T, (1 << 20, 300001), 8, 64, 2048, 16, values="grid8")
+    steps each, 16 bitmap chunks) beside a 300001-key one, decode and verify, each indexer format
+    on its exact grid: the indices equal the oracle's, and the attention over them matches."""
+    values = {"bf16": "grid8", "fp8": "fp8grid", "mxfp8": "mxgrid"}[fmt]
+    spec = W.custom("maxlen", 2, T, (1 << 20, 300001), 8, 64, 2048, 16, idx_dtype=fmt, values=values)
     _run(spec, exact=True)
 
 
