@@ -1173,8 +1173,8 @@ __global__ __launch_bounds__(TQ == 1 ? 256 : 512, TQ == 1 ? 2 : 1) void li_score
 }
 
 // ------------------------------------------------------------------------------------------------
-// Top-K selection.  Workgroups of 1024 threads; a row of n keys is cut into segments of
-// seg_len(n) keys, one workgroup each.
+// Top-K selection.  Workgroups of 1024 threads (256 when every row of the launch is short, see
+// SelShape); a row of n keys is cut into segments of seg_len(n) keys, one workgroup each.
 struct SelectArgs {
   const uint32_t* keys;     // [rows, row_stride] order-preserving score keys
   uint32_t* hist;           // [rows, kBins] histogram of key bits 31..21 (left zero once read)
@@ -1202,7 +1202,6 @@ constexpr int kMaxSeg = 32;                          // workgroups per row at mo
 // keys: 40 KiB of LDS, so four rows share a CU.
 template <int NT>
 struct SelShape {
-  static constexpr int kWaves = NT / 64;
   // 2040 (not 2048) candidates keep the short shape's LDS within a quarter of the CU's 160 KiB
   static constexpr int kCand = NT == kSelThreads ? 8192 : 2040;
   static constexpr int kChunk = NT * kSelPer;        // keys per scan step
